@@ -1,0 +1,259 @@
+"""Benchmark of the N:M sparse x dense product on one MI355X.
+
+Default workload: ViT-B/16 FC1 at batch 64 -- W 3072x768 int8 at 2:4,
+X 768x12608 int8, fused bias + requant to int8 (the headline metric).  A
+step is one nm_spmm call (load, decode, sparse MFMA, epilogue, store) over
+one batch; the weights are packed once beforehand (nm_pack is offline, timed
+separately and reported as `pack_ms`).  Inputs rotate over >= 1 GiB of
+independent buffer sets so no timed call is served from the 256 MB
+Infinity Cache.
+
+Prints ONE JSON line on stdout.  `roofline.achieved` is the algorithmic
+bytes of one launch divided by the average launch duration measured with HIP
+events around the timed launches (on the stream the kernel runs on);
+`cpu_baseline` times the CPU oracle on a bounded row sample of the same
+workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0                              # MI355X HBM3E
+MFMA_PEAK_TOPS = {"i8": 5000.0, "f16": 2500.0, "bf16": 2500.0}   # dense, per dtype
+METRIC = "N:M SpMM dense-equivalent TOPS + % of MI355X roofline (int8 2:4, ViT-B FC1)"
+
+
+def _layers():
+    import nm_inputs
+    out = {nm_inputs.headline().name: nm_inputs.headline()}
+    for layers in nm_inputs.all_configs().values():
+        for L in layers:
+            out.setdefault(L.name, L)
+    return out
+
+
+def _traffic(kernel_name: str, launches_per_step: int = 1):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_name)
+    except ValueError:
+        return None
+    if not rec or rec.get("source_sha") != _source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "semi_structured_sparse_nm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(L, inp, target_s: float = 12.0):
+    """Time the CPU oracle (direct compressed loop + epilogue) on a row sample."""
+    import numpy as np
+    import oracle
+    vals, idx = oracle.compress(inp["W"], L.N, L.M, L.dt)
+    threads = oracle.max_threads()
+
+    def run(rows):
+        t = time.perf_counter()
+        acc = oracle.spmm_direct(vals, idx, inp["X"], L.R, L.K, L.N, L.M, L.dt, rows=rows)
+        if L.out == "i8":
+            oracle.requant_i8(acc, inp["bias"][rows], inp["scale"][rows])
+        return time.perf_counter() - t
+
+    n = max(threads, 8)
+    rows = np.arange(n) % L.R
+    dt = run(rows)
+    n2 = int(min(L.R, max(n, n * target_s / max(dt, 1e-3) * 0.8)))
+    n2 = max(threads, (n2 // threads) * threads)
+    rows = (np.arange(n2) * (L.R // max(1, n2))) % L.R
+    # repeat the sample until about target_s of CPU time has been measured
+    reps, total = 0, 0.0
+    while total < target_s and reps < 100:
+        total += run(rows)
+        reps += 1
+    dense_ops = 2.0 * L.K * L.T * n2 * reps
+    return {"value": dense_ops / total / 1e12, "unit": "TOPS (dense-equivalent)", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n2} of {L.R} rows x all {L.T} tokens of {L.name}, {reps} pass(es) "
+                      f"(direct compressed-index loop + epilogue, {total:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="vitb_fc1_2of4_i8")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--details", default="", help="write a JSON file of extra figures here")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the product shards by output rows or tokens with no exchange, but no "
+              "multi-GPU launcher is provided", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nm_inputs
+    import semi_structured_sparse_nm_amd as nm
+
+    L = _layers()[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = nm_inputs.make_inputs(L, seed=0)
+    tdt = {"i8": torch.int8, "f16": torch.float16, "bf16": torch.bfloat16}[L.dt]
+    odt = {"i8": torch.int8, "i32": torch.int32, "f16": torch.float16, "bf16": torch.bfloat16,
+           "f32": torch.float32}[L.out]
+
+    def to_dev(a, dt):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if dt == "bf16":
+            t = t.view(torch.bfloat16)
+        return t.to(dev)
+
+    W = to_dev(inp["W"], L.dt)
+    X0 = to_dev(inp["X"], L.dt)
+    bias = None if inp["bias"] is None else torch.from_numpy(inp["bias"]).to(dev)
+    scale = None if inp["scale"] is None else torch.from_numpy(inp["scale"]).to(dev)
+
+    # pack once (offline step), timed on its own
+    p = nm.pack(W, L.N, L.M)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        p = nm.pack(W, L.N, L.M)
+    e1.record()
+    torch.cuda.synchronize()
+    pack_ms = e0.elapsed_time(e1) / 5
+
+    ops, nbytes, dense_ops = nm_inputs.ops_and_bytes(L)
+    footprint = p.values.numel() + (0 if p.meta is None else p.meta.numel()) + \
+        X0.numel() * X0.element_size() + L.R * L.T * torch.empty(0, dtype=odt).element_size()
+    nsets = max(2, math.ceil(args.rotate_gib * 2**30 / footprint))
+    sets = []
+    for i in range(nsets):
+        pv = p.values.clone()
+        pm = None if p.meta is None else p.meta.clone()
+        ps = nm.Packed(p.rows, p.K, p.N, p.M, p.dtype, pv, pm, p.format_version)
+        Xi = X0.clone()
+        Yi = torch.empty((L.R, L.T), dtype=odt, device=dev)
+        sets.append((ps, Xi, Yi))
+    need = nm.workspace_size(p, L.T, odt)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    variant = nm.variant(p, L.T, odt)
+
+    def step(i):
+        ps, Xi, Yi = sets[i % nsets]
+        nm.spmm(ps, Xi, bias=bias, scale=scale, out_dtype=odt, out=Yi, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+
+    # warm (no rotation) figure, labelled as such
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record()
+    for _ in range(args.steps):
+        step(0)
+    w1.record()
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / args.steps
+
+    # quick parity spot check of the timed configuration on sampled rows
+    parity = None
+    try:
+        import oracle
+        rows = np.array([0, L.R // 2, L.R - 1])
+        ps, Xi, Yi = sets[0]
+        step(0)
+        torch.cuda.synchronize()
+        got = Yi[torch.from_numpy(rows).to(dev)].cpu()
+        if L.out == "bf16":
+            got = got.view(torch.int16).numpy().view(np.uint16)
+            got = oracle.to_f64(got, "bf16")
+        else:
+            got = got.numpy()
+        if L.dt == "i8":
+            ref = oracle.reference(inp["W"], inp["X"], L.N, L.M, L.dt, L.out, bias=inp["bias"],
+                                   scale=inp["scale"], rows=rows)
+            parity = "bit-exact" if np.array_equal(got, ref) else "MISMATCH"
+        else:
+            ref = oracle.reference(inp["W"], inp["X"], L.N, L.M, L.dt, "f64", rows=rows)
+            err = float(np.abs(got.astype(np.float64) - ref).max() / np.abs(ref).max())
+            parity = f"max-abs-normalised error {err:.2e}"
+    except Exception as ex:  # noqa: BLE001 - reported, not fatal
+        parity = f"not checked: {ex}"
+
+    t_s = ms * 1e-3
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = ops / (MFMA_PEAK_TOPS[L.dt] * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    if bound == "hbm":
+        achieved, peak, unit = nbytes / t_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = ops / t_s / 1e12, MFMA_PEAK_TOPS[L.dt], "TFLOP/s" if L.dt != "i8" else "TOPS"
+    traffic = _traffic(variant)
+    roof = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "t_roof_us": round(max(t_hbm, t_mfma) * 1e6, 3),
+            "roofline_fraction": round(max(t_hbm, t_mfma) / t_s, 4)}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(L, inp)
+
+    line = {
+        "metric": METRIC, "value": round(dense_ops / t_s / 1e12, 2),
+        "unit": "TOPS (dense-equivalent)", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": L.dt, "data": "synthetic",
+        "config": {"workload": L.name, "R": L.R, "K": L.K, "T": L.T, "N": L.N, "M": L.M,
+                   "in": L.dt, "out": L.out,
+                   "epilogue": "bias+requant" if L.out == "i8" else "none",
+                   "parallelism": "single-gpu"},
+        "roofline": roof, "cpu_baseline": cpu,
+        "kernel": variant, "rotation_sets": nsets, "warm_ms_per_step": round(warm_ms, 5),
+        "effective_GBps": round(nbytes / t_s / 1e9, 1), "pack_ms": round(pack_ms, 4),
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+    if args.details:
+        json.dump(line, open(args.details, "w"), indent=1)
+
+
+if __name__ == "__main__":
+    main()

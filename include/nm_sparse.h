@@ -1,0 +1,147 @@
+/*
+ * nm_sparse.h -- C ABI of the MI355X (gfx950) N:M semi-structured sparse
+ * weight x dense activation product
+ *
+ *     Y[R][T] = epilogue( (mask (.) W)[R][K] . X[K][T] )
+ *
+ * The operation is the N:M sparse matrix multiply of "Realizable N:M Sparse
+ * Transformer Inference via Search-Kernel Co-Design" (arXiv 2607.12505):
+ * Sec. 2.1 defines the constraint (N nonzeros kept in every group of M
+ * weights), Sec. 4.1 lists the three mechanisms of its kernel (packed weights
+ * for light decoding, micro-dense MMA-aligned execution, adaptive
+ * parallelism) and Sec. 4.2 the packed representation that stores each
+ * window's kept values together with their positions.  This library is a new
+ * design of that operation for CDNA4; it computes exactly the same product.
+ *
+ * Conventions (all matrices row-major, element strides given in elements):
+ *   W  [R][K]  weights, row stride ldw >= K
+ *   X  [K][T]  activations, tokens contiguous, row stride ldx >= T
+ *   Y  [R][T]  output, row stride ldy >= T
+ * Groups are M consecutive elements along K starting at k = 0 (K % M == 0).
+ *
+ * Ownership: the caller allocates and owns every buffer (weights, packed
+ * values / meta, X, Y, bias, scale, workspace); device buffers are HIP device
+ * memory.  The library never allocates, frees or keeps global mutable state;
+ * inputs are not modified; Y is fully overwritten.  `stream` is a hipStream_t
+ * (NULL = the default stream); work is enqueued asynchronously on it.
+ *
+ * Errors: every argument is validated on the host before anything is
+ * enqueued; on an error nothing is launched.  A launch failure reported by the
+ * HIP runtime returns NM_EHIP.  Faults inside a kernel surface at the
+ * caller's next synchronisation.  All functions are thread-safe.
+ */
+#ifndef NM_SPARSE_H
+#define NM_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NM_OK = 0,
+  NM_EINVAL = 1,        /* bad argument: null pointer, bad size, N/M, stride, buffer size */
+  NM_EUNSUPPORTED = 2,  /* valid but not provided: M not in {4, 8}, dtype pair, alignment */
+  NM_EHIP = 3           /* the HIP runtime reported an error at launch */
+} nm_status;
+
+typedef enum { NM_I8 = 0, NM_F16 = 1, NM_BF16 = 2, NM_I32 = 3, NM_F32 = 4 } nm_dtype;
+
+#define NM_FORMAT_VERSION 1u
+
+/*
+ * Packed weights (the paper's packed window representation, Sec. 4.2, in a
+ * layout chosen for gfx950).  Plain data: fill rows, K, N, M, dtype, the two
+ * device buffers and their sizes (from nm_pack_size); nm_pack sets
+ * format_version.  Layout, with b = element bytes, KB = 128 / b dense columns
+ * per block, w = log2(M), C = (KB / M) * N kept slots per block row:
+ *   the matrix is cut into blocks of 16 rows x KB columns, numbered
+ *   rb * ceil(K / KB) + kb; block n's values start at n * 16 * C * b bytes,
+ *   row rr of the block at rr * C * b, slot c at c * b: slot c is kept member
+ *   c % N (ascending in-group position) of group kb * (KB / M) + c / N.
+ *   meta (absent when N == M): block n at n * 16 * MR bytes, MR = ceil(C*w/8)
+ *   rounded up to a multiple of 4; row rr at rr * MR; slot c's in-group
+ *   position in bits [c*w, c*w + w) of the row's little-endian bitstream.
+ *   Slots outside the R x K matrix hold value 0 and position c % N.
+ * One block row is 128 * N / M bytes of values for every dtype, and one block
+ * is the A operand of one gfx950 sparse matrix instruction.
+ */
+typedef struct {
+  int64_t rows;             /* R */
+  int64_t K;                /* dense reduction length, multiple of M */
+  int32_t N, M;             /* N kept of every M */
+  int32_t dtype;            /* nm_dtype of the weights: NM_I8, NM_F16 or NM_BF16 */
+  uint32_t format_version;  /* NM_FORMAT_VERSION, written by nm_pack */
+  void* values;             /* device, values_bytes */
+  size_t values_bytes;
+  void* meta;               /* device, meta_bytes (may be NULL when N == M) */
+  size_t meta_bytes;
+} nm_packed;
+
+/*
+ * Sizes of the two packed buffers for an R x K weight of the given N:M and
+ * dtype.  NM_EINVAL: null outputs, rows < 1, K < M, K % M != 0, N < 1 or
+ * N > M.  NM_EUNSUPPORTED: M not in {4, 8}, dtype not I8 / F16 / BF16.
+ * meta_bytes is 0 when N == M.
+ */
+nm_status nm_pack_size(int64_t rows, int64_t K, int32_t N, int32_t M, int32_t dtype,
+                       size_t* values_bytes, size_t* meta_bytes);
+
+/*
+ * Select and pack (Sec. 2.1 constraint, Sec. 4.2 packed windows).  For every
+ * row and every group of M consecutive K-elements, keep the N members of
+ * largest magnitude, equal magnitudes going to the lower position (fp16 /
+ * bf16 magnitudes are compared as the sign-cleared bit patterns, which orders
+ * every finite value by |w| with +0 == -0), and write them with their
+ * positions in the layout above.  W is device memory [rows][ldw] of
+ * desc->dtype; desc->values / desc->meta are caller-allocated device buffers
+ * of exactly the sizes nm_pack_size returns (NM_EINVAL otherwise).
+ * Requires ldw >= K and W 2-byte aligned for 16-bit dtypes.
+ */
+nm_status nm_pack(const void* W, int64_t ldw, nm_packed* desc, void* stream);
+
+/*
+ * Device workspace nm_spmm needs for this weight, token count and output
+ * dtype (partial sums of a split reduction); 0 when none is needed.
+ */
+nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype, size_t* bytes);
+
+/*
+ * Y = epilogue(acc), acc[r][t] = sum over kept slots (r, k) of W[r][k] X[k][t].
+ * Supported (weight dtype -> y_dtype) pairs and epilogues:
+ *   I8  -> I32 : y = acc + bias[r]                (int32 accumulate, exact)
+ *   I8  -> I8  : y = sat_[-128,127](rne(f32(acc + bias[r]) * scale[r]))
+ *                (int32 add, RNE conversion, one binary32 multiply, round
+ *                half to even, saturate; scale required)
+ *   F16 -> F16 / F32,  BF16 -> BF16 / F32 :
+ *                y = round_to_y(acc + bias[r]), acc in fp32 (products exact)
+ * bias: NULL or device int32[R] (I8 weights) / float[R] (fp weights).
+ * scale: device float[R], required iff y_dtype == NM_I8, else ignored.
+ * X: device [K][ldx] of the weight dtype; Y: device [R][ldy] of y_dtype.
+ * workspace: device, at least nm_spmm_workspace_size bytes (may be NULL if 0).
+ * NM_EINVAL: null pointers, T < 1, ldx < T, ldy < T, bad descriptor (sizes
+ * not those of nm_pack_size, wrong format_version), small workspace.
+ * NM_EUNSUPPORTED: dtype pair not listed, X / Y not aligned to their element.
+ * T is unbounded; R and K are those of the packed weight.
+ */
+nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
+                  int32_t y_dtype, const void* bias, const float* scale, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* nm_status_str(nm_status s);
+
+/*
+ * Name of the kernel variant nm_spmm would launch for these arguments
+ * (static string; "invalid" when the arguments would be rejected).  For
+ * tests and profiling; launches nothing.
+ */
+const char* nm_spmm_variant(const nm_packed* w, int64_t T, int32_t y_dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NM_SPARSE_H */

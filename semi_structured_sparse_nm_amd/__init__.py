@@ -1,0 +1,185 @@
+"""MI355X (gfx950) N:M semi-structured sparse weight x dense activation product.
+
+Thin Python binding of libnmsparse.so (C ABI in include/nm_sparse.h): it only
+marshals torch tensors to device pointers and the current HIP stream; every
+step of the computation runs in the library's HIP kernels.  PyTorch provides
+device memory and streams.  There is no CPU fallback: without the built
+library every call raises.
+
+    p = pack(W, N, M)                      # W: [R, K] int8 / float16 / bfloat16 on the GPU
+    Y = spmm(p, X, bias=None, scale=None, out_dtype=None)   # X: [K, T]  ->  Y: [R, T]
+
+Operation: paper "Realizable N:M Sparse Transformer Inference via
+Search-Kernel Co-Design" (arXiv 2607.12505) -- Sec. 2.1 N:M constraint,
+Sec. 4.2 packed windows and micro-dense execution.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnmsparse.so")
+
+NM_OK, NM_EINVAL, NM_EUNSUPPORTED, NM_EHIP = 0, 1, 2, 3
+NM_I8, NM_F16, NM_BF16, NM_I32, NM_F32 = 0, 1, 2, 3, 4
+FORMAT_VERSION = 1
+
+_TORCH_TO_NM = {torch.int8: NM_I8, torch.float16: NM_F16, torch.bfloat16: NM_BF16,
+                torch.int32: NM_I32, torch.float32: NM_F32}
+_NM_TO_TORCH = {v: k for k, v in _TORCH_TO_NM.items()}
+
+
+class NmPacked(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int32),
+                ("M", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("format_version", ctypes.c_uint32), ("values", ctypes.c_void_p),
+                ("values_bytes", ctypes.c_size_t), ("meta", ctypes.c_void_p),
+                ("meta_bytes", ctypes.c_size_t)]
+
+
+class NmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libnmsparse.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m semi_structured_sparse_nm_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        PP = ctypes.POINTER(NmPacked)
+        L.nm_pack_size.argtypes = [I64, I64, I32, I32, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
+        L.nm_pack.argtypes = [P, I64, PP, P]
+        L.nm_spmm_workspace_size.argtypes = [PP, I64, I32, ctypes.POINTER(SZ)]
+        L.nm_spmm.argtypes = [PP, P, I64, I64, P, I64, I32, P, P, P, SZ, P]
+        L.nm_status_str.argtypes = [ctypes.c_int]
+        L.nm_status_str.restype = ctypes.c_char_p
+        L.nm_spmm_variant.argtypes = [PP, I64, I32]
+        L.nm_spmm_variant.restype = ctypes.c_char_p
+        for f in ("nm_pack_size", "nm_pack", "nm_spmm_workspace_size", "nm_spmm"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_str(s: int) -> str:
+    return lib().nm_status_str(int(s)).decode()
+
+
+def _check(st: int, what: str):
+    if st != NM_OK:
+        raise NmError(st, what)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def pack_size(rows: int, K: int, N: int, M: int, dtype: int):
+    vb, mb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().nm_pack_size(rows, K, N, M, dtype, ctypes.byref(vb), ctypes.byref(mb)),
+           "nm_pack_size")
+    return vb.value, mb.value
+
+
+@dataclass
+class Packed:
+    """Packed N:M weights on the GPU (two uint8 device buffers + shape)."""
+    rows: int
+    K: int
+    N: int
+    M: int
+    dtype: int
+    values: torch.Tensor
+    meta: torch.Tensor | None
+    format_version: int = FORMAT_VERSION
+
+    def desc(self) -> NmPacked:
+        d = NmPacked()
+        d.rows, d.K, d.N, d.M, d.dtype = self.rows, self.K, self.N, self.M, self.dtype
+        d.format_version = self.format_version
+        d.values, d.values_bytes = self.values.data_ptr(), self.values.numel()
+        if self.meta is not None:
+            d.meta, d.meta_bytes = self.meta.data_ptr(), self.meta.numel()
+        else:
+            d.meta, d.meta_bytes = None, 0
+        return d
+
+    @property
+    def torch_dtype(self):
+        return _NM_TO_TORCH[self.dtype]
+
+
+def pack(W: torch.Tensor, N: int, M: int) -> Packed:
+    """nm_pack: keep the N largest-|w| of every M consecutive K-elements of each row."""
+    if W.dim() != 2 or W.stride(1) != 1:
+        raise ValueError("W must be a 2-D tensor with unit stride along K")
+    dt = _TORCH_TO_NM.get(W.dtype)
+    if dt not in (NM_I8, NM_F16, NM_BF16):
+        raise TypeError(f"unsupported weight dtype {W.dtype}")
+    R, K = W.shape
+    vb, mb = pack_size(R, K, N, M, dt)
+    values = torch.empty(vb, dtype=torch.uint8, device=W.device)
+    meta = torch.empty(mb, dtype=torch.uint8, device=W.device) if mb else None
+    p = Packed(R, K, N, M, dt, values, meta, 0)
+    d = p.desc()
+    _check(lib().nm_pack(W.data_ptr(), W.stride(0), ctypes.byref(d), _stream(W.device)), "nm_pack")
+    p.format_version = d.format_version
+    return p
+
+
+def default_out_dtype(wdt: int) -> torch.dtype:
+    return {NM_I8: torch.int32, NM_F16: torch.float16, NM_BF16: torch.bfloat16}[wdt]
+
+
+def workspace_size(p: Packed, T: int, out_dtype: torch.dtype) -> int:
+    n = ctypes.c_size_t()
+    d = p.desc()
+    _check(lib().nm_spmm_workspace_size(ctypes.byref(d), T, _TORCH_TO_NM[out_dtype], ctypes.byref(n)),
+           "nm_spmm_workspace_size")
+    return n.value
+
+
+def variant(p: Packed, T: int, out_dtype: torch.dtype) -> str:
+    d = p.desc()
+    return lib().nm_spmm_variant(ctypes.byref(d), T, _TORCH_TO_NM[out_dtype]).decode()
+
+
+def spmm(p: Packed, X: torch.Tensor, bias: torch.Tensor | None = None,
+         scale: torch.Tensor | None = None, out_dtype: torch.dtype | None = None,
+         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """nm_spmm: Y[R, T] = epilogue((mask . W) @ X) with X [K, T] (tokens contiguous)."""
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D tensor with unit stride along T")
+    if X.shape[0] != p.K:
+        raise ValueError(f"X has {X.shape[0]} rows, the weight has K={p.K}")
+    T = X.shape[1]
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else default_out_dtype(p.dtype)
+    if out is None:
+        out = torch.empty((p.rows, T), dtype=out_dtype, device=X.device)
+    if out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (p.rows, T):
+        raise ValueError("out must be [R, T] with unit stride along T")
+    need = workspace_size(p, T, out_dtype)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    d = p.desc()
+    st = lib().nm_spmm(ctypes.byref(d), X.data_ptr(), X.stride(0), T, out.data_ptr(), out.stride(0),
+                       _TORCH_TO_NM[out_dtype], None if bias is None else bias.data_ptr(),
+                       None if scale is None else scale.data_ptr(),
+                       None if workspace is None else workspace.data_ptr(),
+                       0 if workspace is None else workspace.numel(), _stream(X.device))
+    _check(st, "nm_spmm")
+    return out

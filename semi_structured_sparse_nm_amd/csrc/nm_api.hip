@@ -1,0 +1,167 @@
+// C ABI of the library (include/nm_sparse.h): host-side validation, kernel
+// variant choice per shape, launches.  Stateless and thread-safe.
+#include <string.h>
+
+#include "nm_common.hpp"
+
+using nm::Geometry;
+using nm::SpmmArgs;
+
+namespace {
+
+bool is_weight_dtype(int dt) { return dt == NM_I8 || dt == NM_F16 || dt == NM_BF16; }
+
+nm_status check_shape(int64_t rows, int64_t K, int32_t N, int32_t M, int32_t dtype) {
+  if (rows < 1 || K < 1 || N < 1 || M < 1 || N > M) return NM_EINVAL;
+  if (M != 4 && M != 8) return NM_EUNSUPPORTED;
+  if (K % M != 0) return NM_EINVAL;
+  if (!is_weight_dtype(dtype)) return NM_EUNSUPPORTED;
+  return NM_OK;
+}
+
+bool pair_supported(int wdt, int ydt) {
+  switch (wdt) {
+    case NM_I8: return ydt == NM_I32 || ydt == NM_I8;
+    case NM_F16: return ydt == NM_F16 || ydt == NM_F32;
+    case NM_BF16: return ydt == NM_BF16 || ydt == NM_F32;
+    default: return false;
+  }
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+nm_status check_desc(const nm_packed* w, Geometry* out) {
+  if (!w) return NM_EINVAL;
+  nm_status st = check_shape(w->rows, w->K, w->N, w->M, w->dtype);
+  if (st != NM_OK) return st;
+  Geometry g = Geometry::make(w->rows, w->K, w->N, w->M, nm::dtype_bytes(w->dtype));
+  if (!w->values || w->values_bytes != g.values_bytes()) return NM_EINVAL;
+  if (g.w != 0 && (!w->meta || w->meta_bytes != g.meta_bytes())) return NM_EINVAL;
+  if (!aligned(w->values, 16) || (g.w != 0 && !aligned(w->meta, 16))) return NM_EUNSUPPORTED;
+  *out = g;
+  return NM_OK;
+}
+
+// Variant table (adaptive parallelism per shape).  Only the generic kernel
+// exists so far.
+enum Variant { V_INVALID = 0, V_GENERIC };
+
+const char* variant_name(Variant v) {
+  switch (v) {
+    case V_GENERIC: return "generic_dense_expand";
+    default: return "invalid";
+  }
+}
+
+Variant choose(const Geometry& g, int wdt, int64_t T, int ydt) {
+  (void)g; (void)wdt; (void)T; (void)ydt;
+  return V_GENERIC;
+}
+
+size_t workspace_for(Variant v, const Geometry& g, int64_t T) {
+  (void)v; (void)g; (void)T;
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+nm_status nm_pack_size(int64_t rows, int64_t K, int32_t N, int32_t M, int32_t dtype,
+                       size_t* values_bytes, size_t* meta_bytes) {
+  if (!values_bytes || !meta_bytes) return NM_EINVAL;
+  nm_status st = check_shape(rows, K, N, M, dtype);
+  if (st != NM_OK) return st;
+  Geometry g = Geometry::make(rows, K, N, M, nm::dtype_bytes(dtype));
+  *values_bytes = g.values_bytes();
+  *meta_bytes = g.meta_bytes();
+  return NM_OK;
+}
+
+nm_status nm_pack(const void* W, int64_t ldw, nm_packed* desc, void* stream) {
+  if (!W || !desc) return NM_EINVAL;
+  nm_status st = check_shape(desc->rows, desc->K, desc->N, desc->M, desc->dtype);
+  if (st != NM_OK) return st;
+  if (ldw < desc->K) return NM_EINVAL;
+  Geometry g = Geometry::make(desc->rows, desc->K, desc->N, desc->M, nm::dtype_bytes(desc->dtype));
+  if (!desc->values || desc->values_bytes != g.values_bytes()) return NM_EINVAL;
+  if (g.w != 0 && (!desc->meta || desc->meta_bytes != g.meta_bytes())) return NM_EINVAL;
+  if (!aligned(W, (size_t)g.eb)) return NM_EUNSUPPORTED;
+  if (!aligned(desc->values, 16) || (g.w != 0 && !aligned(desc->meta, 16))) return NM_EUNSUPPORTED;
+  hipError_t e = nm::launch_pack(W, ldw, g, desc->dtype, static_cast<uint8_t*>(desc->values),
+                                 g.w ? static_cast<uint8_t*>(desc->meta) : nullptr,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return NM_EHIP;
+  desc->format_version = NM_FORMAT_VERSION;
+  return NM_OK;
+}
+
+nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype, size_t* bytes) {
+  if (!bytes) return NM_EINVAL;
+  Geometry g;
+  nm_status st = check_desc(w, &g);
+  if (st != NM_OK) return st;
+  if (T < 1) return NM_EINVAL;
+  if (!pair_supported(w->dtype, y_dtype)) return NM_EUNSUPPORTED;
+  *bytes = workspace_for(choose(g, w->dtype, T, y_dtype), g, T);
+  return NM_OK;
+}
+
+nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
+                  int32_t y_dtype, const void* bias, const float* scale, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  Geometry g;
+  nm_status st = check_desc(w, &g);
+  if (st != NM_OK) return st;
+  if (w->format_version != NM_FORMAT_VERSION) return NM_EINVAL;
+  if (!X || !Y || T < 1 || ldx < T || ldy < T) return NM_EINVAL;
+  if (!pair_supported(w->dtype, y_dtype)) return NM_EUNSUPPORTED;
+  if (y_dtype == NM_I8 && !scale) return NM_EINVAL;
+  if (!aligned(X, (size_t)g.eb) || !aligned(Y, (size_t)nm::dtype_bytes(y_dtype))) return NM_EUNSUPPORTED;
+  if (bias && !aligned(bias, 4)) return NM_EUNSUPPORTED;
+  if (scale && !aligned(scale, 4)) return NM_EUNSUPPORTED;
+  Variant v = choose(g, w->dtype, T, y_dtype);
+  size_t need = workspace_for(v, g, T);
+  if (workspace_bytes < need || (need && !workspace)) return NM_EINVAL;
+
+  SpmmArgs a;
+  a.g = g;
+  a.wdt = w->dtype;
+  a.ydt = y_dtype;
+  a.values = static_cast<const uint8_t*>(w->values);
+  a.meta = g.w ? static_cast<const uint8_t*>(w->meta) : nullptr;
+  a.X = X;
+  a.ldx = ldx;
+  a.T = T;
+  a.Y = Y;
+  a.ldy = ldy;
+  a.bias = bias;
+  a.scale = (y_dtype == NM_I8) ? scale : nullptr;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  switch (v) {
+    case V_GENERIC: e = nm::launch_spmm_generic(a, s); break;
+    default: return NM_EINVAL;
+  }
+  return e == hipSuccess ? NM_OK : NM_EHIP;
+}
+
+const char* nm_status_str(nm_status s) {
+  switch (s) {
+    case NM_OK: return "NM_OK: success";
+    case NM_EINVAL: return "NM_EINVAL: invalid argument";
+    case NM_EUNSUPPORTED: return "NM_EUNSUPPORTED: unsupported configuration";
+    case NM_EHIP: return "NM_EHIP: HIP runtime error at launch";
+    default: return "unknown nm_status";
+  }
+}
+
+const char* nm_spmm_variant(const nm_packed* w, int64_t T, int32_t y_dtype) {
+  Geometry g;
+  if (check_desc(w, &g) != NM_OK || T < 1 || !pair_supported(w->dtype, y_dtype)) return "invalid";
+  return variant_name(choose(g, w->dtype, T, y_dtype));
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// Shared definitions of the HIP library: packed-layout geometry, launch
+// argument bundles and small device helpers.  Internal; the public surface is
+// include/nm_sparse.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/nm_sparse.h"
+
+namespace nm {
+
+// ---------------------------------------------------------------- layout
+// Geometry of the blocked packed layout (documented with nm_packed in the
+// public header): 16-row x KB-column blocks, KB = 128 / element bytes.
+struct Geometry {
+  int64_t R, K;
+  int N, M;
+  int eb;          // element bytes (1 or 2)
+  int KB;          // dense columns per block
+  int GB;          // groups per block row
+  int C;           // kept slots per block row
+  int w;           // index bits (2 or 3), 0 when N == M
+  int MR;          // meta bytes per block row (multiple of 4), 0 when N == M
+  int64_t nRB, nKB;
+  int64_t vblk;    // value bytes per block
+  int64_t mblk;    // meta bytes per block
+
+  static Geometry make(int64_t R, int64_t K, int N, int M, int eb) {
+    Geometry g;
+    g.R = R; g.K = K; g.N = N; g.M = M; g.eb = eb;
+    g.KB = 128 / eb;
+    g.GB = g.KB / M;
+    g.C = g.GB * N;
+    g.w = (N == M) ? 0 : (M == 4 ? 2 : 3);
+    int mr = (g.C * g.w + 7) / 8;
+    g.MR = (mr + 3) / 4 * 4;
+    g.nRB = (R + 15) / 16;
+    g.nKB = (K + g.KB - 1) / g.KB;
+    g.vblk = (int64_t)16 * g.C * eb;
+    g.mblk = (int64_t)16 * g.MR;
+    return g;
+  }
+  size_t values_bytes() const { return (size_t)(nRB * nKB * vblk); }
+  size_t meta_bytes() const { return (size_t)(nRB * nKB * mblk); }
+};
+
+inline int dtype_bytes(int dt) {
+  switch (dt) {
+    case NM_I8: return 1;
+    case NM_F16: case NM_BF16: return 2;
+    case NM_I32: case NM_F32: return 4;
+    default: return 0;
+  }
+}
+
+// ---------------------------------------------------------------- launches
+struct SpmmArgs {
+  Geometry g;
+  int wdt;                 // weight / activation dtype (NM_I8, NM_F16, NM_BF16)
+  int ydt;                 // output dtype
+  const uint8_t* values;
+  const uint8_t* meta;
+  const void* X;
+  int64_t ldx;
+  int64_t T;
+  void* Y;
+  int64_t ldy;
+  const void* bias;        // int32[R] or float[R] or nullptr
+  const float* scale;      // float[R] (int8 output) or nullptr
+  void* ws;                // workspace
+  size_t ws_bytes;
+};
+
+// Kernel variants; each launcher returns hipSuccess or the launch error.
+hipError_t launch_pack(const void* W, int64_t ldw, const Geometry& g, int wdt, uint8_t* values,
+                       uint8_t* meta, hipStream_t s);
+hipError_t launch_spmm_generic(const SpmmArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- device
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// binary32 -> binary16 / bfloat16 bits, round to nearest even (finite inputs;
+// bfloat16 NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;  // v_cvt_f16_f32 rounds to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// int8 requantisation: sat(rne(f32(a) * s)); `a` already includes the bias.
+// The product is one rounded binary32 multiply (no contraction into an fma),
+// then round-half-even and saturation.
+__device__ __forceinline__ int requant_i8(int a, float s) {
+  float f = (float)a;
+  float q = __fmul_rn(f, s);
+  q = __builtin_rintf(q);
+  q = fminf(fmaxf(q, -128.0f), 127.0f);
+  return (int)q;
+}
+
+}  // namespace nm

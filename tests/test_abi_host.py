@@ -1,0 +1,148 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+ - the shared library loads and exports every function include/nm_sparse.h
+   declares;
+ - nm_pack_size matches the packed layout's size formulas;
+ - every documented validation error is returned before anything is launched
+   (the arguments are rejected on the host, so no device is touched).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import semi_structured_sparse_nm_amd as nm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nm_sparse.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert {"nm_pack", "nm_spmm", "nm_pack_size", "nm_spmm_workspace_size",
+            "nm_status_str"} <= set(names)
+    L = nm.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in the header but not exported"
+
+
+def test_status_strings_cover_every_code():
+    for s in (nm.NM_OK, nm.NM_EINVAL, nm.NM_EUNSUPPORTED, nm.NM_EHIP):
+        assert nm.status_str(s).startswith("NM_")
+    assert nm.status_str(99) == "unknown nm_status"
+
+
+@pytest.mark.parametrize("dt,eb", [(nm.NM_I8, 1), (nm.NM_F16, 2), (nm.NM_BF16, 2)])
+@pytest.mark.parametrize("N,M", [(1, 4), (2, 4), (3, 4), (4, 4), (1, 8), (2, 8), (3, 8), (4, 8), (8, 8)])
+@pytest.mark.parametrize("R,K", [(1, 8), (17, 96), (192, 192), (3072, 768), (4096, 11008)])
+def test_pack_size_formula(dt, eb, N, M, R, K):
+    vb, mb = nm.pack_size(R, K, N, M, dt)
+    KB = 128 // eb
+    C = KB // M * N
+    w = 0 if N == M else {4: 2, 8: 3}[M]
+    MR = (C * w + 7) // 8
+    MR = (MR + 3) // 4 * 4
+    nblk = -(-R // 16) * -(-K // KB)
+    assert vb == nblk * 16 * C * eb
+    assert mb == nblk * 16 * MR
+
+
+@pytest.mark.parametrize("args,want", [
+    ((0, 8, 2, 4, nm.NM_I8), nm.NM_EINVAL),        # rows < 1
+    ((4, 0, 2, 4, nm.NM_I8), nm.NM_EINVAL),        # K < 1
+    ((4, 8, 0, 4, nm.NM_I8), nm.NM_EINVAL),        # N < 1
+    ((4, 8, 5, 4, nm.NM_I8), nm.NM_EINVAL),        # N > M
+    ((4, 10, 2, 4, nm.NM_I8), nm.NM_EINVAL),       # K % M
+    ((4, 12, 2, 6, nm.NM_I8), nm.NM_EUNSUPPORTED),  # M not in {4, 8}
+    ((4, 16, 2, 16, nm.NM_I8), nm.NM_EUNSUPPORTED),
+    ((4, 8, 2, 4, nm.NM_I32), nm.NM_EUNSUPPORTED),  # weight dtype
+    ((4, 8, 2, 4, 17), nm.NM_EUNSUPPORTED),
+])
+def test_pack_size_errors(args, want):
+    vb, mb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert nm.lib().nm_pack_size(*args, ctypes.byref(vb), ctypes.byref(mb)) == want
+    assert nm.lib().nm_pack_size(4, 8, 2, 4, nm.NM_I8, None, ctypes.byref(mb)) == nm.NM_EINVAL
+
+
+# Fake, well-aligned device addresses: every case below is rejected on the
+# host before a launch, so they are never dereferenced.
+FAKE = 0x7f0000000000
+
+
+def _desc(R=32, K=64, N=2, M=4, dt=nm.NM_I8, **kw):
+    vb, mb = nm.pack_size(R, K, N, M, dt)
+    d = nm.NmPacked()
+    d.rows, d.K, d.N, d.M, d.dtype = R, K, N, M, dt
+    d.format_version = nm.FORMAT_VERSION
+    d.values, d.values_bytes = FAKE, vb
+    d.meta, d.meta_bytes = (FAKE + (1 << 24), mb) if mb else (None, 0)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _spmm(d, X=FAKE + (2 << 24), ldx=100, T=100, Y=FAKE + (3 << 24), ldy=100, ydt=nm.NM_I32,
+          bias=None, scale=None, ws=None, wsb=0):
+    return nm.lib().nm_spmm(ctypes.byref(d), X, ldx, T, Y, ldy, ydt, bias, scale, ws, wsb, None)
+
+
+def test_spmm_validation_errors():
+    L = nm.lib()
+    ok = _desc()
+    assert L.nm_spmm(None, FAKE, 1, 1, FAKE, 1, nm.NM_I32, None, None, None, 0, None) == nm.NM_EINVAL
+    assert _spmm(ok, X=None) == nm.NM_EINVAL
+    assert _spmm(ok, Y=None) == nm.NM_EINVAL
+    assert _spmm(ok, T=0) == nm.NM_EINVAL
+    assert _spmm(ok, ldx=99) == nm.NM_EINVAL
+    assert _spmm(ok, ldy=99) == nm.NM_EINVAL
+    assert _spmm(ok, ydt=nm.NM_I8) == nm.NM_EINVAL            # scale required for int8 output
+    assert _spmm(ok, ydt=nm.NM_F16) == nm.NM_EUNSUPPORTED    # int8 weights -> fp16 not provided
+    assert _spmm(ok, ydt=99) == nm.NM_EUNSUPPORTED
+    assert _spmm(_desc(values_bytes=ok.values_bytes + 1)) == nm.NM_EINVAL
+    assert _spmm(_desc(meta_bytes=0)) == nm.NM_EINVAL
+    assert _spmm(_desc(meta=None)) == nm.NM_EINVAL
+    assert _spmm(_desc(values=None)) == nm.NM_EINVAL
+    assert _spmm(_desc(format_version=0)) == nm.NM_EINVAL
+    bad = _desc()
+    bad.N = 5
+    assert _spmm(bad) == nm.NM_EINVAL
+    bad = _desc()
+    bad.M = 6
+    assert _spmm(bad) == nm.NM_EUNSUPPORTED
+    assert _spmm(_desc(values=FAKE + 8)) == nm.NM_EUNSUPPORTED  # packed buffers need 16 B alignment
+    f16 = _desc(dt=nm.NM_F16)
+    assert _spmm(f16, ydt=nm.NM_F16, X=FAKE + 1) == nm.NM_EUNSUPPORTED  # X not 2-byte aligned
+    assert _spmm(f16, ydt=nm.NM_F32, Y=FAKE + 2) == nm.NM_EUNSUPPORTED  # Y not 4-byte aligned
+    assert _spmm(f16, ydt=nm.NM_BF16) == nm.NM_EUNSUPPORTED
+
+
+def test_pack_validation_errors():
+    L = nm.lib()
+    d = _desc(format_version=0)
+    assert L.nm_pack(None, 64, ctypes.byref(d), None) == nm.NM_EINVAL
+    assert L.nm_pack(FAKE, 64, None, None) == nm.NM_EINVAL
+    assert L.nm_pack(FAKE, 63, ctypes.byref(d), None) == nm.NM_EINVAL          # ldw < K
+    bad = _desc(values_bytes=d.values_bytes - 1, format_version=0)
+    assert L.nm_pack(FAKE, 64, ctypes.byref(bad), None) == nm.NM_EINVAL
+    f16 = _desc(dt=nm.NM_F16, format_version=0)
+    assert L.nm_pack(FAKE + 1, 64, ctypes.byref(f16), None) == nm.NM_EUNSUPPORTED
+    assert d.format_version == 0   # untouched on error
+
+
+def test_workspace_and_variant_queries():
+    L = nm.lib()
+    d = _desc()
+    n = ctypes.c_size_t(123)
+    assert L.nm_spmm_workspace_size(ctypes.byref(d), 100, nm.NM_I32, ctypes.byref(n)) == nm.NM_OK
+    assert L.nm_spmm_workspace_size(ctypes.byref(d), 0, nm.NM_I32, ctypes.byref(n)) == nm.NM_EINVAL
+    assert L.nm_spmm_workspace_size(ctypes.byref(d), 100, nm.NM_I32, None) == nm.NM_EINVAL
+    assert L.nm_spmm_variant(ctypes.byref(d), 100, nm.NM_I32).decode() != "invalid"
+    assert L.nm_spmm_variant(ctypes.byref(d), 0, nm.NM_I32).decode() == "invalid"
+    assert L.nm_spmm_variant(None, 100, nm.NM_I32).decode() == "invalid"

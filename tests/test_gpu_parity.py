@@ -1,0 +1,162 @@
+"""GPU parity of nm_pack and nm_spmm against the CPU oracle (needs an MI355X).
+
+ - nm_pack: the packed bytes, decoded by the oracle's independent reader,
+   equal the oracle's compression bit for bit, and padding is clean.
+ - nm_spmm at sizes the oracle finishes in seconds (several tiles plus ragged
+   tails): every dtype pair, every N:M, element by element.
+ - Edge shapes: T in {1, 15, 16, 17}, K = M, R = 1 / 17, row strides beyond T,
+   output padding untouched.
+ - Identity activations return the masked weights; repeated runs are
+   bitwise identical.
+ - Every workload shape at full size (the launch configuration the benchmark
+   times), compared on sampled rows the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+import nm_inputs
+import oracle
+from tests._parity import compare, layer_case, packed_host, reference, run
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [("i8", "i32"), ("i8", "i8"), ("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"),
+         ("bf16", "f32")]
+NMS = [(1, 4), (2, 4), (3, 4), (4, 4), (1, 8), (2, 8), (4, 8), (8, 8)]
+
+
+def _inputs(dt, out, R, K, T, N, M, seed, tag):
+    if dt == "i8" and out == "i32":
+        return (nm_inputs.uniform_int8((R, K), seed, tag, "W"),
+                nm_inputs.uniform_int8((K, T), seed, tag, "X"),
+                nm_inputs.uniform_int8((R,), seed, tag, "b").astype(np.int32) * 1000, None)
+    if dt == "i8":
+        q = nm_inputs.quant_layer(R, K, T, N, M, seed, tag)
+        return q.W, q.X, q.bias, q.scale
+    W = nm_inputs.normal((R, K), 0.02, dt, seed, tag, "W")
+    X = nm_inputs.normal((K, T), 1.0, dt, seed, tag, "X")
+    b = nm_inputs.normal((R,), 0.05, "f32", seed, tag, "b")
+    return W, X, b, None
+
+
+@pytest.mark.parametrize("dt", ["i8", "f16", "bf16"])
+@pytest.mark.parametrize("N,M", NMS)
+def test_pack_matches_oracle(dt, N, M):
+    for R, K in ((1, M), (17, 96 if M == 4 else 96), (40, 264 if M == 4 else 264), (33, 512)):
+        if dt == "i8":
+            # small integers: many magnitude ties
+            W = nm_inputs.uniform_int8((R, K), 1, "pack", dt, N, M, R, lo=-3, hi=3)
+            W[0, :M] = -128
+        else:
+            W = nm_inputs.normal((R, K), 0.02, dt, 1, "pack", N, M, R)
+            if dt == "f16":
+                W[0, :4] = np.array([0.0, -0.0, -0.0, 0.0], np.float16)
+        _, p = run(W, np.zeros((K, 1), W.dtype), N, M, dt, {"i8": "i32", "f16": "f16",
+                                                          "bf16": "bf16"}[dt])
+        v, m = packed_host(p)
+        vals, idx = oracle.read_packed(v, m, R, K, N, M, dt)
+        cv, ci = oracle.compress(W, N, M, dt)
+        assert np.array_equal(ci, idx), (R, K)
+        assert np.array_equal(cv.view(np.uint8), vals.view(np.uint8)), (R, K)
+        assert oracle.check_padding(v, m, R, K, N, M, dt) == 0, (R, K)
+
+
+def test_pack_row_stride():
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    from tests._parity import dev
+    R, K = 20, 200
+    W = nm_inputs.uniform_int8((R, K + 24), 2, "ldw")
+    full = dev(W, "i8")
+    p = nm.pack(full[:, :K], 2, 4)
+    torch.cuda.synchronize()
+    v, m = packed_host(p)
+    vals, idx = oracle.read_packed(v, m, R, K, 2, 4, "i8")
+    cv, ci = oracle.compress(np.ascontiguousarray(W[:, :K]), 2, 4, "i8")
+    assert np.array_equal(ci, idx) and np.array_equal(cv, vals)
+
+
+@pytest.mark.parametrize("dt,out", PAIRS)
+@pytest.mark.parametrize("N,M", NMS)
+def test_spmm_small(dt, out, N, M):
+    R, K, T = 96, 192, 197
+    W, X, b, s = _inputs(dt, out, R, K, T, N, M, 3, f"small-{dt}-{out}-{N}-{M}")
+    Y, _ = run(W, X, N, M, dt, out, bias=b, scale=s)
+    compare(Y, reference(W, X, N, M, dt, out, bias=b, scale=s), out, f"{dt}->{out} {N}:{M}")
+
+
+@pytest.mark.parametrize("dt,out", PAIRS)
+@pytest.mark.parametrize("R,K,T", [(1, 8, 1), (17, 8, 15), (16, 96, 16), (17, 96, 17),
+                                   (33, 200, 64), (5, 1032, 3)])
+def test_spmm_edges(dt, out, R, K, T):
+    N, M = (2, 4) if K % 8 else (3, 8)
+    W, X, b, s = _inputs(dt, out, R, K, T, N, M, 4, f"edge-{dt}-{out}-{R}-{K}-{T}")
+    Y, _ = run(W, X, N, M, dt, out, bias=b, scale=s, ldx_pad=5, ldy_pad=3, sentinel=7)
+    compare(Y[:, :T], reference(W, X, N, M, dt, out, bias=b, scale=s), out, "edge")
+    pad = Y[:, T:]
+    want = 7 if out != "bf16" else oracle.round_to(np.array([7.0]), "bf16")[0]
+    assert np.all(pad == want), "writes beyond T"
+
+
+@pytest.mark.parametrize("dt", ["i8", "f16", "bf16"])
+@pytest.mark.parametrize("N,M", [(2, 4), (1, 4), (2, 8), (4, 8)])
+def test_identity_activation(dt, N, M):
+    R, K = 48, 256
+    out = {"i8": "i32", "f16": "f32", "bf16": "f32"}[dt]
+    if dt == "i8":
+        W = nm_inputs.uniform_int8((R, K), 5, "ident")
+        X = np.eye(K, dtype=np.int8)
+    else:
+        W = nm_inputs.normal((R, K), 0.02, dt, 5, "ident")
+        one = np.float16(1.0) if dt == "f16" else np.uint16(0x3F80)
+        X = np.zeros((K, K), W.dtype)
+        np.fill_diagonal(X, one)
+    Y, _ = run(W, X, N, M, dt, out)
+    vals, idx = oracle.compress(W, N, M, dt)
+    Wm = oracle.to_f64(oracle.decompress(vals, idx, R, K, N, M, dt), dt)
+    assert np.array_equal(np.asarray(Y).astype(np.float64), Wm)   # every output is one product
+
+
+@pytest.mark.parametrize("dt,out", [("i8", "i8"), ("f16", "f16"), ("bf16", "f32")])
+def test_repeat_runs_bitwise_identical(dt, out):
+    R, K, T = 256, 768, 1000
+    W, X, b, s = _inputs(dt, out, R, K, T, 2, 4, 6, "repeat")
+    Y1, _ = run(W, X, 2, 4, dt, out, bias=b, scale=s)
+    Y2, _ = run(W, X, 2, 4, dt, out, bias=b, scale=s)
+    assert np.array_equal(np.asarray(Y1).view(np.uint8), np.asarray(Y2).view(np.uint8))
+
+
+def test_config1_exact():
+    (L,) = nm_inputs.config1()
+    W, X, b, s = layer_case(L)
+    Y, _ = run(W, X, L.N, L.M, L.dt, L.out)
+    ref = reference(W, X, L.N, L.M, L.dt, L.out)
+    compare(Y, ref, L.out, L.name)
+    # closed-form row checksums, exact in int64
+    vals, idx = oracle.compress(W, L.N, L.M, L.dt)
+    Wm = oracle.decompress(vals, idx, L.R, L.K, L.N, L.M, L.dt).astype(np.int64)
+    assert np.array_equal(Y.astype(np.int64).sum(axis=1), Wm @ X.astype(np.int64).sum(axis=1))
+
+
+def _full_layers():
+    seen, out = set(), []
+    for cfg, layers in nm_inputs.all_configs().items():
+        if cfg == "1":
+            continue
+        for L in layers:
+            key = (L.R, L.K, L.T, L.N, L.M, L.dt, L.out)
+            if key in seen:        # the mixed stack repeats shapes of the ViT-B layers
+                continue
+            seen.add(key)
+            out.append(L)
+    return out
+
+
+@pytest.mark.parametrize("L", _full_layers(), ids=lambda L: L.name)
+def test_full_size_sampled_rows(L):
+    W, X, b, s = layer_case(L)
+    Y, _ = run(W, X, L.N, L.M, L.dt, L.out, bias=b, scale=s)
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, L.R - 1], rng.integers(0, L.R, 6)]))
+    ref = reference(W, X, L.N, L.M, L.dt, L.out, bias=b, scale=s, rows=rows)
+    compare(np.asarray(Y)[rows], ref, L.out, L.name)
