@@ -1,5 +1,6 @@
 // C ABI of the library (include/nm_sparse.h): host-side validation, kernel
 // variant choice per shape, launches.  Stateless and thread-safe.
+#include <stdlib.h>
 #include <string.h>
 
 #include "nm_common.hpp"
@@ -42,20 +43,62 @@ nm_status check_desc(const nm_packed* w, Geometry* out) {
   return NM_OK;
 }
 
-// Variant table (adaptive parallelism per shape).  Only the generic kernel
-// exists so far.
-enum Variant { V_INVALID = 0, V_GENERIC };
+// Variant table (the paper's adaptive parallelism, Sec. 4.1: the kernel and
+// its tiling follow the operator's shape).  NM_SPMM_VARIANT=<name> in the
+// environment forces a variant where its requirements hold (tile sweeps).
+enum Variant {
+  V_INVALID = 0,
+  V_GENERIC,
+  V_SMFMAC_I8,      // int8 2:4 sparse MFMA, 256 x 128 tile
+  V_COUNT
+};
 
 const char* variant_name(Variant v) {
   switch (v) {
     case V_GENERIC: return "generic_dense_expand";
+    case V_SMFMAC_I8: return "smfmac_i8_2of4_256x128";
     default: return "invalid";
   }
 }
 
-Variant choose(const Geometry& g, int wdt, int64_t T, int ydt) {
-  (void)g; (void)wdt; (void)T; (void)ydt;
+struct Call {
+  const Geometry* g;
+  int wdt, ydt;
+  int64_t T, ldx, ldy;
+  const void* X;
+  const void* Y;
+};
+
+bool eligible(Variant v, const Call& c) {
+  switch (v) {
+    case V_GENERIC: return true;
+    case V_SMFMAC_I8:
+      // 2:4 int8; X rows in whole 16-byte chunks; 32-bit buffer offsets
+      // (X, Y and the packed weights below 2 GiB); int8 output stored as
+      // 8-byte row pieces
+      return c.wdt == NM_I8 && c.g->N == 2 && c.g->M == 4 && c.T % 16 == 0 && c.ldx % 16 == 0 &&
+             aligned(c.X, 16) && c.g->K * c.ldx < (1ll << 31) && c.g->values_bytes() < (1ull << 31) &&
+             c.g->R * c.ldy * 4 < (1ll << 31) &&
+             (c.ydt == NM_I32 || (c.ydt == NM_I8 && c.ldy % 8 == 0 && aligned(c.Y, 8)));
+    default: return false;
+  }
+}
+
+Variant choose(const Call& c) {
+  const char* force = getenv("NM_SPMM_VARIANT");
+  if (force && *force) {
+    for (int v = V_GENERIC; v < V_COUNT; ++v)
+      if (strcmp(force, variant_name((Variant)v)) == 0 && eligible((Variant)v, c)) return (Variant)v;
+  }
+  if (eligible(V_SMFMAC_I8, c)) return V_SMFMAC_I8;
   return V_GENERIC;
+}
+
+Call make_call(const Geometry& g, int wdt, int ydt, int64_t T, int64_t ldx, int64_t ldy, const void* X,
+               const void* Y) {
+  Call c;
+  c.g = &g; c.wdt = wdt; c.ydt = ydt; c.T = T; c.ldx = ldx; c.ldy = ldy; c.X = X; c.Y = Y;
+  return c;
 }
 
 size_t workspace_for(Variant v, const Geometry& g, int64_t T) {
@@ -103,7 +146,13 @@ nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype,
   if (st != NM_OK) return st;
   if (T < 1) return NM_EINVAL;
   if (!pair_supported(w->dtype, y_dtype)) return NM_EUNSUPPORTED;
-  *bytes = workspace_for(choose(g, w->dtype, T, y_dtype), g, T);
+  // the variant may depend on strides and alignment; report the largest need
+  size_t need = 0;
+  for (int v = V_GENERIC; v < V_COUNT; ++v) {
+    size_t n = workspace_for((Variant)v, g, T);
+    if (n > need) need = n;
+  }
+  *bytes = need;
   return NM_OK;
 }
 
@@ -120,7 +169,7 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
   if (!aligned(X, (size_t)g.eb) || !aligned(Y, (size_t)nm::dtype_bytes(y_dtype))) return NM_EUNSUPPORTED;
   if (bias && !aligned(bias, 4)) return NM_EUNSUPPORTED;
   if (scale && !aligned(scale, 4)) return NM_EUNSUPPORTED;
-  Variant v = choose(g, w->dtype, T, y_dtype);
+  Variant v = choose(make_call(g, w->dtype, y_dtype, T, ldx, ldy, X, Y));
   size_t need = workspace_for(v, g, T);
   if (workspace_bytes < need || (need && !workspace)) return NM_EINVAL;
 
@@ -143,6 +192,7 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
   hipError_t e = hipSuccess;
   switch (v) {
     case V_GENERIC: e = nm::launch_spmm_generic(a, s); break;
+    case V_SMFMAC_I8: e = nm::launch_spmm_smfmac_i8(a, 0, s); break;
     default: return NM_EINVAL;
   }
   return e == hipSuccess ? NM_OK : NM_EHIP;
@@ -161,7 +211,9 @@ const char* nm_status_str(nm_status s) {
 const char* nm_spmm_variant(const nm_packed* w, int64_t T, int32_t y_dtype) {
   Geometry g;
   if (check_desc(w, &g) != NM_OK || T < 1 || !pair_supported(w->dtype, y_dtype)) return "invalid";
-  return variant_name(choose(g, w->dtype, T, y_dtype));
+  // dense row-major operands, 256-byte aligned (what a fresh allocation gives)
+  const void* al = reinterpret_cast<const void*>((uintptr_t)256);
+  return variant_name(choose(make_call(g, w->dtype, y_dtype, T, T, T, al, al)));
 }
 
 }  // extern "C"

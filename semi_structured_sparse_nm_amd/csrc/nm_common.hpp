@@ -41,8 +41,8 @@ struct Geometry {
     g.mblk = (int64_t)16 * g.MR;
     return g;
   }
-  size_t values_bytes() const { return (size_t)(nRB * nKB * vblk); }
-  size_t meta_bytes() const { return (size_t)(nRB * nKB * mblk); }
+  __host__ __device__ size_t values_bytes() const { return (size_t)(nRB * nKB * vblk); }
+  __host__ __device__ size_t meta_bytes() const { return (size_t)(nRB * nKB * mblk); }
 };
 
 inline int dtype_bytes(int dt) {
@@ -76,6 +76,7 @@ struct SpmmArgs {
 hipError_t launch_pack(const void* W, int64_t ldw, const Geometry& g, int wdt, uint8_t* values,
                        uint8_t* meta, hipStream_t s);
 hipError_t launch_spmm_generic(const SpmmArgs& a, hipStream_t s);
+hipError_t launch_spmm_smfmac_i8(const SpmmArgs& a, int cfg, hipStream_t s);
 
 // ---------------------------------------------------------------- device
 typedef int v4i __attribute__((ext_vector_type(4)));

@@ -160,3 +160,34 @@ def test_full_size_sampled_rows(L):
     rows = np.unique(np.concatenate([[0, L.R - 1], rng.integers(0, L.R, 6)]))
     ref = reference(W, X, L.N, L.M, L.dt, L.out, bias=b, scale=s, rows=rows)
     compare(np.asarray(Y)[rows], ref, L.out, L.name)
+
+
+FAST_I8 = ["smfmac_i8_2of4_256x128"]
+
+
+@pytest.fixture
+def force_variant():
+    import os
+    old = os.environ.get("NM_SPMM_VARIANT")
+    yield lambda name: os.environ.__setitem__("NM_SPMM_VARIANT", name)
+    if old is None:
+        os.environ.pop("NM_SPMM_VARIANT", None)
+    else:
+        os.environ["NM_SPMM_VARIANT"] = old
+
+
+@pytest.mark.parametrize("variant", FAST_I8)
+@pytest.mark.parametrize("out", ["i8", "i32"])
+@pytest.mark.parametrize("R,K,T", [(300, 192, 144), (17, 4, 16), (256, 96, 1008), (520, 768, 400),
+                                   (3072, 768, 12608), (259, 1280, 272)])
+def test_fast_i8_variants(force_variant, variant, out, R, K, T):
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    force_variant(variant)
+    W, X, b, s = _inputs("i8", out, R, K, T, 2, 4, 8, f"fast-{variant}-{out}-{R}-{K}-{T}")
+    p = nm.pack(torch.from_numpy(W).cuda(), 2, 4)
+    assert nm.variant(p, T, torch.int8 if out == "i8" else torch.int32) == variant
+    Y, _ = run(W, X, 2, 4, "i8", out, bias=b, scale=s, ldx_pad=32, ldy_pad=16 if out == "i8" else 3,
+               sentinel=5)
+    compare(Y[:, :T], reference(W, X, 2, 4, "i8", out, bias=b, scale=s), out, variant)
+    assert np.all(Y[:, T:] == 5), "writes beyond T"
