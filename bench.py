@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--details", default="", help="write a JSON file of extra figures here")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB three times (a known-size "
+                         "reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -124,6 +127,13 @@ def main():
     L = _layers()[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     inp = nm_inputs.make_inputs(L, seed=0)
     tdt = {"i8": torch.int8, "f16": torch.float16, "bf16": torch.bfloat16}[L.dt]
     odt = {"i8": torch.int8, "i32": torch.int32, "f16": torch.float16, "bf16": torch.bfloat16,
