@@ -107,6 +107,7 @@ def main():
     ap.add_argument("--workload", default="vitb_fc1_2of4_i8")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--details", default="", help="write a JSON file of extra figures here")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB three times (a known-size "
@@ -184,24 +185,44 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step(i)
-    t_end.record()
-    torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
 
+    # The timed launches are captured once into a HIP graph and replayed, so
+    # the GPU runs them back to back without host launch gaps; the events
+    # bracket the replay on the stream the kernels run on, and the per-launch
+    # average is what rocprofv3's kernel trace reports for the same command.
+    def timed(seq):
+        graph = None
+        if not args.no_graph:
+            try:
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s):
+                    graph = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(graph, stream=s):
+                        for i in seq:
+                            step(i)
+                torch.cuda.current_stream().wait_stream(s)
+                torch.cuda.synchronize()
+                graph.replay()          # warm the graph once
+                torch.cuda.synchronize()
+            except Exception as ex:     # noqa: BLE001 - fall back to eager launches
+                print(f"bench.py: graph capture unavailable ({ex}); timing eager launches", file=sys.stderr)
+                graph = None
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in seq:
+                step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / len(seq), graph is not None
+
+    ms, graphed = timed(list(range(args.steps)))
     # warm (no rotation) figure, labelled as such
-    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0.record()
-    for _ in range(args.steps):
-        step(0)
-    w1.record()
-    torch.cuda.synchronize()
-    warm_ms = w0.elapsed_time(w1) / args.steps
+    warm_ms, _ = timed([0] * args.steps)
 
     # quick parity spot check of the timed configuration on sampled rows
     parity = None
@@ -256,7 +277,7 @@ def main():
                    "epilogue": "bias+requant" if L.out == "i8" else "none",
                    "parallelism": "single-gpu"},
         "roofline": roof, "cpu_baseline": cpu,
-        "kernel": variant, "rotation_sets": nsets, "warm_ms_per_step": round(warm_ms, 5),
+        "kernel": variant, "rotation_sets": nsets, "launch": "hip-graph" if graphed else "eager", "warm_ms_per_step": round(warm_ms, 5),
         "effective_GBps": round(nbytes / t_s / 1e9, 1), "pack_ms": round(pack_ms, 4),
         "parity": parity,
     }

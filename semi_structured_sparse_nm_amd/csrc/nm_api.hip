@@ -51,6 +51,7 @@ enum Variant {
   V_GENERIC,
   V_SMFMAC_I8,      // int8 2:4 sparse MFMA, 256 x 128 tile per workgroup
   V_SMFMAC_I8P,     // the same tile, persistent workgroups, cross-tile pipeline
+  V_SMFMAC_I8P8,    // persistent, 8-wave workgroups (512 x 128 tiles, one per CU)
   V_COUNT
 };
 
@@ -59,6 +60,7 @@ const char* variant_name(Variant v) {
     case V_GENERIC: return "generic_dense_expand";
     case V_SMFMAC_I8: return "smfmac_i8_2of4_256x128";
     case V_SMFMAC_I8P: return "smfmac_i8_2of4_persistent";
+    case V_SMFMAC_I8P8: return "smfmac_i8_2of4_persistent_w8";
     default: return "invalid";
   }
 }
@@ -76,12 +78,13 @@ bool eligible(Variant v, const Call& c) {
     case V_GENERIC: return true;
     case V_SMFMAC_I8:
     case V_SMFMAC_I8P:
+    case V_SMFMAC_I8P8:
       // 2:4 int8; X rows in whole 16-byte chunks; 32-bit buffer offsets,
       // which must not wrap for the rows a tile reaches past K and R (up to
-      // 128 k and 256 rows); int8 output stored as 16-byte row pieces
+      // 128 k and 512 rows); int8 output stored as 16-byte row pieces
       return c.wdt == NM_I8 && c.g->N == 2 && c.g->M == 4 && c.T % 16 == 0 && c.ldx % 16 == 0 &&
              aligned(c.X, 16) && (c.g->K + 128) * c.ldx < (1ll << 31) &&
-             c.g->values_bytes() < (1ull << 31) && (c.g->R + 256) * c.ldy * 4 < (1ll << 31) &&
+             c.g->values_bytes() < (1ull << 31) && (c.g->R + 512) * c.ldy * 4 < (1ll << 31) &&
              (c.ydt == NM_I32 || (c.ydt == NM_I8 && c.ldy % 16 == 0 && aligned(c.Y, 16)));
     default: return false;
   }
@@ -196,7 +199,8 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
   switch (v) {
     case V_GENERIC: e = nm::launch_spmm_generic(a, s); break;
     case V_SMFMAC_I8: e = nm::launch_spmm_smfmac_i8(a, 0, s); break;
-    case V_SMFMAC_I8P: e = nm::launch_spmm_smfmac_i8p(a, s); break;
+    case V_SMFMAC_I8P: e = nm::launch_spmm_smfmac_i8p(a, 0, s); break;
+    case V_SMFMAC_I8P8: e = nm::launch_spmm_smfmac_i8p(a, 1, s); break;
     default: return NM_EINVAL;
   }
   return e == hipSuccess ? NM_OK : NM_EHIP;

@@ -8,31 +8,40 @@
 //
 // Scheduling (the kernel side of "Realizable N:M Sparse Transformer Inference
 // via Search-Kernel Co-Design", Sec. 4.1, adaptive parallelism, taken to the
-// launch level): two workgroups per CU stay resident and walk a list of
-// 256 x 128 output tiles.  Their loads form one continuous stream over
-// (tile, 128-column block) pairs, one block ahead of the compute, so the first
-// block of the next tile is in flight while the current tile's last block is
-// multiplied and requantised; no tile starts cold.
+// launch level): NW-wave workgroups stay resident (two waves per SIMD) and
+// walk a list of (64 NW) x 128 output tiles.  Their loads form one continuous
+// stream over (tile, 128-column block) pairs, two blocks ahead of the compute
+// (three X stages in LDS, three register sets of A fragments), so the next
+// tile's first blocks are in flight while the current tile is multiplied and
+// requantised; no tile starts cold.
 //
-// Waits: every step starts with vmcnt(0) -- all loads and stores issued
-// before it, at least one step earlier, are complete -- and a barrier.  The
-// count is exact on every path, so the compiler's own waitcnt insertion
-// (which sees the register loads) needs no extra waits inside the step.
-// The direct-to-LDS loads are inline asm and invisible to that pass; were
-// they visible it would wait for all of them before every LDS read, because
-// it cannot tell which LDS array such a load writes.
+// Waits.  Vector memory operations complete in issue order (one vmcnt
+// counter).  Block n's loads L(n) are a fixed group: A fragments (8 register
+// loads) first, then the X stage and the tile's bias / scale rows (direct-to-
+// LDS).  Step n waits until at most |L(n+1)| + (stores of the previous
+// epilogue) operations are outstanding, which is exactly "L(n) has landed",
+// then a barrier publishes every wave's part of the stage.  L(n+2) is issued
+// after the first token tile of block n is multiplied: by then the compiler's
+// own waits for the A(n) registers are placed, and they count only the
+// register loads it can see (A(n+1) and the stores), so they hold back at
+// most A(n+1), issued a whole block earlier -- never an X stage.
 //
 // Tile order: each XCD (dispatch is round-robin over 8 XCDs) owns a
 // contiguous range of tiles, row tile fastest; its workgroups sweep that
 // range together, so the row tiles of one 128-token strip of X run at about
 // the same time on one XCD and the strip comes from HBM once into its L2.
 //
-// Epilogue (int8 output): f32(acc + bias[r]) * scale[r] (a separately
-// rounded product), clamp to [-128, 127], add 1.5 * 2^23 so the low byte is
-// the round-half-even int8, written as a byte into a per-wave row-major LDS
-// staging area (16-byte chunks XOR-swizzled by row so the byte writes and the
-// 16-byte reads spread over the banks), then stored as 16-byte pieces, eight
-// lanes per 128-byte row segment.  int32 output: acc + bias, direct stores.
+// Epilogue (int8 output), per half tile (64 tokens): f32(acc) * scale[r] (a
+// separately rounded product; the bias is the accumulator's start value),
+// clamp to [-128, 127], add 1.5 * 2^23 so the low byte is the round-half-even
+// int8; the four rows a lane holds for one token are packed into a dword, the
+// four row blocks' dwords of one token into 16 bytes, written token-major to
+// a per-wave LDS area (16-byte chunk c of token t stored at c ^ f(t), which
+// keeps the 16-byte writes and the transpose reads conflict-free), then read
+// back with ds_read_b64_tr_b8 so each lane holds 16 consecutive tokens of one
+// row and stores them as one 16-byte piece; the four lane groups of a store
+// cover 64 consecutive bytes of the same 16 rows.  int32 output: acc (bias
+// included) stored directly.
 #include "nm_common.hpp"
 
 namespace nm {
@@ -87,22 +96,28 @@ __device__ __forceinline__ v2i lds_tr8(const uint8_t* p) {
 
 constexpr int RB = 4;              // row blocks (16 rows) per wave
 constexpr int TN = 8;              // token tiles (16 tokens) per wave
-constexpr int NW = 4;              // waves per workgroup, stacked over rows
-constexpr int BM = NW * RB * 16;   // 256 rows per tile
 constexpr int BN = TN * 16;        // 128 tokens per tile
-[[maybe_unused]] constexpr int QB = 128 * 32;       // bytes per 32-token quarter of an X stage
 constexpr int STAGE = 128 * BN;    // bytes per X stage (16 KB)
-[[maybe_unused]] constexpr int DPW = STAGE / 1024 / NW;   // direct-to-LDS loads per wave per block (4)
+constexpr int NS_I8 = 8;           // global stores of one int8 epilogue, per lane
 
-template <bool OUT_I8>
-__global__ void __launch_bounds__(256, 2) smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles,
-                                                            int nwg_xcd) {
+template <int NW, bool OUT_I8>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   // device pass only (device-only types and builtins)
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = NW * RB * 16;           // rows per tile
+  constexpr int DPW = STAGE / 1024 / NW;     // 1 KB direct-to-LDS loads per wave per block
+  // one group of loads per block and wave: A values + meta, X (+ bias and
+  // scale on a tile's first block)
+  constexpr int NL = 2 * RB + DPW;
+  constexpr int NS = OUT_I8 ? NS_I8 : 63;
+  constexpr int WAIT_PEND = (NL + NS) < 63 ? (NL + NS) : 63;
+
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ostage[OUT_I8 ? NW * 64 * 128 : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t bsbuf[NW * 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs2[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ostage[OUT_I8 ? NW * 4096 : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t bsbuf[NW * 4 * 512];
 
   const Geometry& g = a.g;
   const int lane = threadIdx.x & 63;
@@ -121,6 +136,7 @@ __global__ void __launch_bounds__(256, 2) smfmac_i8p_kernel(SpmmArgs a, int mtil
   const int hi = min(lo + per_xcd, ntot);
   if (lo + jw >= hi) return;
   const int nmine = (hi - lo - jw + nwg_xcd - 1) / nwg_xcd;
+  const int total = nmine * nKB;              // blocks this workgroup computes
   auto tile_of = [&](int k, int& r0, int& t0) {
     const int L = lo + jw + k * nwg_xcd;
     const int nt = L / mtiles;
@@ -137,145 +153,223 @@ __global__ void __launch_bounds__(256, 2) smfmac_i8p_kernel(SpmmArgs a, int mtil
   const v4i rbias = make_rsrc(a.bias, a.bias ? (int)(g.R * 4) : 0);
   const v4i rscale = make_rsrc(a.scale, a.scale ? (int)(g.R * 4) : 0);
 
-  // ---- X block loads.  Load d of a block (wave w issues d = w DPW + j)
-  // covers quarter d / 4, rows 32 (d % 4) .. + 31; lane l -> row 32 (d % 4) +
-  // l / 2, stored half l % 2, global half (l % 2) ^ (row bit 4).  The tile's
-  // first token and the block's first row go into the scalar offset.
-  int xoff[DPW];
-#pragma unroll
-  for (int j = 0; j < DPW; ++j) {
+  // ---- X block loads.  An X stage is 128 rows (k) of 128 bytes (tokens);
+  // the 16-byte chunk of tokens 16 c .. + 15 of row r sits at position
+  // c ^ f(r), f(r) = (r & 7) ^ ((r >> 4) & 1), which makes the transpose
+  // reads below conflict-free.  Load d of a block (wave w issues d = w DPW
+  // + j) fills rows 8 d .. 8 d + 7: lane l -> row 8 d + l / 8, position
+  // l % 8, so every load reads eight whole 128-byte row segments.  The
+  // tile's first token and the block's first row go into the scalar offset.
+  auto xoff = [&](int j) {
     const int d = wave * DPW + j;
-    const int row = 32 * (d & 3) + (lane >> 1);
-    const int c = (lane & 1) ^ ((row >> 4) & 1);
-    xoff[j] = row * ldx + 32 * (d >> 2) + 16 * c;
-  }
-  auto xstage = [&](auto st) -> uint8_t* { return decltype(st)::value == 0 ? xs0 : xs1; };
-  auto load_x = [&](auto st, int kb, int t0) {
-    uint8_t* sp = xstage(st);
-    const int soff = __builtin_amdgcn_readfirstlane(kb * 128 * ldx + t0);
-#pragma unroll
-    for (int j = 0; j < DPW; ++j) {
-      const int d = wave * DPW + j;
-      lds_dma16(rx, lds_addr(sp + (d >> 2) * QB + (d & 3) * 1024), xoff[j], soff);
-    }
+    const int row = 8 * d + (lane >> 3);
+    const int c = (lane & 7) ^ (row & 7) ^ ((row >> 4) & 1);
+    return row * ldx + 16 * c;
+  };
+  auto xstage = [&](auto st) -> uint8_t* {
+    constexpr int S = decltype(st)::value;
+    return S == 0 ? xs0 : (S == 1 ? xs1 : xs2);
   };
 
   // ---- A fragments (lane (i, g): 16 bytes at row i, offset 16 g of a block,
-  // meta dword g of row i) of row blocks rb0 .. rb0 + RB - 1, rb0 counting
-  // in this wave's 64-row offset
+  // meta dword g of row i) of this wave's row blocks
   const int voff_v = li * 64 + lg * 16;
   const int voff_m = li * 16 + lg * 4;
-  v4i av[2][RB];
-  int ai[2][RB];
-  auto load_a = [&](v4i* v, int* ix, int kb, int rb0) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      // row blocks past the matrix read past the end (zeros), without
-      // letting the offset wrap
-      const int blk = __builtin_amdgcn_readfirstlane(rb0 + rb < nRB ? (rb0 + rb) * nKB + kb : nRB * nKB);
-      v[rb] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, blk * 1024, 0));
-      ix[rb] = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, voff_m, blk * 256, 0);
-    }
-  };
+  v4i av[3][RB];
+  int ai[3][RB];
 
-  v4i acc[RB][TN];
-  // transpose-read bases: row kq + (li >> 1) of a quarter, half li & 1,
-  // stored 16-byte half c ^ (lg & 1); kq = 16 lg (+8, +64, +72)
-  const int rbase = 32 * (16 * lg + (li >> 1)) + 8 * (li & 1);
-  const int tb0 = rbase + 16 * (lg & 1);
-  const int tb1 = rbase + 16 * ((lg & 1) ^ 1);
-  auto bfrag = [&](const uint8_t* sb, int tt) -> v8i {
-    const uint8_t* p = sb + (tt >> 1) * QB + ((tt & 1) ? tb1 : tb0);
-    const v2i p0 = lds_tr8(p);
-    const v2i p1 = lds_tr8(p + 8 * 32);
-    const v2i p2 = lds_tr8(p + 64 * 32);
-    const v2i p3 = lds_tr8(p + 72 * 32);
-    return v8i{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-  };
-  // bias and scale of a tile's rows go to LDS by direct-to-LDS loads (4
-  // bytes per lane: this wave's 64 rows), double-buffered by tile parity,
-  // issued one tile ahead; rows past R and absent vectors read as zero.
-  // Tile k's bias is read at its first block (it is the accumulator's start
-  // value), its scale at its epilogue.
-  uint8_t* const bsw = bsbuf + wave * 1024;
-  auto load_bias_scale = [&](int k, int r0) {
-    uint8_t* bs = bsw + 512 * (k & 1);
-    const int soff = __builtin_amdgcn_readfirstlane(4 * (r0 + 64 * wave));
-    lds_dma4(rbias, lds_addr(bs), 4 * lane, soff);
-    if constexpr (OUT_I8) lds_dma4(rscale, lds_addr(bs + 256), 4 * lane, soff);
-  };
+  // bias and scale of a tile's rows (4 bytes per lane: this wave's 64 rows),
+  // loaded with the tile's first block into one LDS slot per tile index mod
+  // 4, so a slot is rewritten only after its tile's epilogue; rows past R
+  // and absent vectors read as zero.
+  uint8_t* const bsw = bsbuf + wave * 2048;
   auto bias_vec = [&](int k, int rb) {
-    return *reinterpret_cast<const v4i*>(bsw + 512 * (k & 1) + 4 * (16 * rb + 4 * lg));
+    return *reinterpret_cast<const v4i*>(bsw + 512 * (k & 3) + 4 * (16 * rb + 4 * lg));
   };
   auto scale_vec = [&](int k, int rb) {
-    return *reinterpret_cast<const v4f*>(bsw + 512 * (k & 1) + 256 + 4 * (16 * rb + 4 * lg));
+    return *reinterpret_cast<const v4f*>(bsw + 512 * (k & 3) + 256 + 4 * (16 * rb + 4 * lg));
   };
 
-  // acc += A x B over one block (FIRST: acc = A x B + bias, the bias, read
-  // per use as an LDS broadcast, as the accumulator input).  The B fragment
-  // of token tile tt + 1 is read before the products of tile tt are issued,
-  // so the transpose reads' latency hides behind this wave's own SMFMACs.
-  auto compute = [&](auto st, auto first, const v4i* A, const int* I, int kn) {
-    constexpr bool FIRST = decltype(first)::value != 0;
-    const uint8_t* sb = xstage(st);
-    v8i bcur = bfrag(sb, 0);
+  // ---- load cursor: tile lk (rows lr0, tokens lt0), block lkb; ln groups
+  // issued.  A group is issued in parts between the token tiles of a block:
+  // part rb < RB the A fragment of row block rb, then the X loads in two
+  // halves, then (first block of a tile) bias and scale.  Groups past the
+  // end (at most two) still issue their A and X loads, reading nothing but
+  // zeros into a stage and register set nobody reads again, so every group
+  // but a tile's first has the same size.
+  int ln = 0, lk = 0, lkb = 0, lr0 = 0, lt0 = 0;
+  tile_of(0, lr0, lt0);
+  int g_live = 0, g_rb0 = 0, g_soff = 0;
+  auto load_part = [&](auto st, auto part) {
+    constexpr int S = decltype(st)::value;
+    constexpr int P = decltype(part)::value;
+    if constexpr (P == 0) {
+      g_live = __builtin_amdgcn_readfirstlane(ln < total ? 1 : 0);
+      g_rb0 = (lr0 >> 4) + RB * wave;
+      g_soff = __builtin_amdgcn_readfirstlane(g_live ? lkb * 128 * ldx + lt0 : (int)(g.K * a.ldx));
+    }
+    if constexpr (P < RB) {
+      // A first: the compiler's waits for these registers may then hold
+      // back at most later A loads, never an X stage.  Row blocks past the
+      // matrix read past the end (zeros).
+      const int rbc = __builtin_amdgcn_readfirstlane(min(g_rb0 + P, nRB));
+      const int blk = (g_live ? rbc : nRB) * nKB + (rbc < nRB ? lkb : 0);
+      av[S][P] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, blk * 1024, 0));
+      ai[S][P] = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, voff_m, blk * 256, 0);
+    } else if constexpr (P == RB || P == RB + 1) {
+      uint8_t* sp = xstage(st);
+      constexpr int H = DPW / 2, J0 = (P - RB) * H;
 #pragma unroll
-    for (int tt = 0; tt < TN; ++tt) {
-      v8i bnext;
-      if (tt + 1 < TN) bnext = bfrag(sb, tt + 1);
+      for (int j = J0; j < J0 + H; ++j) {
+        const int d = wave * DPW + j;
+        lds_dma16(rx, lds_addr(sp + d * 1024), xoff(j), g_soff);
+      }
+    } else {
+      if (g_live && lkb == 0) {
+        uint8_t* bs = bsw + 512 * (lk & 3);
+        const int boff = __builtin_amdgcn_readfirstlane(4 * (lr0 + 64 * wave));
+        lds_dma4(rbias, lds_addr(bs), 4 * lane, boff);
+        lds_dma4(rscale, lds_addr(bs + 256), 4 * lane, boff);
+      }
+      ++ln;
+      if (g_live && ++lkb == nKB) {
+        lkb = 0;
+        if (++lk < nmine) tile_of(lk, lr0, lt0);
+      }
+    }
+  };
+  constexpr int NPART = RB + 3;
+  auto load_group = [&](auto st) {
+    load_part(st, ic<0>()); load_part(st, ic<1>()); load_part(st, ic<2>()); load_part(st, ic<3>());
+    load_part(st, ic<4>()); load_part(st, ic<5>()); load_part(st, ic<6>());
+  };
+  static_assert(RB == 4 && NPART == 7, "load parts are spelled out for four row blocks");
+  // groups issued so far have sizes NL (plus 2 on a live tile's first block)
+  auto group_size_extra = [&](int m) { return (m < total && m % nKB == 0) ? 2 : 0; };
+
+  v4i acc[RB][TN];
+  // transpose reads of token tile tt: lane (i, g) reads row r = kq + 16 g +
+  // i / 2 (kq = 0, 8, 64, 72), tokens 16 tt + 8 (i & 1) .. + 7, i.e. chunk tt
+  // at position tt ^ f(r) = tt ^ (i / 2) ^ (g & 1).  Of the two lane groups
+  // served together, one reads positions of one parity on even rows and the
+  // other the opposite parity, so the 32 lanes cover all 64 banks once.
+  const int rbase = 128 * (16 * lg + (li >> 1)) + 8 * (li & 1);
+  const int tsw = (li >> 1) ^ (lg & 1);
+  // rbase has no bits 4..6, so rbase + 16 (tt ^ tsw) = xb ^ 16 tt; the
+  // empty asm keeps the compiler from hoisting eight per-tile addresses
+  // (registers are scarce in the main loop)
+  const int xb = rbase | (16 * tsw);
+  auto bfrag = [&](const uint8_t* sb, int tt) -> v8i {
+    int o = xb ^ (16 * tt);
+    asm volatile("" : "+v"(o));
+    const uint8_t* p = sb + o;
+    const v2i p0 = lds_tr8(p);
+    const v2i p1 = lds_tr8(p + 8 * 128);
+    const v2i p2 = lds_tr8(p + 64 * 128);
+    const v2i p3 = lds_tr8(p + 72 * 128);
+    return v8i{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  };
+
+  // acc += A x B over one block (acc starts a tile at the tile's bias).  B
+  // fragments are read two token tiles ahead of their products; the next
+  // load group is issued right after the first token tile's products (see
+  // the header on waits).  One code path for every block: a second variant
+  // for a tile's first block would give the compiler's load-wait bookkeeping
+  // merged paths on which the A registers look freshly loaded, and it then
+  // waits for every load in flight.
+  auto compute = [&](auto st, auto ast, auto nxt) {
+    constexpr int AS = decltype(ast)::value;
+    const uint8_t* sb = xstage(st);
+    v8i bf[3];
+#pragma unroll
+    for (int tt = 0; tt < 3; ++tt) bf[tt] = bfrag(sb, tt);
+    auto tile = [&](auto ttc) {
+      constexpr int tt = decltype(ttc)::value;
+      if constexpr (tt >= 1 && tt + 2 < TN) bf[(tt + 2) % 3] = bfrag(sb, tt + 2);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        acc[rb][tt] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(A[rb], bcur, FIRST ? bias_vec(kn, rb) : acc[rb][tt],
-                                                               I[rb], 0, 0);
-      if (tt + 1 < TN) bcur = bnext;
-    }
-    // issue order: reads of tile 0, then (reads of tile tt + 1, products of
-    // tile tt), then the products of the last tile
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        acc[rb][tt] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(av[AS][rb], bf[tt % 3], acc[rb][tt], ai[AS][rb], 0, 0);
+      // one part of the next load group after each token tile but the last
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (tt < NPART) load_part(nxt, ic<tt>());
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    static_assert(TN == 8 && NPART < TN, "token tiles are spelled out");
+    tile(ic<0>()); tile(ic<1>()); tile(ic<2>()); tile(ic<3>());
+    tile(ic<4>()); tile(ic<5>()); tile(ic<6>()); tile(ic<7>());
+  };
+  // acc = bias of tile k (this wave's own bias rows, loaded with the tile's
+  // first group; the caller has waited for that group)
+  auto init_acc = [&](int k) {
 #pragma unroll
-    for (int tt = 0; tt + 1 < TN; ++tt) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+    for (int rb = 0; rb < RB; ++rb) {
+      const v4i b = bias_vec(k, rb);
+#pragma unroll
+      for (int tt = 0; tt < TN; ++tt) acc[rb][tt] = b;
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
   };
 
-  // int8 output staging: this wave's 64 rows x 128 tokens, row-major, the
-  // 16-byte chunk c of row rl at position c ^ ((rl >> 2) & 7), so that the
-  // byte writes of one instruction (16 tokens x 4 row groups) and the 16-byte
-  // reads (8 whole rows) spread over all banks.  Byte (row 16 rb + 4 lg + v,
-  // token 16 tt + li) sits at obase[tt & 3] + an immediate.
-  uint8_t* const os = ostage + wave * (64 * 128);
-  const int c8 = lane & 7;
-  int obase[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) obase[j] = 512 * lg + 16 * (j ^ lg) + li;
-  // requantise acc[rb][tt] (bias already in it): f32(acc) * scale, separately
-  // rounded; clamp to [-128, 127]; + 1.5 * 2^23 leaves the round-half-even
-  // integer in the low byte
-  auto requant = [&](int rb, int tt, v4f sv) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float f = __fmul_rn((float)acc[rb][tt][v], sv[v]);
-      f = __builtin_amdgcn_fmed3f(f, -128.0f, 127.0f);
-      os[obase[tt & 3] + 2048 * rb + 128 * v + 16 * ((tt & 4) ^ (4 * (rb & 1)))] =
-          (uint8_t)__builtin_bit_cast(uint32_t, f + 12582912.0f);
+  // ---- int8 epilogue staging: this wave's 4 KB, 64 tokens x 64 row
+  // positions; row 16 rb + 4 g + v of the wave is position 16 g + 4 rb + v,
+  // so one lane's four row blocks of one token are 16 contiguous bytes.
+  // Chunk c (positions 16 c .. + 15) of token t sits at c ^ f(t),
+  // f(t) = bit 2 of t | (bit 4 of t) << 1.
+  uint8_t* const os = ostage + (OUT_I8 ? wave * 4096 : 0);
+  auto epilogue_i8 = [&](int k, int r0, int t0) __attribute__((always_inline)) {
+    // writes: token 16 u + li (u = 0..3), chunk lg
+    int wb[2];
+  #pragma unroll
+    for (int par = 0; par < 2; ++par) wb[par] = 64 * li + 16 * (lg ^ ((li >> 2) & 1) ^ (par << 1));
+    // transpose reads: lane 16 G + 2 i + h reads token 16 G + 8 e + i, chunk
+    // q ^ f, byte 8 h; output lane l of group G then holds position 16 q + l,
+    // i.e. row 16 (l >> 2) + 4 q + (l & 3), tokens 16 G + 8 e .. + 7
+    int rq[4];
+    {
+      const int i = (li >> 1) & 7, h = li & 1;
+      const int f = ((i >> 2) & 1) | ((lg & 1) << 1);
+  #pragma unroll
+      for (int q = 0; q < 4; ++q) rq[q] = 1024 * lg + 64 * i + 16 * (q ^ f) + 8 * h;
     }
-  };
-  // staged rows -> Y: piece k is row 8 k + lane / 8 of this wave, tokens
-  // 16 (lane % 8) .. + 15, eight lanes per 128-byte row segment
-  auto store_staged = [&](int r0, int t0) {
+    const int orow = 16 * (li >> 2) + (li & 3);   // + 4 q: this lane's output row in the wave
     const __amdgpu_buffer_rsrc_t ry =
         __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)(g.R * a.ldy), 0x00020000);
-    const bool tok_ok = t0 + 16 * c8 < a.T;
+    const int oob = (int)(g.R * a.ldy);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int rl = 8 * k + (lane >> 3);
-      const v4i piece = *reinterpret_cast<const v4i*>(os + rl * 128 + 16 * (c8 ^ ((rl >> 2) & 7)));
-      if (tok_ok)
-        __builtin_amdgcn_raw_buffer_store_b128(piece, ry, (r0 + 64 * wave + rl) * (int)a.ldy + t0 + 16 * c8, 0, 0);
-      // a few pieces in flight at a time (registers)
-      if (k & 1) __builtin_amdgcn_sched_barrier(0);
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int tt = 4 * h + u;
+        int d[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const v4f sv = scale_vec(k, rb);
+          uint32_t b[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float f = __fmul_rn((float)acc[rb][tt][v], sv[v]);
+            f = __builtin_amdgcn_fmed3f(f, -128.0f, 127.0f);
+            b[v] = __builtin_bit_cast(uint32_t, f + 12582912.0f);
+          }
+          const uint32_t lo2 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+          const uint32_t hi2 = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
+          d[rb] = (int)(lo2 | hi2);
+        }
+        *reinterpret_cast<v4i*>(os + 1024 * u + wb[u & 1]) = v4i{d[0], d[1], d[2], d[3]};
+      }
+      // the wave reads back only what it wrote (LDS operations of one wave
+      // complete in order)
+      // every lane stores (fixed operation count for the waits); pieces past
+      // T go to an offset past the buffer's end, which the range check drops
+      const int tok = t0 + 64 * h + 16 * lg;
+      const bool tok_ok = tok < a.T;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v2i x0 = lds_tr8(os + rq[q]);
+        const v2i x1 = lds_tr8(os + rq[q] + 512);
+        const int row = r0 + 64 * wave + orow + 4 * q;
+        const int off = tok_ok ? row * (int)a.ldy + tok : oob;
+        __builtin_amdgcn_raw_buffer_store_b128(v4i{x0[0], x0[1], x1[0], x1[1]}, ry, off, 0, 0);
+      }
     }
   };
   // int32 output: acc (bias included) stored directly
@@ -283,122 +377,130 @@ __global__ void __launch_bounds__(256, 2) smfmac_i8p_kernel(SpmmArgs a, int mtil
     const __amdgpu_buffer_rsrc_t ry =
         __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)(g.R * a.ldy * 4), 0x00020000);
     const int rw = r0 + 64 * wave + 4 * lg;
+    const int oob = (int)(g.R * a.ldy * 4);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int tt = 0; tt < TN; ++tt) {
-        if (t0 + 16 * tt >= a.T) break;
         const int t = t0 + 16 * tt + li;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          __builtin_amdgcn_raw_buffer_store_b32(acc[rb][tt][v], ry, 4 * ((rw + 16 * rb + v) * (int)a.ldy + t),
-                                                0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(
+              acc[rb][tt][v], ry, t0 + 16 * tt < a.T ? 4 * ((rw + 16 * rb + v) * (int)a.ldy + t) : oob, 0, 0);
       }
   };
 
-  // int8 epilogue of tile k (rows r0, tokens t0)
-  auto epilogue_i8 = [&](int k, int r0, int t0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const v4f sv = scale_vec(k, rb);
-#pragma unroll
-      for (int tt = 0; tt < TN; ++tt) requant(rb, tt, sv);
-    }
-    store_staged(r0, t0);
-  };
-
-  // ---- cursors.  Compute: tile ck (rows cr0, tokens ct0), block ckb.  The
-  // loads run one block ahead: tile lk, block lkb.
-  int ck = 0, ckb = 0, cr0, ct0;
+  // ---- compute cursor: tile ck (rows cr0, tokens ct0), block ckb; block n
+  int n = 0, ck = 0, ckb = 0, cr0, ct0;
   tile_of(0, cr0, ct0);
-  int lk = 0, lkb = 0, lr0 = cr0, lt0 = ct0;
-  auto load_next = [&](auto st) {
-    if (lk >= nmine) return;
-    load_x(st, lkb, lt0);
-    load_a(av[decltype(st)::value], ai[decltype(st)::value], lkb, (lr0 >> 4) + RB * wave);
-    if (++lkb == nKB) {
-      lkb = 0;
-      if (++lk < nmine) tile_of(lk, lr0, lt0);
+  bool pend = false;   // an epilogue's stores were issued after the latest group
+
+  // wait until L(m) has landed, given the group issued after it (its
+  // size: NL, plus 2 when it starts a live tile) and whether an epilogue's
+  // stores were issued after that
+  auto wait_for_group = [&](int extra_after, bool stores_after) {
+    if (stores_after) {
+      if (extra_after)
+        __builtin_amdgcn_s_waitcnt(waitcnt(WAIT_PEND + 2 < 63 ? WAIT_PEND + 2 : 63, 15));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt(WAIT_PEND, 15));
+    } else {
+      if (extra_after)
+        __builtin_amdgcn_s_waitcnt(waitcnt(NL + 2, 15));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
     }
   };
 
-  // prologue: bias / scale of tile 0, block 0
-  load_bias_scale(0, cr0);
-  load_next(ic<0>());
+  load_group(ic<0>());
+  load_group(ic<1>());
+  // tile 0's bias (group 0) has landed once group 1 is all that is left
+  wait_for_group(group_size_extra(1), false);
+  init_acc(0);
 
-  // One block on stage / register set ST (the next block goes to the
-  // other).  Every step starts by waiting for all loads and stores issued
-  // before it (at least one step earlier) and a barrier.
-  bool done = false;
+  // One block: stage / register set ST = n % 3; its loads were issued two
+  // steps ago (or in the prologue).
   auto step = [&](auto st) {
     constexpr int ST = decltype(st)::value;
-    __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
+    constexpr int NX = (ST + 2) % 3;
+    // groups past the end are issued too (see load_group), so L(n + 1) is
+    // always in flight behind L(n)
+    wait_for_group(group_size_extra(n + 1), pend);
     barrier_nofence();
-    load_next(ic<ST ^ 1>());
-    if (ckb == 0) {
-      compute(st, ic<1>(), av[ST], ai[ST], ck);
-      // tile ck - 1's bias / scale are read: their buffer takes tile ck + 1's
-      if (ck + 1 < nmine) {
-        int nr0, nt0;
-        tile_of(ck + 1, nr0, nt0);
-        __builtin_amdgcn_s_waitcnt(waitcnt(63, 0));
-        load_bias_scale(ck + 1, nr0);
-      }
-    } else {
-      compute(st, ic<0>(), av[ST], ai[ST], ck);
-    }
+    pend = false;
+    compute(st, ic<ST>(), ic<NX>());
+    ++n;
     if (++ckb < nKB) return;
     ckb = 0;
     if constexpr (OUT_I8)
       epilogue_i8(ck, cr0, ct0);
     else
       store_i32(cr0, ct0);
-    if (++ck == nmine) {
-      done = true;
-      return;
+    pend = true;
+    ++ck;
+    if (ck < nmine) {
+      tile_of(ck, cr0, ct0);
+      // the next tile's bias rows arrive with its first group, L(n); the
+      // group after it and the epilogue's stores may still be in flight
+      wait_for_group(group_size_extra(n + 1), true);
+      init_acc(ck);
     }
-    tile_of(ck, cr0, ct0);
   };
-  for (;;) {
+  // The trip count is known up front, so every exit is a plain counter
+  // test: no path from a step's end leads back to the loop head except the
+  // real back edge (the compiler's own load-wait bookkeeping merges the
+  // states of every edge into the head).
+  const int trips = total / 3, rest = total - 3 * trips;
+  for (int it = 0; it < trips; ++it) {
     step(ic<0>());
-    if (done) break;
     step(ic<1>());
-    if (done) break;
+    step(ic<2>());
   }
+  if (rest > 0) step(ic<0>());
+  if (rest > 1) step(ic<1>());
   __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
 #endif
 }
 
-int persistent_wgs(int device) {
+int cu_count(int device) {
   static int cache[64];
-  if (device < 0 || device >= 64) return 512;
+  if (device < 0 || device >= 64) return 256;
   if (!cache[device]) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
       cus = 256;
-    cache[device] = 2 * cus;   // two resident workgroups per CU
+    cache[device] = cus;
   }
   return cache[device];
 }
 
-}  // namespace
-
-hipError_t launch_spmm_smfmac_i8p(const SpmmArgs& a, hipStream_t s) {
+template <int NW>
+hipError_t launch_nw(const SpmmArgs& a, hipStream_t s) {
+  constexpr int BM = NW * RB * 16;
   const int mtiles = (int)((a.g.R + BM - 1) / BM);
   const int ntiles = (int)((a.T + BN - 1) / BN);
   const int ntot = mtiles * ntiles;
   const int per_xcd = (ntot + 7) / 8;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  int nwg_xcd = persistent_wgs(dev) / 8;
+  // two waves per SIMD: 8 / NW workgroups per CU
+  int nwg_xcd = cu_count(dev) * (8 / NW) / 8;
   if (nwg_xcd > per_xcd) nwg_xcd = per_xcd;
   if (nwg_xcd < 1) nwg_xcd = 1;
   const int grid = 8 * nwg_xcd;
   if (a.ydt == NM_I8)
-    hipLaunchKernelGGL((smfmac_i8p_kernel<true>), dim3(grid), dim3(256), 0, s, a, mtiles, ntiles, nwg_xcd);
+    hipLaunchKernelGGL((smfmac_i8p_kernel<NW, true>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles, nwg_xcd);
   else
-    hipLaunchKernelGGL((smfmac_i8p_kernel<false>), dim3(grid), dim3(256), 0, s, a, mtiles, ntiles, nwg_xcd);
+    hipLaunchKernelGGL((smfmac_i8p_kernel<NW, false>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles, nwg_xcd);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// cfg 0: 4-wave workgroups (256 x 128 tiles, two per CU); cfg 1: 8-wave
+// workgroups (512 x 128 tiles, one per CU)
+hipError_t launch_spmm_smfmac_i8p(const SpmmArgs& a, int cfg, hipStream_t s) {
+  return cfg == 1 ? launch_nw<8>(a, s) : launch_nw<4>(a, s);
 }
 
 }  // namespace nm

@@ -162,7 +162,7 @@ def test_full_size_sampled_rows(L):
     compare(np.asarray(Y)[rows], ref, L.out, L.name)
 
 
-FAST_I8 = ["smfmac_i8_2of4_256x128", "smfmac_i8_2of4_persistent"]
+FAST_I8 = ["smfmac_i8_2of4_256x128", "smfmac_i8_2of4_persistent", "smfmac_i8_2of4_persistent_w8"]
 
 
 @pytest.fixture
