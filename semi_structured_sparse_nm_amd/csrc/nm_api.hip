@@ -52,6 +52,7 @@ enum Variant {
   V_SMFMAC_I8,      // int8 2:4 sparse MFMA, 256 x 128 tile per workgroup
   V_SMFMAC_I8P,     // the same tile, persistent workgroups, cross-tile pipeline
   V_SMFMAC_I8P8,    // persistent, 8-wave workgroups (512 x 128 tiles, one per CU)
+  V_SMFMAC_H,       // fp16 / bf16 2:4 sparse MFMA, persistent 256 x 128 tiles
   V_COUNT
 };
 
@@ -61,6 +62,7 @@ const char* variant_name(Variant v) {
     case V_SMFMAC_I8: return "smfmac_i8_2of4_256x128";
     case V_SMFMAC_I8P: return "smfmac_i8_2of4_persistent";
     case V_SMFMAC_I8P8: return "smfmac_i8_2of4_persistent_w8";
+    case V_SMFMAC_H: return "smfmac_h_2of4_persistent";
     default: return "invalid";
   }
 }
@@ -86,6 +88,14 @@ bool eligible(Variant v, const Call& c) {
              aligned(c.X, 16) && (c.g->K + 128) * c.ldx < (1ll << 31) &&
              c.g->values_bytes() < (1ull << 31) && (c.g->R + 512) * c.ldy * 4 < (1ll << 31) &&
              (c.ydt == NM_I32 || (c.ydt == NM_I8 && c.ldy % 16 == 0 && aligned(c.Y, 16)));
+    case V_SMFMAC_H:
+      // fp16 / bf16 2:4; X rows in whole 16-byte pieces; 32-bit buffer
+      // offsets that do not wrap for the rows a tile reaches past K and R;
+      // 16-bit output stored as 16-byte row pieces
+      return (c.wdt == NM_F16 || c.wdt == NM_BF16) && c.g->N == 2 && c.g->M == 4 && c.T % 16 == 0 &&
+             c.ldx % 8 == 0 && aligned(c.X, 16) && (c.g->K + 64) * c.ldx * 2 < (1ll << 31) &&
+             c.g->values_bytes() < (1ull << 31) && (c.g->R + 256) * c.ldy * 4 < (1ll << 31) &&
+             (c.ydt == NM_F32 || (c.ldy % 8 == 0 && aligned(c.Y, 16)));
     default: return false;
   }
 }
@@ -97,6 +107,7 @@ Variant choose(const Call& c) {
       if (strcmp(force, variant_name((Variant)v)) == 0 && eligible((Variant)v, c)) return (Variant)v;
   }
   if (eligible(V_SMFMAC_I8P, c)) return V_SMFMAC_I8P;
+  if (eligible(V_SMFMAC_H, c)) return V_SMFMAC_H;
   return V_GENERIC;
 }
 
@@ -201,6 +212,7 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
     case V_SMFMAC_I8: e = nm::launch_spmm_smfmac_i8(a, 0, s); break;
     case V_SMFMAC_I8P: e = nm::launch_spmm_smfmac_i8p(a, 0, s); break;
     case V_SMFMAC_I8P8: e = nm::launch_spmm_smfmac_i8p(a, 1, s); break;
+    case V_SMFMAC_H: e = nm::launch_spmm_smfmac_h(a, s); break;
     default: return NM_EINVAL;
   }
   return e == hipSuccess ? NM_OK : NM_EHIP;

@@ -191,3 +191,27 @@ def test_fast_i8_variants(force_variant, variant, out, R, K, T):
                sentinel=5)
     compare(Y[:, :T], reference(W, X, 2, 4, "i8", out, bias=b, scale=s), out, variant)
     assert np.all(Y[:, T:] == 5), "writes beyond T"
+
+
+FAST_H = ["smfmac_h_2of4_persistent"]
+
+
+@pytest.mark.parametrize("variant", FAST_H)
+@pytest.mark.parametrize("dt,out", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("R,K,T", [(300, 192, 144), (17, 4, 16), (256, 96, 1008), (520, 768, 400),
+                                   (259, 1280, 272), (64, 4100, 32)])
+def test_fast_h_variants(force_variant, variant, dt, out, R, K, T):
+    """fp16 / bf16 2:4 sparse-MFMA kernel forced on ragged rows, partial
+    64-column blocks (K % 64 != 0), several token tiles and row strides."""
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    from tests._parity import TORCH_DT, dev
+    force_variant(variant)
+    W, X, b, s = _inputs(dt, out, R, K, T, 2, 4, 9, f"fasth-{dt}-{out}-{R}-{K}-{T}")
+    p = nm.pack(dev(W, dt), 2, 4)
+    assert nm.variant(p, T, TORCH_DT[out]) == variant
+    Y, _ = run(W, X, 2, 4, dt, out, bias=b, scale=s, ldx_pad=24, ldy_pad=8, sentinel=5)
+    compare(Y[:, :T], reference(W, X, 2, 4, dt, out, bias=b, scale=s), out, variant)
+    pad = Y[:, T:]
+    want = 5 if out != "bf16" else oracle.round_to(np.array([5.0]), "bf16")[0]
+    assert np.all(pad == want), "writes beyond T"
