@@ -53,6 +53,7 @@ enum Variant {
   V_SMFMAC_I8P,     // the same tile, persistent workgroups, cross-tile pipeline
   V_SMFMAC_I8P8,    // persistent, 8-wave workgroups (512 x 128 tiles, one per CU)
   V_SMFMAC_H,       // fp16 / bf16 2:4 sparse MFMA, persistent 256 x 128 tiles
+  V_SMFMAC_HD,      // fp16 / bf16 2:4, decode shapes (T <= 16): K split across 8 waves
   V_COUNT
 };
 
@@ -63,6 +64,7 @@ const char* variant_name(Variant v) {
     case V_SMFMAC_I8P: return "smfmac_i8_2of4_persistent";
     case V_SMFMAC_I8P8: return "smfmac_i8_2of4_persistent_w8";
     case V_SMFMAC_H: return "smfmac_h_2of4_persistent";
+    case V_SMFMAC_HD: return "smfmac_h_2of4_decode";
     default: return "invalid";
   }
 }
@@ -96,6 +98,12 @@ bool eligible(Variant v, const Call& c) {
              c.ldx % 8 == 0 && aligned(c.X, 16) && (c.g->K + 64) * c.ldx * 2 < (1ll << 31) &&
              c.g->values_bytes() < (1ull << 31) && (c.g->R + 256) * c.ldy * 4 < (1ll << 31) &&
              (c.ydt == NM_F32 || (c.ldy % 8 == 0 && aligned(c.Y, 16)));
+    case V_SMFMAC_HD:
+      // fp16 / bf16 2:4 with at most 16 tokens; X rows in whole 16-byte
+      // pieces; 32-bit buffer offsets that do not wrap past K
+      return (c.wdt == NM_F16 || c.wdt == NM_BF16) && c.g->N == 2 && c.g->M == 4 && c.T <= 16 &&
+             c.ldx % 8 == 0 && aligned(c.X, 16) && (c.g->K + 64) * c.ldx * 2 < (1ll << 31) &&
+             c.g->values_bytes() < (1ull << 31);
     default: return false;
   }
 }
@@ -107,6 +115,7 @@ Variant choose(const Call& c) {
       if (strcmp(force, variant_name((Variant)v)) == 0 && eligible((Variant)v, c)) return (Variant)v;
   }
   if (eligible(V_SMFMAC_I8P, c)) return V_SMFMAC_I8P;
+  if (eligible(V_SMFMAC_HD, c)) return V_SMFMAC_HD;
   if (eligible(V_SMFMAC_H, c)) return V_SMFMAC_H;
   return V_GENERIC;
 }
@@ -213,6 +222,7 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
     case V_SMFMAC_I8P: e = nm::launch_spmm_smfmac_i8p(a, 0, s); break;
     case V_SMFMAC_I8P8: e = nm::launch_spmm_smfmac_i8p(a, 1, s); break;
     case V_SMFMAC_H: e = nm::launch_spmm_smfmac_h(a, s); break;
+    case V_SMFMAC_HD: e = nm::launch_spmm_smfmac_hd(a, s); break;
     default: return NM_EINVAL;
   }
   return e == hipSuccess ? NM_OK : NM_EHIP;

@@ -215,3 +215,25 @@ def test_fast_h_variants(force_variant, variant, dt, out, R, K, T):
     pad = Y[:, T:]
     want = 5 if out != "bf16" else oracle.round_to(np.array([5.0]), "bf16")[0]
     assert np.all(pad == want), "writes beyond T"
+
+
+@pytest.mark.parametrize("dt,out", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("R,K,T", [(16, 64, 16), (17, 4, 1), (300, 200, 3), (96, 4100, 16), (40, 512, 8),
+                                   (33, 11008, 16)])
+def test_decode_h_variant(force_variant, dt, out, R, K, T):
+    """fp16 / bf16 2:4 decode kernel (K split over eight waves, partials summed
+    in LDS): fewer blocks than waves, partial blocks, ragged rows, T < 16."""
+    import semi_structured_sparse_nm_amd as nm
+    from tests._parity import TORCH_DT, dev
+    force_variant("smfmac_h_2of4_decode")
+    W, X, b, s = _inputs(dt, out, R, K, T, 2, 4, 10, f"dec-{dt}-{out}-{R}-{K}-{T}")
+    p = nm.pack(dev(W, dt), 2, 4)
+    # nm_spmm_variant assumes dense rows (ldx = T); the run pads X rows to a
+    # multiple of 8 elements, which the forced kernel needs
+    if T % 8 == 0:
+        assert nm.variant(p, T, TORCH_DT[out]) == "smfmac_h_2of4_decode"
+    Y, _ = run(W, X, 2, 4, dt, out, bias=b, scale=s, ldx_pad=(-T) % 8 + 8, ldy_pad=3, sentinel=5)
+    compare(Y[:, :T], reference(W, X, 2, 4, dt, out, bias=b, scale=s), out, "decode")
+    pad = Y[:, T:]
+    want = 5 if out != "bf16" else oracle.round_to(np.array([5.0]), "bf16")[0]
+    assert np.all(pad == want), "writes beyond T"
