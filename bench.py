@@ -99,6 +99,85 @@ def cpu_baseline(L, inp, target_s: float = 12.0):
                       f"(direct compressed-index loop + epilogue, {total:.1f} s)"}
 
 
+def run_stack(args):
+    """The 48-layer mixed-N:M ViT-B int8 stack (12 blocks x qkv / proj / fc1 /
+    fc2, per-layer N:M drawn with seed 0), run back to back on one stream.
+
+    Reports every layer's time (a HIP graph of `reps` launches of that layer
+    alone), their sum, and the time of one pass of the whole stack (a HIP
+    graph of the 48 launches in order, replayed).  Inputs are seeded int8
+    tensors drawn on the GPU (timing only; parity of every shape is covered
+    by the tests)."""
+    import torch
+
+    import nm_inputs
+    import semi_structured_sparse_nm_amd as nm
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    layers = nm_inputs.config4()
+    built = []
+    for i, L in enumerate(layers):
+        gen.manual_seed(1000 + i)
+        W = torch.randint(-127, 128, (L.R, L.K), dtype=torch.int8, device=dev, generator=gen)
+        X = torch.randint(-127, 128, (L.K, L.T), dtype=torch.int8, device=dev, generator=gen)
+        b = torch.randint(-2000, 2000, (L.R,), dtype=torch.int32, device=dev, generator=gen)
+        sc = torch.full((L.R,), 1.0 / 4096, dtype=torch.float32, device=dev)
+        p = nm.pack(W, L.N, L.M)
+        Y = torch.empty((L.R, L.T), dtype=torch.int8, device=dev)
+        built.append((L, p, X, b, sc, Y))
+    torch.cuda.synchronize()
+
+    def launch(item):
+        L, p, X, b, sc, Y = item
+        nm.spmm(p, X, bias=b, scale=sc, out_dtype=torch.int8, out=Y)
+
+    def graph_time(items, reps):
+        for it in items:
+            launch(it)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                for _ in range(reps):
+                    for it in items:
+                        launch(it)
+        torch.cuda.current_stream().wait_stream(st)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps      # microseconds per repetition
+
+    per = []
+    for it in built:
+        L = it[0]
+        us = graph_time([it], 20)
+        ops, nbytes, dense = nm_inputs.ops_and_bytes(L)
+        t_roof = max(nbytes / 8e12, ops / 5e15) * 1e6
+        per.append({"layer": L.name, "R": L.R, "K": L.K, "N": L.N, "M": L.M,
+                    "kernel": nm.variant(it[1], L.T, torch.int8), "us": round(us, 2),
+                    "t_roof_us": round(t_roof, 3), "roofline_fraction": round(t_roof / us, 4)})
+    pass_us = graph_time(built, 5)
+    dense_total = sum(nm_inputs.ops_and_bytes(L)[2] for L in layers)
+    roof_total = sum(r["t_roof_us"] for r in per)
+    out = {"stack": "vitb_int8_mixed_nm_48_layers", "tokens": nm_inputs.VIT_B_TOKENS,
+           "pass_us": round(pass_us, 1), "sum_of_layers_us": round(sum(r["us"] for r in per), 1),
+           "sum_of_rooflines_us": round(roof_total, 1), "roofline_fraction": round(roof_total / pass_us, 4),
+           "dense_equivalent_TOPS": round(dense_total / (pass_us * 1e-6) / 1e12, 1),
+           "layers": per}
+    text = json.dumps(out)
+    if args.details:
+        json.dump(out, open(args.details, "w"), indent=1)
+    print(text, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,12 +191,17 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB three times (a known-size "
                          "reference for HBM byte counters)")
+    ap.add_argument("--stack", action="store_true",
+                    help="time the 48-layer mixed-N:M ViT-B int8 stack instead of one layer")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the product shards by output rows or tokens with no exchange, but no "
               "multi-GPU launcher is provided", file=sys.stderr)
         sys.exit(2)
+    if args.stack:
+        run_stack(args)
+        return
 
     import numpy as np
     import torch
