@@ -54,6 +54,7 @@ enum Variant {
   V_SMFMAC_I8P8,    // persistent, 8-wave workgroups (512 x 128 tiles, one per CU)
   V_SMFMAC_H,       // fp16 / bf16 2:4 sparse MFMA, persistent 256 x 128 tiles
   V_SMFMAC_HD,      // fp16 / bf16 2:4, decode shapes (T <= 16): K split across 8 waves
+  V_EXPAND,         // any other N:M (int8, fp16, bf16): windows expanded in registers, dense MFMA
   V_COUNT
 };
 
@@ -65,6 +66,7 @@ const char* variant_name(Variant v) {
     case V_SMFMAC_I8P8: return "smfmac_i8_2of4_persistent_w8";
     case V_SMFMAC_H: return "smfmac_h_2of4_persistent";
     case V_SMFMAC_HD: return "smfmac_h_2of4_decode";
+    case V_EXPAND: return "expand_mfma_persistent";
     default: return "invalid";
   }
 }
@@ -104,6 +106,16 @@ bool eligible(Variant v, const Call& c) {
       return (c.wdt == NM_F16 || c.wdt == NM_BF16) && c.g->N == 2 && c.g->M == 4 && c.T <= 16 &&
              c.ldx % 8 == 0 && aligned(c.X, 16) && (c.g->K + 64) * c.ldx * 2 < (1ll << 31) &&
              c.g->values_bytes() < (1ull << 31);
+    case V_EXPAND:
+      // an instantiated N:M other than 2:4; whole 16-token tiles; X rows in
+      // whole 16-byte pieces; 32-bit buffer offsets that do not wrap for the
+      // rows a tile reaches past K and R (up to 128 k and 256 rows); 8- and
+      // 16-bit output stored as 16-byte row pieces
+      return nm::expand_supported(c.g->N, c.g->M) && !(c.g->N == 2 && c.g->M == 4) && c.T % 16 == 0 &&
+             c.ldx % (16 / c.g->eb) == 0 && aligned(c.X, 16) && (c.g->K + 128) * c.ldx * c.g->eb < (1ll << 31) &&
+             c.g->values_bytes() + 1024 < (1ull << 31) && c.g->meta_bytes() + 1024 < (1ull << 31) &&
+             (c.g->R + 256) * c.ldy * 4 < (1ll << 31) &&
+             (c.ydt == NM_I32 || c.ydt == NM_F32 || (c.ldy % (16 / nm::dtype_bytes(c.ydt)) == 0 && aligned(c.Y, 16)));
     default: return false;
   }
 }
@@ -117,6 +129,7 @@ Variant choose(const Call& c) {
   if (eligible(V_SMFMAC_I8P, c)) return V_SMFMAC_I8P;
   if (eligible(V_SMFMAC_HD, c)) return V_SMFMAC_HD;
   if (eligible(V_SMFMAC_H, c)) return V_SMFMAC_H;
+  if (eligible(V_EXPAND, c)) return V_EXPAND;
   return V_GENERIC;
 }
 
@@ -223,6 +236,7 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
     case V_SMFMAC_I8P8: e = nm::launch_spmm_smfmac_i8p(a, 1, s); break;
     case V_SMFMAC_H: e = nm::launch_spmm_smfmac_h(a, s); break;
     case V_SMFMAC_HD: e = nm::launch_spmm_smfmac_hd(a, s); break;
+    case V_EXPAND: e = nm::launch_spmm_expand(a, s); break;
     default: return NM_EINVAL;
   }
   return e == hipSuccess ? NM_OK : NM_EHIP;

@@ -1,0 +1,647 @@
+// Persistent N:M sparse x dense product for every N:M the sparse matrix
+// instructions do not take directly (1:4, 3:4, 1:8, 2:8, 4:8, N = M), int8
+// and fp16 / bf16, on the gfx950 dense matrix cores.
+//
+// This is the pages' micro-dense execution ("Realizable N:M Sparse
+// Transformer Inference via Search-Kernel Co-Design", Sec. 4.2): the kept
+// values of each window are placed at their positions inside a dense
+// fragment so the matrix core sees only regular dense operands, and the
+// irregularity stays in load and decode.  Here the decode is done in
+// registers, per lane, with compile-time N and M: each kept value's position
+// (log2(M) bits of the packed row's meta) becomes a shift inside its group's
+// 32- or 64-bit slice of the fragment.
+//
+// The k-to-lane assignment of the dense MFMA is free as long as both
+// operands use the same one.  Lane group g takes, over the two MFMA steps of
+// a packed block, the dense run [LR g, LR (g + 1)) (LR = 32 int8 / 16 fp16
+// elements): its kept values are one contiguous run of the packed row and
+// its positions one contiguous run of meta bits, so a lane loads its whole
+// share of a row block with one or two loads.  The B fragments (X) follow
+// the same assignment.
+//
+// Workgroups of eight waves (one per CU, two waves per SIMD), each wave 32
+// rows x 128 tokens, persistent over a per-XCD tile list; X in three LDS
+// stages by direct-to-LDS loads; A in three register sets; exact vmcnt
+// counts and one barrier per block, as in the 2:4 kernels.  Epilogues: int8
+// bias + requant, int32, fp16 / bf16 (LDS transpose and 16-byte row pieces),
+// fp32 (direct).
+#include "nm_common.hpp"
+
+namespace nm {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+template <int N> struct ic { static constexpr int value = N; };
+
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+constexpr int waitcnt(int vm, int lgkm) {
+  return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
+}
+__device__ __forceinline__ v4i make_rsrc(const void* p, int num_records) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  return v4i{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), num_records, 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(v4i rsrc, uint32_t lds, int voff, int soff) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(v4i rsrc, uint32_t lds, int voff, int soff) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ v2i lds_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(p));
+}
+__device__ __forceinline__ v2i lds_tr16(const uint8_t* p) {
+  return __builtin_bit_cast(
+      v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p)));
+}
+
+constexpr int RB = 2;              // row blocks (16 rows) per wave
+constexpr int TN = 8;              // token tiles (16 tokens) per wave
+constexpr int NW = 8;              // waves per workgroup, stacked over rows
+constexpr int BM = NW * RB * 16;   // 256 rows per tile
+constexpr int BN = TN * 16;        // 128 tokens per tile
+constexpr int STAGE = 16384;       // bytes per X stage (128 B of dense k x 128 tokens)
+constexpr int DPW = STAGE / 1024 / NW;
+
+// Per-dtype geometry: EB element bytes, LR dense elements per lane per
+// block, a step (one MFMA) covers LR / 2.
+template <int WT> struct Ty {
+  static constexpr int EB = (WT == NM_I8) ? 1 : 2;
+  static constexpr int LR = (WT == NM_I8) ? 32 : 16;
+};
+
+// Dense 16-byte A fragment of step S from a lane's packed run: vd holds the
+// run's kept values (element e at byte e EB), mb its positions (W bits each,
+// element e at bit e W).  Group q of the step occupies bytes q M EB .. of
+// the fragment.
+template <int WT, int NN, int MM, int S>
+__device__ __forceinline__ v4i expand_step(const uint32_t* vd, uint64_t mb) {
+  constexpr int EB = Ty<WT>::EB;
+  constexpr int RUN = Ty<WT>::LR / 2;             // dense elements per step
+  constexpr int G = RUN / MM;                     // groups per step
+  constexpr int KS = G * NN;                      // kept per step
+  constexpr int W = (NN == MM) ? 0 : (MM == 4 ? 2 : 3);
+  if constexpr (NN == MM) {
+    return v4i{(int)vd[4 * S], (int)vd[4 * S + 1], (int)vd[4 * S + 2], (int)vd[4 * S + 3]};
+  } else {
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      uint64_t lo = 0, hi = 0;                    // the group's 64 (or 128) bits
+#pragma unroll
+      for (int j = 0; j < NN; ++j) {
+        const int e = S * KS + q * NN + j;        // element of the lane's run
+        const uint32_t el = (vd[(e * EB) >> 2] >> (8 * ((e * EB) & 3))) & (EB == 1 ? 0xFFu : 0xFFFFu);
+        const uint32_t pos = (uint32_t)(mb >> (e * W)) & ((1u << W) - 1u);
+        if constexpr (MM * EB == 4) {
+          lo |= (uint64_t)(el << (8 * pos));
+        } else if constexpr (MM * EB == 8) {
+          lo |= (uint64_t)el << ((8 * EB) * pos);
+        } else {                                  // fp16, M = 8: 128 bits
+          const uint64_t sh = (uint64_t)el << (16 * (pos & 3));
+          lo |= (pos < 4) ? sh : 0;
+          hi |= (pos < 4) ? 0 : sh;
+        }
+      }
+      if constexpr (MM * EB == 4) {
+        o[q] = (uint32_t)lo;
+      } else if constexpr (MM * EB == 8) {
+        o[2 * q] = (uint32_t)lo;
+        o[2 * q + 1] = (uint32_t)(lo >> 32);
+      } else {
+        o[0] = (uint32_t)lo; o[1] = (uint32_t)(lo >> 32);
+        o[2] = (uint32_t)hi; o[3] = (uint32_t)(hi >> 32);
+      }
+    }
+    return v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+  }
+}
+
+template <int WT>
+__device__ __forceinline__ auto mfma(v4i a, v4i b, typename std::conditional<WT == NM_I8, v4i, v4f>::type c) {
+  if constexpr (WT == NM_I8)
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+  else if constexpr (WT == NM_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0,
+                                                   0, 0);
+}
+
+template <int OUT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (OUT == NM_F16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{lo, hi}), v2h));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{lo, hi}), v2bf));
+}
+
+template <int WT, int NN, int MM, int OUT>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr bool I8 = WT == NM_I8;
+  constexpr int EB = Ty<WT>::EB;
+  constexpr int LR = Ty<WT>::LR;
+  constexpr int KL = LR * NN / MM;                // kept per lane per block
+  constexpr int VB = KL * EB;                     // their bytes
+  constexpr int VD = VB / 4;
+  constexpr int W = (NN == MM) ? 0 : (MM == 4 ? 2 : 3);
+  constexpr int MBL = KL * W;                     // meta bits per lane per block
+  constexpr int NVL = (VB + 15) / 16;             // value loads per row block
+  constexpr int LA = NVL + (W ? 1 : 0);           // A loads per row block (values, positions)
+  constexpr int NL = RB * LA + DPW;               // loads per group (+2 on a tile's first block)
+  constexpr bool OUT16 = OUT == NM_F16 || OUT == NM_BF16;
+  constexpr int NS = (OUT == NM_I8) ? 4 : (OUT16 ? 8 : 63);
+  constexpr int WAIT_PEND = (NL + NS) < 63 ? (NL + NS) : 63;
+  typedef typename std::conditional<I8, v4i, v4f>::type Acc;
+  static_assert(VB % 4 == 0 && VD <= 8, "lane runs of whole dwords, at most 32 bytes");
+  static_assert(MBL <= 48, "a lane's positions fit a 64-bit window at any bit offset used");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t xs0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs2[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ostage[(OUT == NM_I8 || OUT16) ? NW * 2048 : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t bsbuf[NW * 4 * 512];
+
+  const Geometry& g = a.g;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int nKB = (int)g.nKB;
+  const int ldx = (int)a.ldx;
+  const int nRB = (int)g.nRB;
+
+  const int ntot = mtiles * ntiles;
+  const int per_xcd = (ntot + 7) / 8;
+  const int xcd = blockIdx.x % 8, jw = blockIdx.x / 8;
+  const int lo = xcd * per_xcd;
+  const int hi = min(lo + per_xcd, ntot);
+  if (lo + jw >= hi) return;
+  const int nmine = (hi - lo - jw + nwg_xcd - 1) / nwg_xcd;
+  const int total = nmine * nKB;
+  auto tile_of = [&](int k, int& r0, int& t0) {
+    const int L = lo + jw + k * nwg_xcd;
+    const int nt = L / mtiles;
+    r0 = (L - nt * mtiles) * BM;
+    t0 = nt * BN;
+  };
+
+  const v4i rx = make_rsrc(a.X, (int)(g.K * a.ldx * EB));
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values), 0, (int)g.values_bytes(), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.meta), 0, W ? (int)g.meta_bytes() : 0, 0x00020000);
+  const v4i rbias = make_rsrc(a.bias, a.bias ? (int)(g.R * 4) : 0);
+  const v4i rscale = make_rsrc(a.scale, a.scale ? (int)(g.R * 4) : 0);
+
+  // ---- X stage layouts (chunk positions swizzled so the transpose reads of
+  // the two lane groups served together hit disjoint banks).
+  // int8: 128 rows (k) x 128 B; 16-byte chunk c of row r at c ^ f(r),
+  //       f(r) = (r & 7) ^ (((r >> 4) ^ (r >> 5)) & 1); load d: rows 8 d ..
+  //       + 7, lane l -> row 8 d + l / 8, position l % 8.
+  // 16-bit: 64 rows x 256 B; 32-byte chunk c of row r at c ^ h(r),
+  //       h(r) = (r & 7) ^ 4 ((r >> 4) & 1); load d: rows 4 d .. + 3, lane l
+  //       -> row 4 d + l / 16, position (l % 16) / 2, half l % 2.
+  auto xoff = [&](int j) {
+    const int d = wave * DPW + j;
+    if constexpr (I8) {
+      const int row = 8 * d + (lane >> 3);
+      const int c = (lane & 7) ^ (row & 7) ^ (((row >> 4) ^ (row >> 5)) & 1);
+      return row * ldx + 16 * c;
+    } else {
+      const int row = 4 * d + (lane >> 4);
+      const int c = ((lane & 15) >> 1) ^ (row & 7) ^ (((row >> 4) & 1) << 2);
+      return row * ldx * 2 + 32 * c + 16 * (lane & 1);
+    }
+  };
+  auto xstage = [&](auto st) -> uint8_t* {
+    constexpr int S = decltype(st)::value;
+    return S == 0 ? xs0 : (S == 1 ? xs1 : xs2);
+  };
+
+  // ---- A: lane (i, g) of row block rb loads its run: VB bytes at row i,
+  // offset g VB of the block, and its MBL position bits, which start at bit
+  // g MBL of the row's meta: a 64-bit window from the dword holding that bit
+  // (one dword back when the window would leave the row, whose last dword
+  // then holds all of them), or one dword when a row has only one.
+  constexpr int C_B = 4 * VB;                      // packed row bytes per block
+  constexpr int MRB = W ? ((4 * MBL + 7) / 8 + 3) / 4 * 4 : 0;   // meta row bytes
+  const int voff_v = li * C_B + lg * VB;
+  int mdw = (lg * MBL) >> 5, mshift = (lg * MBL) & 31;
+  if (MRB >= 8 && 4 * mdw + 8 > MRB) { mdw -= 1; mshift += 32; }
+  const int voff_m = li * MRB + 4 * mdw;
+  uint32_t av[3][RB][VD];
+  uint64_t am[3][RB];
+
+  uint8_t* const bsw = bsbuf + wave * 2048;
+  auto bias_i = [&](int k, int rb) {
+    return *reinterpret_cast<const v4i*>(bsw + 512 * (k & 3) + 4 * (16 * rb + 4 * lg));
+  };
+  auto bias_f = [&](int k, int rb) {
+    return *reinterpret_cast<const v4f*>(bsw + 512 * (k & 3) + 4 * (16 * rb + 4 * lg));
+  };
+  auto scale_vec = [&](int k, int rb) {
+    return *reinterpret_cast<const v4f*>(bsw + 512 * (k & 3) + 256 + 4 * (16 * rb + 4 * lg));
+  };
+
+  int ln = 0, lk = 0, lkb = 0, lr0 = 0, lt0 = 0;
+  tile_of(0, lr0, lt0);
+  int g_live = 0, g_rb0 = 0, g_soff = 0;
+  // group parts: 0, 1: A of row block 0, 1; 2, 3: X halves; 4: bias / scale
+  // on a tile's first block and the cursor
+  auto load_part = [&](auto st, auto part) {
+    constexpr int S = decltype(st)::value;
+    constexpr int P = decltype(part)::value;
+    // Every offset that can leave its buffer (blocks past the matrix, rows
+    // past K, tokens past a row's end, groups past the end) is in the
+    // vector offset, which the range check covers; the scalar offset is 0.
+    if constexpr (P == 0) {
+      g_live = __builtin_amdgcn_readfirstlane(ln < total ? 1 : 0);
+      g_rb0 = (lr0 >> 4) + RB * wave;
+      g_soff = __builtin_amdgcn_readfirstlane(g_live ? (lkb * (128 / EB) * ldx + lt0) * EB
+                                                     : (int)(g.K * a.ldx * EB));
+    }
+    if constexpr (P < RB) {
+      const int rbc = __builtin_amdgcn_readfirstlane(min(g_rb0 + P, nRB));
+      const int blk = (g_live ? rbc : nRB) * nKB + (rbc < nRB ? lkb : 0);
+      const int vo = voff_v + blk * C_B * 16;
+#pragma unroll
+      for (int c = 0; c < NVL; ++c) {
+        const int rem = VB - 16 * c;
+        if (rem >= 16) {
+          const v4i x = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * c, 0, 0));
+          av[S][P][4 * c] = x[0]; av[S][P][4 * c + 1] = x[1];
+          av[S][P][4 * c + 2] = x[2]; av[S][P][4 * c + 3] = x[3];
+        } else if (rem == 12) {
+          const auto x = __builtin_amdgcn_raw_buffer_load_b96(rv, vo + 16 * c, 0, 0);
+          av[S][P][4 * c] = x[0]; av[S][P][4 * c + 1] = x[1]; av[S][P][4 * c + 2] = x[2];
+        } else if (rem == 8) {
+          const auto x = __builtin_amdgcn_raw_buffer_load_b64(rv, vo + 16 * c, 0, 0);
+          av[S][P][4 * c] = x[0]; av[S][P][4 * c + 1] = x[1];
+        } else {
+          av[S][P][4 * c] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo + 16 * c, 0, 0);
+        }
+      }
+      if constexpr (MRB >= 8) {
+        const auto m = __builtin_amdgcn_raw_buffer_load_b64(rm, voff_m + blk * MRB * 16, 0, 0);
+        am[S][P] = ((uint64_t)m[1] << 32) | m[0];
+      } else if constexpr (MRB == 4) {
+        am[S][P] = __builtin_amdgcn_raw_buffer_load_b32(rm, voff_m + blk * MRB * 16, 0, 0);
+      }
+    } else if constexpr (P == RB || P == RB + 1) {
+      uint8_t* sp = xstage(st);
+      constexpr int H = DPW / 2, J0 = (P - RB) * H;
+#pragma unroll
+      for (int j = J0; j < J0 + H; ++j) {
+        const int d = wave * DPW + j;
+        lds_dma16(rx, lds_addr(sp + d * 1024), xoff(j) + g_soff, 0);
+      }
+    } else {
+      if (g_live && lkb == 0) {
+        uint8_t* bs = bsw + 512 * (lk & 3);
+        const int boff = 4 * (lr0 + 32 * wave + lane);
+        lds_dma4(rbias, lds_addr(bs), boff, 0);
+        lds_dma4(rscale, lds_addr(bs + 256), boff, 0);
+      }
+      ++ln;
+      if (g_live && ++lkb == nKB) {
+        lkb = 0;
+        if (++lk < nmine) tile_of(lk, lr0, lt0);
+      }
+    }
+  };
+  constexpr int NPART = RB + 3;
+  static_assert(DPW % 2 == 0 && NPART < TN, "two X halves, one part per token tile");
+  auto load_group = [&](auto st) {
+    load_part(st, ic<0>()); load_part(st, ic<1>()); load_part(st, ic<2>()); load_part(st, ic<3>());
+    load_part(st, ic<4>());
+  };
+  static_assert(RB == 2 && NPART == 5, "load parts are spelled out for two row blocks");
+  auto group_size_extra = [&](int m) { return (m < total && m % nKB == 0) ? 2 : 0; };
+
+  // ---- B transpose reads for token tile tt: lane (j, g) gets, for step s,
+  // the dense k of its group's run: int8 rows 32 g + 16 s .. + 15 (tr8 reads
+  // of rows 32 g + kq + i / 2, kq = 0, 8, 16, 24), fp16 rows 16 g + 8 s ..
+  // + 7 (tr16 reads of rows 16 g + kq + e, kq = 0, 4, 8, 12).
+  int xa, xb;
+  if constexpr (I8) {
+    const int base = 128 * (32 * lg + (li >> 1)) + 8 * (li & 1);
+    xa = base | (16 * ((li >> 1) ^ (lg & 1)));
+    xb = base | (16 * ((li >> 1) ^ (lg & 1) ^ 1));
+  } else {
+    const int e_s = li >> 2, q_s = li & 3;
+    xa = (256 * (16 * lg + e_s) + 8 * q_s) | (32 * (e_s ^ (4 * (lg & 1))));
+    xb = (256 * (16 * lg + 4 + e_s) + 8 * q_s) | (32 * (e_s ^ 4 ^ (4 * (lg & 1))));
+  }
+  auto bfrag = [&](const uint8_t* sb, int tt) -> v8i {
+    if constexpr (I8) {
+      int oa = xa ^ (16 * tt), ob = xb ^ (16 * tt);
+      asm volatile("" : "+v"(oa), "+v"(ob));
+      const v2i p0 = lds_tr8(sb + oa);
+      const v2i p1 = lds_tr8(sb + oa + 8 * 128);
+      const v2i p2 = lds_tr8(sb + ob + 16 * 128);
+      const v2i p3 = lds_tr8(sb + ob + 24 * 128);
+      return v8i{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    } else {
+      int oa = xa ^ (32 * tt), ob = xb ^ (32 * tt);
+      asm volatile("" : "+v"(oa), "+v"(ob));
+      const v2i p0 = lds_tr16(sb + oa);
+      const v2i p1 = lds_tr16(sb + ob);
+      const v2i p2 = lds_tr16(sb + oa + 8 * 256);
+      const v2i p3 = lds_tr16(sb + ob + 8 * 256);
+      return v8i{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    }
+  };
+
+  Acc acc[RB][TN];
+  auto compute = [&](auto st, auto ast, auto nxt) {
+    constexpr int AS = decltype(ast)::value;
+    const uint8_t* sb = xstage(st);
+    // dense fragments of this block: both steps of both row blocks
+    v4i da[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const uint64_t mb = W ? (am[AS][rb] >> mshift) : 0;
+      da[rb][0] = expand_step<WT, NN, MM, 0>(av[AS][rb], mb);
+      da[rb][1] = expand_step<WT, NN, MM, 1>(av[AS][rb], mb);
+    }
+    v8i bf[2];
+    bf[0] = bfrag(sb, 0);
+    bf[1] = bfrag(sb, 1);
+    auto tile = [&](auto ttc) {
+      constexpr int tt = decltype(ttc)::value;
+      if constexpr (tt >= 1 && tt + 1 < TN) bf[(tt + 1) % 2] = bfrag(sb, tt + 1);
+      const v8i b = bf[tt % 2];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        acc[rb][tt] = mfma<WT>(da[rb][0], v4i{b[0], b[1], b[2], b[3]}, acc[rb][tt]);
+        acc[rb][tt] = mfma<WT>(da[rb][1], v4i{b[4], b[5], b[6], b[7]}, acc[rb][tt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (tt < NPART) load_part(nxt, ic<tt>());
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    tile(ic<0>()); tile(ic<1>()); tile(ic<2>()); tile(ic<3>());
+    tile(ic<4>()); tile(ic<5>()); tile(ic<6>()); tile(ic<7>());
+  };
+  auto init_acc = [&](int k) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      Acc b;
+      if constexpr (I8) b = bias_i(k, rb); else b = bias_f(k, rb);
+#pragma unroll
+      for (int tt = 0; tt < TN; ++tt) acc[rb][tt] = b;
+    }
+  };
+
+  // ---- epilogues.  Staging rows: position p = 8 g + 4 rb + v of a token
+  // holds wave row 16 rb + 4 g + v; a lane's 8 rows of one token are one
+  // chunk (8 bytes int8, 16 bytes 16-bit) at chunk position g ^ f(t).
+  uint8_t* const os = ostage + ((OUT == NM_I8 || OUT16) ? wave * 2048 : 0);
+  auto epilogue_i8 = [&](int k, int r0, int t0) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)(g.R * a.ldy), 0x00020000);
+    const int oob = (int)(g.R * a.ldy);
+    // token t (0..63 of the half) is a 32-byte row, f(t) = ((t >> 4) & 1) << 1;
+    // reads: lane 16 G + 2 i + h reads token 16 G + 8 j + i, chunk (2 s + h)
+    // ^ 2 (G & 1); output lane l then holds position 16 s + l, tokens 16 G +
+    // 8 j .. + 7
+    int wb = 32 * li + 8 * lg;
+    int rbs = (32 * (16 * lg + (li >> 1))) | (8 * (((li & 1)) ^ (2 * (lg & 1))));
+    asm volatile("" : "+v"(wb), "+v"(rbs));
+    const int orow = 16 * ((li >> 2) & 1) + 4 * (li >> 3) + (li & 3);   // + 8 s
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int tt = 4 * h + u;
+        int d[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const v4f sv = scale_vec(k, rb);
+          uint32_t bb[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float f = __fmul_rn((float)acc[rb][tt][v], sv[v]);
+            f = __builtin_amdgcn_fmed3f(f, -128.0f, 127.0f);
+            bb[v] = __builtin_bit_cast(uint32_t, f + 12582912.0f);
+          }
+          d[rb] = (int)(__builtin_amdgcn_perm(bb[1], bb[0], 0x0c0c0400u) |
+                        __builtin_amdgcn_perm(bb[3], bb[2], 0x04000c0cu));
+        }
+        // token 16 u + li: f = 2 (u & 1)
+        *reinterpret_cast<v2i*>(os + ((512 * u + wb) ^ (16 * (u & 1)))) = v2i{d[0], d[1]};
+      }
+      const int tok = t0 + 64 * h + 16 * lg;
+      const bool tok_ok = tok < a.T;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const v2i x0 = lds_tr8(os + (rbs ^ (16 * s)));
+        const v2i x1 = lds_tr8(os + (rbs ^ (16 * s)) + 256);
+        const int row = r0 + 32 * wave + orow + 8 * s;
+        const int off = tok_ok ? row * (int)a.ldy + tok : oob;
+        __builtin_amdgcn_raw_buffer_store_b128(v4i{x0[0], x0[1], x1[0], x1[1]}, ry, off, 0, 0);
+      }
+    }
+  };
+  auto epilogue_h = [&](int r0, int t0) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)(g.R * a.ldy * 2), 0x00020000);
+    const int oob = (int)(g.R * a.ldy * 2);
+    // token t (0..31 of the quarter) is a 64-byte row, f(t) = ((t >> 3) & 1)
+    // << 1 over 16-byte chunks; reads: lane 16 G + 4 e + q reads token 8 G +
+    // 4 j + e, chunk (2 s + q / 2) ^ f, byte 8 (q % 2); output lane l then
+    // holds position 16 s + l, tokens 8 G + 4 j .. + 3
+    const int e_s = li >> 2, q_s = li & 3;
+    int wb = (64 * li) | (16 * (lg ^ (((li >> 3) & 1) << 1)));
+    int rbs = (64 * (8 * lg + e_s) + 8 * (q_s & 1)) | (16 * ((q_s >> 1) ^ ((lg & 1) << 1)));
+    asm volatile("" : "+v"(wb), "+v"(rbs));
+    const int orow = 16 * ((li >> 2) & 1) + 4 * (li >> 3) + (li & 3);   // + 8 s
+#pragma unroll
+    for (int u4 = 0; u4 < 4; ++u4) {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int tt = 2 * u4 + w;
+        const uint32_t d0 = pack2<OUT>(acc[0][tt][0], acc[0][tt][1]);
+        const uint32_t d1 = pack2<OUT>(acc[0][tt][2], acc[0][tt][3]);
+        const uint32_t d2 = pack2<OUT>(acc[1][tt][0], acc[1][tt][1]);
+        const uint32_t d3 = pack2<OUT>(acc[1][tt][2], acc[1][tt][3]);
+        *reinterpret_cast<v4i*>(os + wb + 1024 * w) = v4i{(int)d0, (int)d1, (int)d2, (int)d3};
+      }
+      const int tok = t0 + 32 * u4 + 8 * lg;
+      const bool tok_ok = tok < a.T;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint8_t* rp = os + (rbs ^ (32 * s));
+        const v2i x0 = lds_tr16(rp);
+        const v2i x1 = lds_tr16(rp + 256);
+        const int row = r0 + 32 * wave + orow + 8 * s;
+        const int off = tok_ok ? (row * (int)a.ldy + tok) * 2 : oob;
+        __builtin_amdgcn_raw_buffer_store_b128(v4i{x0[0], x0[1], x1[0], x1[1]}, ry, off, 0, 0);
+      }
+    }
+  };
+  auto store_direct = [&](int r0, int t0) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)(g.R * a.ldy * 4), 0x00020000);
+    const int rw = r0 + 32 * wave + 4 * lg;
+    const int oob = (int)(g.R * a.ldy * 4);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int tt = 0; tt < TN; ++tt) {
+        const int t = t0 + 16 * tt + li;
+        // whole-vector cast (a bit cast of one element of a vector lvalue
+        // reads element 0)
+        const v4i ai4 = __builtin_bit_cast(v4i, acc[rb][tt]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          __builtin_amdgcn_raw_buffer_store_b32(ai4[v], ry,
+                                                t < a.T ? 4 * ((rw + 16 * rb + v) * (int)a.ldy + t) : oob, 0, 0);
+      }
+  };
+
+  int n = 0, ck = 0, ckb = 0, cr0, ct0;
+  tile_of(0, cr0, ct0);
+  bool pend = false;
+  auto wait_for_group = [&](int extra_after, bool stores_after) {
+    if (stores_after) {
+      if (extra_after)
+        __builtin_amdgcn_s_waitcnt(waitcnt(WAIT_PEND + 2 < 63 ? WAIT_PEND + 2 : 63, 15));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt(WAIT_PEND, 15));
+    } else {
+      if (extra_after)
+        __builtin_amdgcn_s_waitcnt(waitcnt(NL + 2, 15));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
+    }
+  };
+
+  load_group(ic<0>());
+  load_group(ic<1>());
+  wait_for_group(group_size_extra(1), false);
+  init_acc(0);
+
+  auto step = [&](auto st) {
+    constexpr int ST = decltype(st)::value;
+    constexpr int NX = (ST + 2) % 3;
+    wait_for_group(group_size_extra(n + 1), pend);
+    barrier_nofence();
+    pend = false;
+    compute(st, ic<ST>(), ic<NX>());
+    ++n;
+    if (++ckb < nKB) return;
+    ckb = 0;
+    if constexpr (OUT == NM_I8)
+      epilogue_i8(ck, cr0, ct0);
+    else if constexpr (OUT16)
+      epilogue_h(cr0, ct0);
+    else
+      store_direct(cr0, ct0);
+    pend = true;
+    ++ck;
+    if (ck < nmine) {
+      tile_of(ck, cr0, ct0);
+      wait_for_group(group_size_extra(n + 1), true);
+      init_acc(ck);
+    }
+  };
+  const int trips = total / 3, rest = total - 3 * trips;
+  for (int it = 0; it < trips; ++it) {
+    step(ic<0>());
+    step(ic<1>());
+    step(ic<2>());
+  }
+  if (rest > 0) step(ic<0>());
+  if (rest > 1) step(ic<1>());
+  __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
+#endif
+}
+
+int cu_count(int device) {
+  static int cache[64];
+  if (device < 0 || device >= 64) return 256;
+  if (!cache[device]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
+      cus = 256;
+    cache[device] = cus;
+  }
+  return cache[device];
+}
+
+template <int WT, int NN, int MM, int OUT>
+hipError_t launch_one(const SpmmArgs& a, hipStream_t s) {
+  const int mtiles = (int)((a.g.R + BM - 1) / BM);
+  const int ntiles = (int)((a.T + BN - 1) / BN);
+  const int ntot = mtiles * ntiles;
+  const int per_xcd = (ntot + 7) / 8;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  int nwg_xcd = cu_count(dev) / 8;                // one eight-wave workgroup per CU
+  if (nwg_xcd > per_xcd) nwg_xcd = per_xcd;
+  if (nwg_xcd < 1) nwg_xcd = 1;
+  hipLaunchKernelGGL((expand_kernel<WT, NN, MM, OUT>), dim3(8 * nwg_xcd), dim3(NW * 64), 0, s, a, mtiles, ntiles,
+                     nwg_xcd);
+  return hipGetLastError();
+}
+
+template <int WT, int NN, int MM>
+hipError_t launch_nm(const SpmmArgs& a, hipStream_t s) {
+  if constexpr (WT == NM_I8)
+    return a.ydt == NM_I8 ? launch_one<WT, NN, MM, NM_I8>(a, s) : launch_one<WT, NN, MM, NM_I32>(a, s);
+  else if constexpr (WT == NM_F16)
+    return a.ydt == NM_F16 ? launch_one<WT, NN, MM, NM_F16>(a, s) : launch_one<WT, NN, MM, NM_F32>(a, s);
+  else
+    return a.ydt == NM_BF16 ? launch_one<WT, NN, MM, NM_BF16>(a, s) : launch_one<WT, NN, MM, NM_F32>(a, s);
+}
+
+template <int WT>
+hipError_t launch_wt(const SpmmArgs& a, hipStream_t s) {
+  const int N = a.g.N, M = a.g.M;
+  if (M == 4) {
+    if (N == 1) return launch_nm<WT, 1, 4>(a, s);
+    if (N == 2) return launch_nm<WT, 2, 4>(a, s);
+    if (N == 3) return launch_nm<WT, 3, 4>(a, s);
+    return launch_nm<WT, 4, 4>(a, s);
+  }
+  if (N == 1) return launch_nm<WT, 1, 8>(a, s);
+  if (N == 2) return launch_nm<WT, 2, 8>(a, s);
+  if (N == 4) return launch_nm<WT, 4, 8>(a, s);
+  if (N == 8) return launch_nm<WT, 8, 8>(a, s);
+  return hipErrorInvalidValue;   // N:M not instantiated (the caller checks)
+}
+
+}  // namespace
+
+bool expand_supported(int N, int M) {
+  return (M == 4) || (M == 8 && (N == 1 || N == 2 || N == 4 || N == 8));
+}
+
+hipError_t launch_spmm_expand(const SpmmArgs& a, hipStream_t s) {
+  if (a.wdt == NM_I8) return launch_wt<NM_I8>(a, s);
+  if (a.wdt == NM_F16) return launch_wt<NM_F16>(a, s);
+  return launch_wt<NM_BF16>(a, s);
+}
+
+}  // namespace nm
