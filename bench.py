@@ -178,6 +178,103 @@ def run_stack(args):
     print(text, flush=True)
 
 
+def run_sweep(args):
+    """Every layer of the single-layer workloads (ViT-Tiny slice, ViT-B int8 at
+    four N:M, Swin-T fp16 stages, LLaMA-7B fp16 / bf16 decode and prefill),
+    each timed on its own: inputs drawn on the GPU (timing only; parity of
+    every shape is covered by the tests), buffer sets rotated over
+    `--rotate-gib` so no timed launch is served from the Infinity Cache, a HIP
+    graph of `reps` launches replayed.  One JSON line per layer, then a
+    summary line."""
+    import torch
+
+    import nm_inputs
+    import semi_structured_sparse_nm_amd as nm
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    tdt = {"i8": torch.int8, "f16": torch.float16, "bf16": torch.bfloat16, "i32": torch.int32,
+           "f32": torch.float32}
+    cfgs = nm_inputs.all_configs()
+    want = [c for c in args.sweep.split(",") if c]
+    rows = []
+    for cfg in want:
+        for i, L in enumerate(cfgs[cfg]):
+            gen.manual_seed(2000 + 100 * int(cfg) + i)
+            if L.dt == "i8":
+                W = torch.randint(-127, 128, (L.R, L.K), dtype=torch.int8, device=dev, generator=gen)
+            else:
+                W = (torch.randn((L.R, L.K), device=dev, generator=gen) * 0.02).to(tdt[L.dt])
+            p = nm.pack(W, L.N, L.M)
+            del W
+            bias = scale = None
+            if L.out == "i8":
+                bias = torch.randint(-2000, 2000, (L.R,), dtype=torch.int32, device=dev, generator=gen)
+                scale = torch.full((L.R,), 1.0 / 4096, dtype=torch.float32, device=dev)
+            ebx = torch.empty(0, dtype=tdt[L.dt]).element_size()
+            eby = torch.empty(0, dtype=tdt[L.out]).element_size()
+            footprint = p.values.numel() + (0 if p.meta is None else p.meta.numel()) + \
+                L.K * L.T * ebx + L.R * L.T * eby
+            nsets = max(2, math.ceil(args.rotate_gib * 2**30 / footprint))
+            sets = []
+            for _ in range(nsets):
+                if L.dt == "i8":
+                    X = torch.randint(-127, 128, (L.K, L.T), dtype=torch.int8, device=dev, generator=gen)
+                else:
+                    X = torch.randn((L.K, L.T), device=dev, generator=gen).to(tdt[L.dt])
+                pm = None if p.meta is None else p.meta.clone()
+                ps = nm.Packed(p.rows, p.K, p.N, p.M, p.dtype, p.values.clone(), pm, p.format_version)
+                sets.append((ps, X, torch.empty((L.R, L.T), dtype=tdt[L.out], device=dev)))
+            need = nm.workspace_size(p, L.T, tdt[L.out])
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            reps = max(nsets, 20)
+
+            def launch(j):
+                ps, X, Y = sets[j % nsets]
+                nm.spmm(ps, X, bias=bias, scale=scale, out_dtype=tdt[L.out], out=Y, workspace=ws)
+
+            for j in range(nsets):
+                launch(j)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                with torch.cuda.graph(g, stream=st):
+                    for j in range(reps):
+                        launch(j)
+            torch.cuda.current_stream().wait_stream(st)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            ops, nbytes, dense = nm_inputs.ops_and_bytes(L)
+            t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
+            t_mfma = ops / (MFMA_PEAK_TOPS[L.dt] * 1e12) * 1e6
+            row = {"config": cfg, "layer": L.name, "R": L.R, "K": L.K, "T": L.T, "N": L.N, "M": L.M,
+                   "in": L.dt, "out": L.out, "kernel": nm.variant(p, L.T, tdt[L.out]), "us": round(us, 2),
+                   "bound": "hbm" if t_hbm >= t_mfma else "mfma", "t_roof_us": round(max(t_hbm, t_mfma), 3),
+                   "roofline_fraction": round(max(t_hbm, t_mfma) / us, 4),
+                   "dense_equivalent_TOPS": round(dense / (us * 1e-6) / 1e12, 1),
+                   "effective_GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "rotation_sets": nsets}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+            del sets, g, ws, p
+            torch.cuda.empty_cache()
+    summary = {"sweep": want, "layers": len(rows),
+               "sum_us": round(sum(r["us"] for r in rows), 1),
+               "sum_roof_us": round(sum(r["t_roof_us"] for r in rows), 1)}
+    summary["roofline_fraction_of_sums"] = round(summary["sum_roof_us"] / max(summary["sum_us"], 1e-9), 4)
+    print(json.dumps(summary), flush=True)
+    if args.details:
+        json.dump({"summary": summary, "layers": rows}, open(args.details, "w"), indent=1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +290,8 @@ def main():
                          "reference for HBM byte counters)")
     ap.add_argument("--stack", action="store_true",
                     help="time the 48-layer mixed-N:M ViT-B int8 stack instead of one layer")
+    ap.add_argument("--sweep", default="",
+                    help="comma-separated workload sets to time layer by layer (1, 2, 3, 5)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -201,6 +300,9 @@ def main():
         sys.exit(2)
     if args.stack:
         run_stack(args)
+        return
+    if args.sweep:
+        run_sweep(args)
         return
 
     import numpy as np

@@ -55,6 +55,7 @@ enum Variant {
   V_SMFMAC_H,       // fp16 / bf16 2:4 sparse MFMA, persistent 256 x 128 tiles
   V_SMFMAC_HD,      // fp16 / bf16 2:4, decode shapes (T <= 16): K split across 8 waves
   V_EXPAND,         // any other N:M (int8, fp16, bf16): windows expanded in registers, dense MFMA
+  V_EXPAND_DECODE,  // any N:M, decode shapes (T <= 16): K split across 8 waves, dense MFMA
   V_COUNT
 };
 
@@ -67,6 +68,7 @@ const char* variant_name(Variant v) {
     case V_SMFMAC_H: return "smfmac_h_2of4_persistent";
     case V_SMFMAC_HD: return "smfmac_h_2of4_decode";
     case V_EXPAND: return "expand_mfma_persistent";
+    case V_EXPAND_DECODE: return "expand_mfma_decode";
     default: return "invalid";
   }
 }
@@ -116,6 +118,14 @@ bool eligible(Variant v, const Call& c) {
              c.g->values_bytes() + 1024 < (1ull << 31) && c.g->meta_bytes() + 1024 < (1ull << 31) &&
              (c.g->R + 256) * c.ldy * 4 < (1ll << 31) &&
              (c.ydt == NM_I32 || c.ydt == NM_F32 || (c.ldy % (16 / nm::dtype_bytes(c.ydt)) == 0 && aligned(c.Y, 16)));
+    case V_EXPAND_DECODE:
+      // any instantiated N:M with at most 16 tokens; X rows in whole 16-byte
+      // pieces; 32-bit buffer offsets that do not wrap for the rows past K a
+      // block reaches and the loads past the packed buffers' ends
+      return nm::expand_supported(c.g->N, c.g->M) && c.T <= 16 && c.ldx % (16 / c.g->eb) == 0 &&
+             aligned(c.X, 16) && (c.g->K + 128) * c.ldx * c.g->eb < (1ll << 31) &&
+             c.g->values_bytes() + 2048 < (1ull << 31) && c.g->meta_bytes() + 1024 < (1ull << 31) &&
+             c.g->R * c.ldy < (1ll << 40);
     default: return false;
   }
 }
@@ -126,8 +136,10 @@ Variant choose(const Call& c) {
     for (int v = V_GENERIC; v < V_COUNT; ++v)
       if (strcmp(force, variant_name((Variant)v)) == 0 && eligible((Variant)v, c)) return (Variant)v;
   }
-  if (eligible(V_SMFMAC_I8P, c)) return V_SMFMAC_I8P;
+  // decode shapes (few tokens): K split inside a workgroup per 16-row block
   if (eligible(V_SMFMAC_HD, c)) return V_SMFMAC_HD;
+  if (eligible(V_EXPAND_DECODE, c)) return V_EXPAND_DECODE;
+  if (eligible(V_SMFMAC_I8P, c)) return V_SMFMAC_I8P;
   if (eligible(V_SMFMAC_H, c)) return V_SMFMAC_H;
   if (eligible(V_EXPAND, c)) return V_EXPAND;
   return V_GENERIC;
@@ -237,6 +249,7 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
     case V_SMFMAC_H: e = nm::launch_spmm_smfmac_h(a, s); break;
     case V_SMFMAC_HD: e = nm::launch_spmm_smfmac_hd(a, s); break;
     case V_EXPAND: e = nm::launch_spmm_expand(a, s); break;
+    case V_EXPAND_DECODE: e = nm::launch_spmm_expand_decode(a, s); break;
     default: return NM_EINVAL;
   }
   return e == hipSuccess ? NM_OK : NM_EHIP;

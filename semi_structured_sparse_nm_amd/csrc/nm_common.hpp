@@ -81,6 +81,7 @@ hipError_t launch_spmm_smfmac_i8p(const SpmmArgs& a, int cfg, hipStream_t s);
 hipError_t launch_spmm_smfmac_h(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_smfmac_hd(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_expand(const SpmmArgs& a, hipStream_t s);
+hipError_t launch_spmm_expand_decode(const SpmmArgs& a, hipStream_t s);
 bool expand_supported(int N, int M);   // N:M instantiated by launch_spmm_expand
 
 // ---------------------------------------------------------------- device

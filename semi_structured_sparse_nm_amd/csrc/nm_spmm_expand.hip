@@ -26,6 +26,7 @@
 // bias + requant, int32, fp16 / bf16 (LDS transpose and 16-byte row pieces),
 // fp32 (direct).
 #include "nm_common.hpp"
+#include "nm_expand.hpp"
 
 namespace nm {
 
@@ -82,71 +83,6 @@ constexpr int BN = TN * 16;        // 128 tokens per tile
 constexpr int STAGE = 16384;       // bytes per X stage (128 B of dense k x 128 tokens)
 constexpr int DPW = STAGE / 1024 / NW;
 
-// Per-dtype geometry: EB element bytes, LR dense elements per lane per
-// block, a step (one MFMA) covers LR / 2.
-template <int WT> struct Ty {
-  static constexpr int EB = (WT == NM_I8) ? 1 : 2;
-  static constexpr int LR = (WT == NM_I8) ? 32 : 16;
-};
-
-// Dense 16-byte A fragment of step S from a lane's packed run: vd holds the
-// run's kept values (element e at byte e EB), mb its positions (W bits each,
-// element e at bit e W).  Group q of the step occupies bytes q M EB .. of
-// the fragment.
-template <int WT, int NN, int MM, int S>
-__device__ __forceinline__ v4i expand_step(const uint32_t* vd, uint64_t mb) {
-  constexpr int EB = Ty<WT>::EB;
-  constexpr int RUN = Ty<WT>::LR / 2;             // dense elements per step
-  constexpr int G = RUN / MM;                     // groups per step
-  constexpr int KS = G * NN;                      // kept per step
-  constexpr int W = (NN == MM) ? 0 : (MM == 4 ? 2 : 3);
-  if constexpr (NN == MM) {
-    return v4i{(int)vd[4 * S], (int)vd[4 * S + 1], (int)vd[4 * S + 2], (int)vd[4 * S + 3]};
-  } else {
-    uint32_t o[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int q = 0; q < G; ++q) {
-      uint64_t lo = 0, hi = 0;                    // the group's 64 (or 128) bits
-#pragma unroll
-      for (int j = 0; j < NN; ++j) {
-        const int e = S * KS + q * NN + j;        // element of the lane's run
-        const uint32_t el = (vd[(e * EB) >> 2] >> (8 * ((e * EB) & 3))) & (EB == 1 ? 0xFFu : 0xFFFFu);
-        const uint32_t pos = (uint32_t)(mb >> (e * W)) & ((1u << W) - 1u);
-        if constexpr (MM * EB == 4) {
-          lo |= (uint64_t)(el << (8 * pos));
-        } else if constexpr (MM * EB == 8) {
-          lo |= (uint64_t)el << ((8 * EB) * pos);
-        } else {                                  // fp16, M = 8: 128 bits
-          const uint64_t sh = (uint64_t)el << (16 * (pos & 3));
-          lo |= (pos < 4) ? sh : 0;
-          hi |= (pos < 4) ? 0 : sh;
-        }
-      }
-      if constexpr (MM * EB == 4) {
-        o[q] = (uint32_t)lo;
-      } else if constexpr (MM * EB == 8) {
-        o[2 * q] = (uint32_t)lo;
-        o[2 * q + 1] = (uint32_t)(lo >> 32);
-      } else {
-        o[0] = (uint32_t)lo; o[1] = (uint32_t)(lo >> 32);
-        o[2] = (uint32_t)hi; o[3] = (uint32_t)(hi >> 32);
-      }
-    }
-    return v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-  }
-}
-
-template <int WT>
-__device__ __forceinline__ auto mfma(v4i a, v4i b, typename std::conditional<WT == NM_I8, v4i, v4f>::type c) {
-  if constexpr (WT == NM_I8)
-    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-  else if constexpr (WT == NM_F16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0,
-                                                   0, 0);
-}
-
 template <int OUT>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   if constexpr (OUT == NM_F16)
@@ -160,13 +96,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
 expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr bool I8 = WT == NM_I8;
-  constexpr int EB = Ty<WT>::EB;
-  constexpr int LR = Ty<WT>::LR;
-  constexpr int KL = LR * NN / MM;                // kept per lane per block
-  constexpr int VB = KL * EB;                     // their bytes
-  constexpr int VD = VB / 4;
-  constexpr int W = (NN == MM) ? 0 : (MM == 4 ? 2 : 3);
-  constexpr int MBL = KL * W;                     // meta bits per lane per block
+  typedef Run<WT, NN, MM> RG;
+  constexpr int EB = RG::EB, VB = RG::VB, VD = RG::VD, W = RG::W, C_B = RG::C_B, MRB = RG::MRB;
   constexpr int NVL = (VB + 15) / 16;             // value loads per row block
   constexpr int LA = NVL + (W ? 1 : 0);           // A loads per row block (values, positions)
   constexpr int NL = RB * LA + DPW;               // loads per group (+2 on a tile's first block)
@@ -174,8 +105,6 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   constexpr int NS = (OUT == NM_I8) ? 4 : (OUT16 ? 8 : 63);
   constexpr int WAIT_PEND = (NL + NS) < 63 ? (NL + NS) : 63;
   typedef typename std::conditional<I8, v4i, v4f>::type Acc;
-  static_assert(VB % 4 == 0 && VD <= 8, "lane runs of whole dwords, at most 32 bytes");
-  static_assert(MBL <= 48, "a lane's positions fit a 64-bit window at any bit offset used");
 
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs1[STAGE];
@@ -239,16 +168,12 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     return S == 0 ? xs0 : (S == 1 ? xs1 : xs2);
   };
 
-  // ---- A: lane (i, g) of row block rb loads its run: VB bytes at row i,
-  // offset g VB of the block, and its MBL position bits, which start at bit
-  // g MBL of the row's meta: a 64-bit window from the dword holding that bit
-  // (one dword back when the window would leave the row, whose last dword
-  // then holds all of them), or one dword when a row has only one.
-  constexpr int C_B = 4 * VB;                      // packed row bytes per block
-  constexpr int MRB = W ? ((4 * MBL + 7) / 8 + 3) / 4 * 4 : 0;   // meta row bytes
+  // ---- A: lane (i, g) of row block rb loads its run (VB bytes at row i,
+  // offset g VB of the block) and the 64-bit meta window holding its
+  // positions (one dword when a row's meta is one dword)
   const int voff_v = li * C_B + lg * VB;
-  int mdw = (lg * MBL) >> 5, mshift = (lg * MBL) & 31;
-  if (MRB >= 8 && 4 * mdw + 8 > MRB) { mdw -= 1; mshift += 32; }
+  int mdw, mshift;
+  RG::meta_window(lg, mdw, mshift);
   const int voff_m = li * MRB + 4 * mdw;
   uint32_t av[3][RB][VD];
   uint64_t am[3][RB];
@@ -394,8 +319,8 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
       const v8i b = bf[tt % 2];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        acc[rb][tt] = mfma<WT>(da[rb][0], v4i{b[0], b[1], b[2], b[3]}, acc[rb][tt]);
-        acc[rb][tt] = mfma<WT>(da[rb][1], v4i{b[4], b[5], b[6], b[7]}, acc[rb][tt]);
+        acc[rb][tt] = mfma_dense<WT>(da[rb][0], v4i{b[0], b[1], b[2], b[3]}, acc[rb][tt]);
+        acc[rb][tt] = mfma_dense<WT>(da[rb][1], v4i{b[4], b[5], b[6], b[7]}, acc[rb][tt]);
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (tt < NPART) load_part(nxt, ic<tt>());

@@ -275,3 +275,37 @@ def test_expand_variant_more_shapes(force_variant, dt, out, N, M, R, K, T):
     """More tiles per workgroup than one (1008 tokens), many column blocks
     (K = 4104) and several row tiles."""
     _expand_case(force_variant, dt, out, N, M, R, K, T, 12)
+
+
+def _expand_decode_case(force_variant, dt, out, N, M, R, K, T, seed):
+    import semi_structured_sparse_nm_amd as nm
+    from tests._parity import TORCH_DT, dev
+    force_variant("expand_mfma_decode")
+    W, X, b, s = _inputs(dt, out, R, K, T, N, M, seed, f"expdec-{dt}-{out}-{N}-{M}-{R}-{K}-{T}")
+    p = nm.pack(dev(W, dt), N, M)
+    # nm_spmm_variant assumes dense rows (ldx = T); the run pads X rows to a
+    # multiple of 16 elements, which the forced kernel needs
+    if T % 16 == 0:
+        assert nm.variant(p, T, TORCH_DT[out]) == "expand_mfma_decode"
+    Y, _ = run(W, X, N, M, dt, out, bias=b, scale=s, ldx_pad=(-T) % 16 + 16, ldy_pad=3, sentinel=5)
+    compare(Y[:, :T], reference(W, X, N, M, dt, out, bias=b, scale=s), out, f"expand decode {N}:{M}")
+    pad = Y[:, T:]
+    want = 5 if out != "bf16" else oracle.round_to(np.array([5.0]), "bf16")[0]
+    assert np.all(pad == want), "writes beyond T"
+
+
+@pytest.mark.parametrize("dt,out", PAIRS)
+@pytest.mark.parametrize("N,M", NMS)
+@pytest.mark.parametrize("R,K,T", [(17, 8, 1), (300, 200, 3), (96, 4104, 16)])
+def test_expand_decode_variant(force_variant, dt, out, N, M, R, K, T):
+    """Decode kernel (K split over eight waves, windows expanded in registers,
+    partials summed in LDS in wave order) forced: fewer column blocks than
+    waves, partial blocks, ragged rows, T < 16, every N:M and dtype pair."""
+    _expand_decode_case(force_variant, dt, out, N, M, R, K, T, 13)
+
+
+@pytest.mark.parametrize("dt,out", [("i8", "i8"), ("f16", "f16"), ("bf16", "f32")])
+@pytest.mark.parametrize("N,M", [(1, 4), (3, 4), (4, 8), (8, 8)])
+@pytest.mark.parametrize("R,K,T", [(16, 64, 16), (40, 512, 8), (33, 11008, 16)])
+def test_expand_decode_variant_more_shapes(force_variant, dt, out, N, M, R, K, T):
+    _expand_decode_case(force_variant, dt, out, N, M, R, K, T, 14)
