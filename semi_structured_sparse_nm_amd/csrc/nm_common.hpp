@@ -85,6 +85,12 @@ hipError_t launch_spmm_expand_decode(const SpmmArgs& a, hipStream_t s);
 bool expand_supported(int N, int M);   // N:M instantiated by launch_spmm_expand
 
 // ---------------------------------------------------------------- device
+// Cache policy of the output stores (gfx950 buffer-store cache bits: sc0 |
+// nt).  The output is written once and never read back by the kernel;
+// streaming it past the L2 keeps the packed weights and the activation strip
+// that the next tiles reuse resident there instead of being evicted by it.
+constexpr int kStreamStore = 3;
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));

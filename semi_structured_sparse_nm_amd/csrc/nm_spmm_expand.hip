@@ -102,8 +102,6 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   constexpr int LA = NVL + (W ? 1 : 0);           // A loads per row block (values, positions)
   constexpr int NL = RB * LA + DPW;               // loads per group (+2 on a tile's first block)
   constexpr bool OUT16 = OUT == NM_F16 || OUT == NM_BF16;
-  constexpr int NS = (OUT == NM_I8) ? 4 : (OUT16 ? 8 : 63);
-  constexpr int WAIT_PEND = (NL + NS) < 63 ? (NL + NS) : 63;
   typedef typename std::conditional<I8, v4i, v4f>::type Acc;
 
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[STAGE];
@@ -384,7 +382,7 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         const v2i x1 = lds_tr8(os + (rbs ^ (16 * s)) + 256);
         const int row = r0 + 32 * wave + orow + 8 * s;
         const int off = tok_ok ? row * (int)a.ldy + tok : oob;
-        __builtin_amdgcn_raw_buffer_store_b128(v4i{x0[0], x0[1], x1[0], x1[1]}, ry, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v4i{x0[0], x0[1], x1[0], x1[1]}, ry, off, 0, kStreamStore);
       }
     }
   };
@@ -421,7 +419,7 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         const v2i x1 = lds_tr16(rp + 256);
         const int row = r0 + 32 * wave + orow + 8 * s;
         const int off = tok_ok ? (row * (int)a.ldy + tok) * 2 : oob;
-        __builtin_amdgcn_raw_buffer_store_b128(v4i{x0[0], x0[1], x1[0], x1[1]}, ry, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v4i{x0[0], x0[1], x1[0], x1[1]}, ry, off, 0, kStreamStore);
       }
     }
   };
@@ -441,38 +439,29 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           __builtin_amdgcn_raw_buffer_store_b32(ai4[v], ry,
-                                                t < a.T ? 4 * ((rw + 16 * rb + v) * (int)a.ldy + t) : oob, 0, 0);
+                                                t < a.T ? 4 * ((rw + 16 * rb + v) * (int)a.ldy + t) : oob, 0, kStreamStore);
       }
   };
 
   int n = 0, ck = 0, ckb = 0, cr0, ct0;
   tile_of(0, cr0, ct0);
-  bool pend = false;
-  auto wait_for_group = [&](int extra_after, bool stores_after) {
-    if (stores_after) {
-      if (extra_after)
-        __builtin_amdgcn_s_waitcnt(waitcnt(WAIT_PEND + 2 < 63 ? WAIT_PEND + 2 : 63, 15));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt(WAIT_PEND, 15));
-    } else {
-      if (extra_after)
-        __builtin_amdgcn_s_waitcnt(waitcnt(NL + 2, 15));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
-    }
+  auto wait_for_group = [&](int extra_after) {
+    if (extra_after)
+      __builtin_amdgcn_s_waitcnt(waitcnt(NL + 2, 15));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
   };
 
   load_group(ic<0>());
   load_group(ic<1>());
-  wait_for_group(group_size_extra(1), false);
+  wait_for_group(group_size_extra(1));
   init_acc(0);
 
   auto step = [&](auto st) {
     constexpr int ST = decltype(st)::value;
     constexpr int NX = (ST + 2) % 3;
-    wait_for_group(group_size_extra(n + 1), pend);
+    wait_for_group(group_size_extra(n + 1));
     barrier_nofence();
-    pend = false;
     compute(st, ic<ST>(), ic<NX>());
     ++n;
     if (++ckb < nKB) return;
@@ -483,11 +472,10 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
       epilogue_h(cr0, ct0);
     else
       store_direct(cr0, ct0);
-    pend = true;
     ++ck;
     if (ck < nmine) {
       tile_of(ck, cr0, ct0);
-      wait_for_group(group_size_extra(n + 1), true);
+      wait_for_group(group_size_extra(n + 1));
       init_acc(ck);
     }
   };

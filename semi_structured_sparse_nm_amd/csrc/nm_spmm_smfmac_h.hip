@@ -87,7 +87,6 @@ constexpr int RB = 4;              // row blocks (16 rows) per wave
 constexpr int TN = 8;              // token tiles (16 tokens) per wave
 constexpr int BN = TN * 16;        // 128 tokens per tile
 constexpr int STAGE = 64 * 256;    // bytes per X stage: 64 k x 128 tokens x 2 B
-constexpr int NS_H = 16;           // global stores of one 16-bit epilogue, per lane
 
 template <int WT>
 __device__ __forceinline__ v4f smfmac(v4i a, v8i b, v4f c, int idx) {
@@ -120,8 +119,6 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   constexpr int BM = NW * RB * 16;
   constexpr int DPW = STAGE / 1024 / NW;     // 1 KB direct-to-LDS loads per wave per block
   constexpr int NL = 2 * RB + DPW;           // loads per group (+1 bias on a tile's first block)
-  constexpr int NS = OUT16 ? NS_H : 63;
-  constexpr int WAIT_PEND = (NL + NS) < 63 ? (NL + NS) : 63;
 
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs1[STAGE];
@@ -335,7 +332,7 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         const v2i x1 = lds_tr16(rp + 512);
         const int row = r0 + 64 * wave + orow + 4 * s;
         const int off = tok_ok ? (row * (int)a.ldy + tok) * 2 : oob;
-        __builtin_amdgcn_raw_buffer_store_b128(v4i{x0[0], x0[1], x1[0], x1[1]}, ry, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v4i{x0[0], x0[1], x1[0], x1[1]}, ry, off, 0, kStreamStore);
       }
     }
   };
@@ -356,39 +353,30 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         for (int v = 0; v < 4; ++v)
           __builtin_amdgcn_raw_buffer_store_b32(
               ai4[v], ry,
-              t0 + 16 * tt < a.T ? 4 * ((rw + 16 * rb + v) * (int)a.ldy + t) : oob, 0, 0);
+              t0 + 16 * tt < a.T ? 4 * ((rw + 16 * rb + v) * (int)a.ldy + t) : oob, 0, kStreamStore);
       }
   };
 
   int n = 0, ck = 0, ckb = 0, cr0, ct0;
   tile_of(0, cr0, ct0);
-  bool pend = false;
 
-  auto wait_for_group = [&](int extra_after, bool stores_after) {
-    if (stores_after) {
-      if (extra_after)
-        __builtin_amdgcn_s_waitcnt(waitcnt(WAIT_PEND + 1 < 63 ? WAIT_PEND + 1 : 63, 15));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt(WAIT_PEND, 15));
-    } else {
-      if (extra_after)
-        __builtin_amdgcn_s_waitcnt(waitcnt(NL + 1, 15));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
-    }
+  auto wait_for_group = [&](int extra_after) {
+    if (extra_after)
+      __builtin_amdgcn_s_waitcnt(waitcnt(NL + 1, 15));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
   };
 
   load_group(ic<0>());
   load_group(ic<1>());
-  wait_for_group(group_size_extra(1), false);
+  wait_for_group(group_size_extra(1));
   init_acc(0);
 
   auto step = [&](auto st) {
     constexpr int ST = decltype(st)::value;
     constexpr int NX = (ST + 2) % 3;
-    wait_for_group(group_size_extra(n + 1), pend);
+    wait_for_group(group_size_extra(n + 1));
     barrier_nofence();
-    pend = false;
     compute(st, ic<ST>(), ic<NX>());
     ++n;
     if (++ckb < nKB) return;
@@ -397,11 +385,10 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
       epilogue_h(cr0, ct0);
     else
       store_f32(cr0, ct0);
-    pend = true;
     ++ck;
     if (ck < nmine) {
       tile_of(ck, cr0, ct0);
-      wait_for_group(group_size_extra(n + 1), true);
+      wait_for_group(group_size_extra(n + 1));
       init_acc(ck);
     }
   };

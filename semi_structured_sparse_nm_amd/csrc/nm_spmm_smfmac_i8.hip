@@ -310,7 +310,7 @@ __global__ void __launch_bounds__(256, 2) smfmac_i8_kernel(SpmmArgs a, int mtile
       const int rs = rw & 127;
       const v4i v = *reinterpret_cast<const v4i*>(rowbuf + rs * 128 + 16 * (c ^ ((rs >> 1) & 7)));
       if (t0 + 16 * c < a.T)
-        __builtin_amdgcn_raw_buffer_store_b128(v, ry, (r0 + rw) * (int)a.ldy + t0 + 16 * c, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ry, (r0 + rw) * (int)a.ldy + t0 + 16 * c, 0, kStreamStore);
     }
   } else {
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(256, 2) smfmac_i8_kernel(SpmmArgs a, int mtile
           const int r = 16 * (rb0 + rb) + 4 * lg + v;
           const int t = t0 + tt * 16 + li;
           if (t < a.T)
-            __builtin_amdgcn_raw_buffer_store_b32(acc[rb][tt][v], ry, 4 * (r * (int)a.ldy + t), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(acc[rb][tt][v], ry, 4 * (r * (int)a.ldy + t), 0, kStreamStore);
         }
   }
 #endif

@@ -15,12 +15,16 @@
 // tile's first blocks are in flight while the current tile is multiplied and
 // requantised; no tile starts cold.
 //
-// Waits.  Vector memory operations complete in issue order (one vmcnt
-// counter).  Block n's loads L(n) are a fixed group: A fragments (8 register
-// loads) first, then the X stage and the tile's bias / scale rows (direct-to-
-// LDS).  Step n waits until at most |L(n+1)| + (stores of the previous
-// epilogue) operations are outstanding, which is exactly "L(n) has landed",
-// then a barrier publishes every wave's part of the stage.  L(n+2) is issued
+// Waits.  One vmcnt counter covers loads and stores; loads complete in issue
+// order among themselves, but a store may complete before loads issued
+// ahead of it, so a wait never counts stores.  Block n's loads L(n) are a
+// fixed group: A fragments (8 register loads) first, then the X stage and
+// the tile's bias / scale rows (direct-to-LDS).  Step n waits until at most
+// |L(n+1)| operations are outstanding: whatever else is outstanding then
+// (a stage of L(n+1), an epilogue's stores) leaves no load of L(n) pending,
+// so L(n) has landed; then a barrier publishes every wave's part of the
+// stage.  A tile's stores are waited for (at the latest) by the next step's
+// wait, a block after they were issued.  L(n+2) is issued
 // after the first token tile of block n is multiplied: by then the compiler's
 // own waits for the A(n) registers are placed, and they count only the
 // register loads it can see (A(n+1) and the stores), so they hold back at
@@ -98,7 +102,6 @@ constexpr int RB = 4;              // row blocks (16 rows) per wave
 constexpr int TN = 8;              // token tiles (16 tokens) per wave
 constexpr int BN = TN * 16;        // 128 tokens per tile
 constexpr int STAGE = 128 * BN;    // bytes per X stage (16 KB)
-constexpr int NS_I8 = 8;           // global stores of one int8 epilogue, per lane
 
 template <int NW, bool OUT_I8>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -110,8 +113,6 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   // one group of loads per block and wave: A values + meta, X (+ bias and
   // scale on a tile's first block)
   constexpr int NL = 2 * RB + DPW;
-  constexpr int NS = OUT_I8 ? NS_I8 : 63;
-  constexpr int WAIT_PEND = (NL + NS) < 63 ? (NL + NS) : 63;
 
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs1[STAGE];
@@ -368,7 +369,7 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         const v2i x1 = lds_tr8(os + rq[q] + 512);
         const int row = r0 + 64 * wave + orow + 4 * q;
         const int off = tok_ok ? row * (int)a.ldy + tok : oob;
-        __builtin_amdgcn_raw_buffer_store_b128(v4i{x0[0], x0[1], x1[0], x1[1]}, ry, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v4i{x0[0], x0[1], x1[0], x1[1]}, ry, off, 0, kStreamStore);
       }
     }
   };
@@ -386,36 +387,28 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           __builtin_amdgcn_raw_buffer_store_b32(
-              acc[rb][tt][v], ry, t0 + 16 * tt < a.T ? 4 * ((rw + 16 * rb + v) * (int)a.ldy + t) : oob, 0, 0);
+              acc[rb][tt][v], ry, t0 + 16 * tt < a.T ? 4 * ((rw + 16 * rb + v) * (int)a.ldy + t) : oob, 0, kStreamStore);
       }
   };
 
   // ---- compute cursor: tile ck (rows cr0, tokens ct0), block ckb; block n
   int n = 0, ck = 0, ckb = 0, cr0, ct0;
   tile_of(0, cr0, ct0);
-  bool pend = false;   // an epilogue's stores were issued after the latest group
 
   // wait until L(m) has landed, given the group issued after it (its
   // size: NL, plus 2 when it starts a live tile) and whether an epilogue's
   // stores were issued after that
-  auto wait_for_group = [&](int extra_after, bool stores_after) {
-    if (stores_after) {
-      if (extra_after)
-        __builtin_amdgcn_s_waitcnt(waitcnt(WAIT_PEND + 2 < 63 ? WAIT_PEND + 2 : 63, 15));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt(WAIT_PEND, 15));
-    } else {
-      if (extra_after)
-        __builtin_amdgcn_s_waitcnt(waitcnt(NL + 2, 15));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
-    }
+  auto wait_for_group = [&](int extra_after) {
+    if (extra_after)
+      __builtin_amdgcn_s_waitcnt(waitcnt(NL + 2, 15));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
   };
 
   load_group(ic<0>());
   load_group(ic<1>());
   // tile 0's bias (group 0) has landed once group 1 is all that is left
-  wait_for_group(group_size_extra(1), false);
+  wait_for_group(group_size_extra(1));
   init_acc(0);
 
   // One block: stage / register set ST = n % 3; its loads were issued two
@@ -425,9 +418,8 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     constexpr int NX = (ST + 2) % 3;
     // groups past the end are issued too (see load_group), so L(n + 1) is
     // always in flight behind L(n)
-    wait_for_group(group_size_extra(n + 1), pend);
+    wait_for_group(group_size_extra(n + 1));
     barrier_nofence();
-    pend = false;
     compute(st, ic<ST>(), ic<NX>());
     ++n;
     if (++ckb < nKB) return;
@@ -436,13 +428,12 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
       epilogue_i8(ck, cr0, ct0);
     else
       store_i32(cr0, ct0);
-    pend = true;
     ++ck;
     if (ck < nmine) {
       tile_of(ck, cr0, ct0);
       // the next tile's bias rows arrive with its first group, L(n); the
       // group after it and the epilogue's stores may still be in flight
-      wait_for_group(group_size_extra(n + 1), true);
+      wait_for_group(group_size_extra(n + 1));
       init_acc(ck);
     }
   };
