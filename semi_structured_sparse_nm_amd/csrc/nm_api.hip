@@ -56,6 +56,7 @@ enum Variant {
   V_SMFMAC_HD,      // fp16 / bf16 2:4, decode shapes (T <= 16): K split across 8 waves
   V_EXPAND,         // any other N:M (int8, fp16, bf16): windows expanded in registers, dense MFMA
   V_EXPAND_DECODE,  // any N:M, decode shapes (T <= 16): K split across 8 waves, dense MFMA
+  V_SMFMAC_I8S,     // int8 2:4, K <= 1024: weights held in registers, workgroups walk token strips
   V_COUNT
 };
 
@@ -69,6 +70,7 @@ const char* variant_name(Variant v) {
     case V_SMFMAC_HD: return "smfmac_h_2of4_decode";
     case V_EXPAND: return "expand_mfma_persistent";
     case V_EXPAND_DECODE: return "expand_mfma_decode";
+    case V_SMFMAC_I8S: return "smfmac_i8_2of4_stationary";
     default: return "invalid";
   }
 }
@@ -93,6 +95,13 @@ bool eligible(Variant v, const Call& c) {
       return c.wdt == NM_I8 && c.g->N == 2 && c.g->M == 4 && c.T % 16 == 0 && c.ldx % 16 == 0 &&
              aligned(c.X, 16) && (c.g->K + 128) * c.ldx < (1ll << 31) &&
              c.g->values_bytes() < (1ull << 31) && (c.g->R + 512) * c.ldy * 4 < (1ll << 31) &&
+             (c.ydt == NM_I32 || (c.ydt == NM_I8 && c.ldy % 16 == 0 && aligned(c.Y, 16)));
+    case V_SMFMAC_I8S:
+      // as the persistent int8 2:4 kernel, with 2 to 8 column blocks (the
+      // weights of a wave's rows over all of K fit its registers)
+      return c.wdt == NM_I8 && c.g->N == 2 && c.g->M == 4 && nm::smfmac_i8s_supported(c.g->nKB) &&
+             c.T % 16 == 0 && c.ldx % 16 == 0 && aligned(c.X, 16) && (c.g->K + 128) * c.ldx < (1ll << 31) &&
+             c.g->values_bytes() + 8192 < (1ull << 31) && (c.g->R + 256) * c.ldy * 4 < (1ll << 31) &&
              (c.ydt == NM_I32 || (c.ydt == NM_I8 && c.ldy % 16 == 0 && aligned(c.Y, 16)));
     case V_SMFMAC_H:
       // fp16 / bf16 2:4; X rows in whole 16-byte pieces; 32-bit buffer
@@ -139,6 +148,11 @@ Variant choose(const Call& c) {
   // decode shapes (few tokens): K split inside a workgroup per 16-row block
   if (eligible(V_SMFMAC_HD, c)) return V_SMFMAC_HD;
   if (eligible(V_EXPAND_DECODE, c)) return V_EXPAND_DECODE;
+  // int8 2:4 with K <= 1024: the weight-stationary kernel while a row block
+  // is shared by enough token strips per workgroup to amortise its weight
+  // loads; measured on MI355X at T = 12608: R = 768 and 2304 faster (15.6 /
+  // 27.7 us against 17.1 / 29.8 us), R = 3072 slower (33.2 against 31.4 us)
+  if (eligible(V_SMFMAC_I8S, c) && c.g->R <= 2304) return V_SMFMAC_I8S;
   if (eligible(V_SMFMAC_I8P, c)) return V_SMFMAC_I8P;
   if (eligible(V_SMFMAC_H, c)) return V_SMFMAC_H;
   if (eligible(V_EXPAND, c)) return V_EXPAND;
@@ -250,6 +264,7 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
     case V_SMFMAC_HD: e = nm::launch_spmm_smfmac_hd(a, s); break;
     case V_EXPAND: e = nm::launch_spmm_expand(a, s); break;
     case V_EXPAND_DECODE: e = nm::launch_spmm_expand_decode(a, s); break;
+    case V_SMFMAC_I8S: e = nm::launch_spmm_smfmac_i8s(a, s); break;
     default: return NM_EINVAL;
   }
   return e == hipSuccess ? NM_OK : NM_EHIP;

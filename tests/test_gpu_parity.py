@@ -309,3 +309,29 @@ def test_expand_decode_variant(force_variant, dt, out, N, M, R, K, T):
 @pytest.mark.parametrize("R,K,T", [(16, 64, 16), (40, 512, 8), (33, 11008, 16)])
 def test_expand_decode_variant_more_shapes(force_variant, dt, out, N, M, R, K, T):
     _expand_decode_case(force_variant, dt, out, N, M, R, K, T, 14)
+
+
+@pytest.mark.parametrize("out", ["i8", "i32"])
+@pytest.mark.parametrize("R,K,T", [(300, 192, 144), (520, 384, 400), (259, 512, 272), (64, 640, 32),
+                                   (1100, 768, 2000), (2000, 896, 4096), (700, 1000, 1008),
+                                   (3072, 768, 12608)])
+def test_stationary_i8_variant(force_variant, out, R, K, T):
+    """Weight-stationary int8 2:4 kernel forced: every column-block count it
+    takes (2..8, a partial last block), ragged rows, workgroup runs that
+    cross row blocks (weights reloaded mid-run), padded row strides."""
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    variant = "smfmac_i8_2of4_stationary"
+    force_variant(variant)
+    W, X, b, s = _inputs("i8", out, R, K, T, 2, 4, 15, f"stat-{out}-{R}-{K}-{T}")
+    p = nm.pack(torch.from_numpy(W).cuda(), 2, 4)
+    assert nm.variant(p, T, torch.int8 if out == "i8" else torch.int32) == variant
+    Y, _ = run(W, X, 2, 4, "i8", out, bias=b, scale=s, ldx_pad=32, ldy_pad=16 if out == "i8" else 3,
+               sentinel=5)
+    if R * T > 4_000_000:
+        rows = np.unique(np.concatenate([[0, R - 1], np.random.default_rng(3).integers(0, R, 40)]))
+        ref = reference(W, X, 2, 4, "i8", out, bias=b, scale=s, rows=rows)
+        compare(np.asarray(Y)[rows, :T], ref, out, variant)
+    else:
+        compare(Y[:, :T], reference(W, X, 2, 4, "i8", out, bias=b, scale=s), out, variant)
+    assert np.all(Y[:, T:] == 5), "writes beyond T"
