@@ -57,6 +57,7 @@ enum Variant {
   V_EXPAND,         // any other N:M (int8, fp16, bf16): windows expanded in registers, dense MFMA
   V_EXPAND_DECODE,  // any N:M, decode shapes (T <= 16): K split across 8 waves, dense MFMA
   V_SMFMAC_I8S,     // int8 2:4, K <= 1024: weights held in registers, workgroups walk token strips
+  V_EXPAND32,       // as V_EXPAND with 32 x 32 dense MFMA (forced only: measured slower)
   V_COUNT
 };
 
@@ -71,6 +72,7 @@ const char* variant_name(Variant v) {
     case V_EXPAND: return "expand_mfma_persistent";
     case V_EXPAND_DECODE: return "expand_mfma_decode";
     case V_SMFMAC_I8S: return "smfmac_i8_2of4_stationary";
+    case V_EXPAND32: return "expand_mfma32_persistent";
     default: return "invalid";
   }
 }
@@ -127,6 +129,14 @@ bool eligible(Variant v, const Call& c) {
              c.g->values_bytes() + 1024 < (1ull << 31) && c.g->meta_bytes() + 1024 < (1ull << 31) &&
              (c.g->R + 256) * c.ldy * 4 < (1ll << 31) &&
              (c.ydt == NM_I32 || c.ydt == NM_F32 || (c.ldy % (16 / nm::dtype_bytes(c.ydt)) == 0 && aligned(c.Y, 16)));
+    case V_EXPAND32:
+      // as the 16 x 16 dense-expand kernel; a lane's 32 rows span two packed
+      // row blocks, so offsets reach one block column past a row block
+      return nm::expand32_supported(c.g->N, c.g->M) && c.T % 16 == 0 && c.ldx % (16 / c.g->eb) == 0 &&
+             aligned(c.X, 16) && (c.g->K + 128) * c.ldx * c.g->eb < (1ll << 31) &&
+             2 * c.g->values_bytes() + 65536 < (1ull << 31) && 2 * c.g->meta_bytes() + 65536 < (1ull << 31) &&
+             (c.g->R + 256) * c.ldy * 4 < (1ll << 31) &&
+             (c.ydt == NM_I32 || c.ydt == NM_F32 || (c.ldy % (16 / nm::dtype_bytes(c.ydt)) == 0 && aligned(c.Y, 16)));
     case V_EXPAND_DECODE:
       // any instantiated N:M with at most 16 tokens; X rows in whole 16-byte
       // pieces; 32-bit buffer offsets that do not wrap for the rows past K a
@@ -155,6 +165,9 @@ Variant choose(const Call& c) {
   if (eligible(V_SMFMAC_I8S, c) && c.g->R <= 2304) return V_SMFMAC_I8S;
   if (eligible(V_SMFMAC_I8P, c)) return V_SMFMAC_I8P;
   if (eligible(V_SMFMAC_H, c)) return V_SMFMAC_H;
+  // the 32 x 32-fragment dense-expand kernel is correct but measured 2-10%
+  // slower than the 16 x 16 one on every ViT-B, Swin and LLaMA shape (the
+  // block loop is not bound by the matrix cores): forced only
   if (eligible(V_EXPAND, c)) return V_EXPAND;
   return V_GENERIC;
 }
@@ -263,6 +276,7 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
     case V_SMFMAC_H: e = nm::launch_spmm_smfmac_h(a, s); break;
     case V_SMFMAC_HD: e = nm::launch_spmm_smfmac_hd(a, s); break;
     case V_EXPAND: e = nm::launch_spmm_expand(a, s); break;
+    case V_EXPAND32: e = nm::launch_spmm_expand32(a, s); break;
     case V_EXPAND_DECODE: e = nm::launch_spmm_expand_decode(a, s); break;
     case V_SMFMAC_I8S: e = nm::launch_spmm_smfmac_i8s(a, s); break;
     default: return NM_EINVAL;

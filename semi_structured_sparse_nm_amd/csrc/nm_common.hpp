@@ -84,6 +84,8 @@ hipError_t launch_spmm_smfmac_i8s(const SpmmArgs& a, hipStream_t s);
 bool smfmac_i8s_supported(int64_t nKB);   // column-block counts launch_spmm_smfmac_i8s instantiates
 hipError_t launch_spmm_expand(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_expand_decode(const SpmmArgs& a, hipStream_t s);
+hipError_t launch_spmm_expand32(const SpmmArgs& a, hipStream_t s);
+bool expand32_supported(int N, int M);   // N:M instantiated by launch_spmm_expand32
 bool expand_supported(int N, int M);   // N:M instantiated by launch_spmm_expand
 
 // ---------------------------------------------------------------- device

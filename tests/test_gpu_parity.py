@@ -243,13 +243,16 @@ EXPAND_NMS = [(1, 4), (3, 4), (4, 4), (1, 8), (2, 8), (4, 8), (8, 8)]
 EXPAND_SHAPES = [(300, 192, 144), (17, 8, 16), (259, 1288, 272)]
 
 
-def _expand_case(force_variant, dt, out, N, M, R, K, T, seed):
+EXPAND_VARIANTS = ["expand_mfma_persistent", "expand_mfma32_persistent"]
+
+
+def _expand_case(force_variant, variant, dt, out, N, M, R, K, T, seed):
     import semi_structured_sparse_nm_amd as nm
     from tests._parity import TORCH_DT, dev
-    force_variant("expand_mfma_persistent")
+    force_variant(variant)
     W, X, b, s = _inputs(dt, out, R, K, T, N, M, seed, f"expand-{dt}-{out}-{N}-{M}-{R}-{K}-{T}")
     p = nm.pack(dev(W, dt), N, M)
-    assert nm.variant(p, T, TORCH_DT[out]) == "expand_mfma_persistent"
+    assert nm.variant(p, T, TORCH_DT[out]) == variant
     narrow = out in ("i8", "f16", "bf16")
     Y, _ = run(W, X, N, M, dt, out, bias=b, scale=s, ldx_pad=32, ldy_pad=16 if narrow else 3, sentinel=5)
     compare(Y[:, :T], reference(W, X, N, M, dt, out, bias=b, scale=s), out, f"expand {N}:{M}")
@@ -258,23 +261,26 @@ def _expand_case(force_variant, dt, out, N, M, R, K, T, seed):
     assert np.all(pad == want), "writes beyond T"
 
 
+@pytest.mark.parametrize("variant", EXPAND_VARIANTS)
 @pytest.mark.parametrize("dt,out", PAIRS)
 @pytest.mark.parametrize("N,M", EXPAND_NMS)
 @pytest.mark.parametrize("R,K,T", EXPAND_SHAPES)
-def test_expand_variant(force_variant, dt, out, N, M, R, K, T):
-    """Dense-expand kernel (every N:M but 2:4, windows expanded in registers)
-    forced on ragged rows, partial column blocks, several token tiles and
-    padded row strides, every dtype pair."""
-    _expand_case(force_variant, dt, out, N, M, R, K, T, 11)
+def test_expand_variant(force_variant, variant, dt, out, N, M, R, K, T):
+    """Dense-expand kernels (every N:M but 2:4, windows expanded in
+    registers; 16 x 16 and 32 x 32 fragments) forced on ragged rows, partial
+    column blocks, several token tiles and padded row strides, every dtype
+    pair."""
+    _expand_case(force_variant, variant, dt, out, N, M, R, K, T, 11)
 
 
+@pytest.mark.parametrize("variant", EXPAND_VARIANTS)
 @pytest.mark.parametrize("dt,out", [("i8", "i8"), ("f16", "f16"), ("bf16", "f32")])
 @pytest.mark.parametrize("N,M", [(1, 4), (3, 4), (4, 8), (8, 8)])
 @pytest.mark.parametrize("R,K,T", [(256, 96, 1008), (520, 768, 400), (64, 4104, 32)])
-def test_expand_variant_more_shapes(force_variant, dt, out, N, M, R, K, T):
+def test_expand_variant_more_shapes(force_variant, variant, dt, out, N, M, R, K, T):
     """More tiles per workgroup than one (1008 tokens), many column blocks
     (K = 4104) and several row tiles."""
-    _expand_case(force_variant, dt, out, N, M, R, K, T, 12)
+    _expand_case(force_variant, variant, dt, out, N, M, R, K, T, 12)
 
 
 def _expand_decode_case(force_variant, dt, out, N, M, R, K, T, seed):
