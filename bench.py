@@ -275,6 +275,51 @@ def run_sweep(args):
         json.dump({"summary": summary, "layers": rows}, open(args.details, "w"), indent=1)
 
 
+def run_lut(args):
+    """Latency look-up table for the mixed-N:M ViT-B stack: measure every
+    (layer shape, N:M) of the stack's choice set, time stacks of four
+    different seeded N:M draws, calibrate the per-launch gap on the first
+    and report how well the table predicts the other three."""
+    import torch
+
+    import nm_inputs
+    from semi_structured_sparse_nm_amd.lut import LayerShape, measure_layers, time_stack
+
+    torch.cuda.set_device(0)
+    T = nm_inputs.VIT_B_TOKENS
+    choices = [(1, 4), (2, 4), (4, 8), (8, 8)]
+    shapes = [LayerShape(R, K, T, n, m) for (R, K) in nm_inputs.VIT_B_LAYERS.values() for n, m in choices]
+    lut = measure_layers(shapes, reps=20, copies=4)
+    print(json.dumps({"lut_entries": len(lut)}), file=sys.stderr, flush=True)
+
+    def stack(seed):
+        out = []
+        for i, (n, m) in enumerate(nm_inputs.stack_nm(seed)):
+            R, K = list(nm_inputs.VIT_B_LAYERS.values())[i % 4]
+            out.append(LayerShape(R, K, T, n, m))
+        return out
+
+    measured = {}
+    for seed in range(4):
+        measured[seed] = time_stack(stack(seed), reps=3, seed=seed)
+        print(json.dumps({"stack_seed": seed, "measured_us": round(measured[seed], 1)}), file=sys.stderr, flush=True)
+    raw = {seed: lut.predict(stack(seed)) for seed in range(4)}
+    gap = lut.calibrate(stack(0), measured[0])
+    val = []
+    for seed in range(1, 4):
+        pred = lut.predict(stack(seed))
+        val.append({"seed": seed, "measured_us": round(measured[seed], 1), "predicted_us": round(pred, 1),
+                    "uncalibrated_us": round(raw[seed], 1),
+                    "error": round((pred - measured[seed]) / measured[seed], 4)})
+    out = {"lut": "vitb_int8_mixed_nm_stack", "entries": len(lut), "tokens": T,
+           "calibration": {"seed": 0, "measured_us": round(measured[0], 1), "gap_us_per_launch": round(gap, 2)},
+           "validation": val,
+           "max_abs_error": round(max(abs(v["error"]) for v in val), 4)}
+    print(json.dumps(out), flush=True)
+    if args.details:
+        json.dump({"result": out, "lut": json.loads(lut.to_json())}, open(args.details, "w"), indent=1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +335,9 @@ def main():
                          "reference for HBM byte counters)")
     ap.add_argument("--stack", action="store_true",
                     help="time the 48-layer mixed-N:M ViT-B int8 stack instead of one layer")
+    ap.add_argument("--lut", action="store_true",
+                    help="build the latency look-up table of the mixed ViT-B stack and validate it on "
+                         "stacks of other N:M draws")
     ap.add_argument("--sweep", default="",
                     help="comma-separated workload sets to time layer by layer (1, 2, 3, 5)")
     args = ap.parse_args()
@@ -303,6 +351,9 @@ def main():
         return
     if args.sweep:
         run_sweep(args)
+        return
+    if args.lut:
+        run_lut(args)
         return
 
     import numpy as np
