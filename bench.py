@@ -289,7 +289,7 @@ def run_lut(args):
     T = nm_inputs.VIT_B_TOKENS
     choices = [(1, 4), (2, 4), (4, 8), (8, 8)]
     shapes = [LayerShape(R, K, T, n, m) for (R, K) in nm_inputs.VIT_B_LAYERS.values() for n, m in choices]
-    lut = measure_layers(shapes, reps=20, copies=4)
+    lut = measure_layers(shapes, reps=20)
     print(json.dumps({"lut_entries": len(lut)}), file=sys.stderr, flush=True)
 
     def stack(seed):
@@ -320,6 +320,70 @@ def run_lut(args):
         json.dump({"result": out, "lut": json.loads(lut.to_json())}, open(args.details, "w"), indent=1)
 
 
+def run_search(args):
+    """Latency-constrained layer-wise N:M search over the 48 ViT-B layers
+    (choices 1:4, 2:4, 4:8, 8:8): latencies from a freshly measured look-up
+    table (calibrated on one measured stack), quality proxy = retained
+    weight energy of seeded synthetic weights; for three budgets, the exact,
+    greedy and evolutionary solvers, and the evolutionary assignment's stack
+    timed on the GPU against its budget."""
+    import numpy as np
+    import torch
+
+    import nm_inputs
+    from semi_structured_sparse_nm_amd.lut import LayerShape, measure_layers, time_stack
+    from semi_structured_sparse_nm_amd.search import (Problem, retained_energy, solve_evolutionary, solve_exact,
+                                                      solve_greedy)
+
+    torch.cuda.set_device(0)
+    T = nm_inputs.VIT_B_TOKENS
+    choices = [(1, 4), (2, 4), (4, 8), (8, 8)]
+    dims = list(nm_inputs.VIT_B_LAYERS.values())
+    shapes = [LayerShape(R, K, T, n, m) for (R, K) in dims for n, m in choices]
+    lut = measure_layers(shapes, reps=20)
+    layer_dims = [dims[i % 4] for i in range(48)]
+
+    def stack(assign):
+        return [LayerShape(R, K, T, *choices[c]) for (R, K), c in zip(layer_dims, assign)]
+
+    calib = [c for c in np.random.default_rng(0).integers(0, 4, 48)]
+    lut.calibrate(stack(calib), time_stack(stack(calib), reps=3))
+    rng = np.random.default_rng(2024)
+    energy, score = [], np.zeros((48, 4))
+    for l, (R, K) in enumerate(layer_dims):
+        W = rng.standard_normal((R, K)) * 0.02
+        energy.append(float((W * W).sum()))
+        for c, (n, m) in enumerate(choices):
+            score[l, c] = retained_energy(W, n, m)
+    score *= (np.array(energy) / sum(energy))[:, None]     # model-level retained energy fraction
+    # a layer's latency in the stack: its table entry plus the calibrated gap
+    lat = np.array([[lut.lookup(LayerShape(R, K, T, *nm)) + lut.gap_us for nm in choices]
+                    for (R, K) in layer_dims])
+    fastest, dense = lat.min(axis=1).sum(), lat[:, 3].sum()
+    results = []
+    for frac in (0.25, 0.5, 0.75):
+        budget = fastest + frac * (dense - fastest)
+        p = Problem(score, lat, budget)
+        ex, gr = solve_exact(p, res=0.01), solve_greedy(p)
+        t0 = time.perf_counter()
+        ev = solve_evolutionary(p, pop=64, generations=200, seed=0)
+        ev_s = time.perf_counter() - t0
+        measured = time_stack(stack(ev.choice), reps=3, seed=11)
+        results.append({"budget_us": round(budget, 1), "exact_value": round(ex.value, 5),
+                        "greedy_value": round(gr.value, 5), "evolutionary_value": round(ev.value, 5),
+                        "evolutionary_predicted_us": round(ev.latency, 1), "evolutionary_measured_us": round(measured, 1),
+                        "measured_over_budget": round(measured / budget - 1, 4), "evolutionary_s": round(ev_s, 2),
+                        "choice_counts": {f"{n}:{m}": int(sum(1 for c in ev.choice if choices[c] == (n, m)))
+                                          for n, m in choices}})
+        print(json.dumps(results[-1]), file=sys.stderr, flush=True)
+    out = {"search": "vitb_int8_48_layers", "choices": ["1:4", "2:4", "4:8", "8:8"],
+           "objective": "retained weight energy (proxy)", "all_fastest_us": round(fastest, 1),
+           "all_dense_us": round(dense, 1), "gap_us_per_launch": round(lut.gap_us, 2), "budgets": results}
+    print(json.dumps(out), flush=True)
+    if args.details:
+        json.dump(out, open(args.details, "w"), indent=1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +402,8 @@ def main():
     ap.add_argument("--lut", action="store_true",
                     help="build the latency look-up table of the mixed ViT-B stack and validate it on "
                          "stacks of other N:M draws")
+    ap.add_argument("--search", action="store_true",
+                    help="latency-constrained layer-wise N:M search over the ViT-B stack, solutions timed")
     ap.add_argument("--sweep", default="",
                     help="comma-separated workload sets to time layer by layer (1, 2, 3, 5)")
     args = ap.parse_args()
@@ -354,6 +420,9 @@ def main():
         return
     if args.lut:
         run_lut(args)
+        return
+    if args.search:
+        run_search(args)
         return
 
     import numpy as np

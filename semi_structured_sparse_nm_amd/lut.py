@@ -187,12 +187,19 @@ def _graph_time(items, reps: int) -> float:
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
+def _footprint(layer: LayerShape) -> int:
+    eb = {"i8": 1, "f16": 2, "bf16": 2}[layer.dt]
+    ob = {"i8": 1, "i32": 4, "f16": 2, "bf16": 2, "f32": 4}[layer.out]
+    return layer.R * layer.K * eb * layer.N // layer.M + layer.K * layer.T * eb + layer.R * layer.T * ob
+
+
 def measure_layers(layers: Iterable[LayerShape], lut: LatencyLUT | None = None, reps: int = 20,
-                   copies: int = 4, seed: int = 0) -> LatencyLUT:
+                   rotate_bytes: int = 1 << 30, max_copies: int = 32, seed: int = 0) -> LatencyLUT:
     """Measure every distinct layer shape of ``layers`` into ``lut`` (a new
-    one by default): ``copies`` independent operand sets launched in turn, so
-    consecutive launches do not find their inputs in the caches, as in a
-    stack of distinct layers."""
+    one by default).  Independent operand sets totalling at least
+    ``rotate_bytes`` (more than the 256 MB Infinity Cache) are launched in
+    turn, so no launch finds its inputs in the caches -- the state a layer
+    meets in a stack of distinct layers."""
     import torch
 
     device = torch.device("cuda", torch.cuda.current_device())
@@ -202,8 +209,9 @@ def measure_layers(layers: Iterable[LayerShape], lut: LatencyLUT | None = None, 
         if (L.key, L.T) in seen:
             continue
         seen.add((L.key, L.T))
+        copies = max(2, min(max_copies, -(-rotate_bytes // _footprint(L))))
         items = [_build(L, seed + 101 * c, device) for c in range(copies)]
-        lut.add(L, _graph_time(items, reps) / copies)
+        lut.add(L, _graph_time(items, max(reps, copies)) / copies)
         del items
         torch.cuda.empty_cache()
     return lut

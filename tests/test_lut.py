@@ -80,7 +80,7 @@ def test_measured_table_predicts_a_measured_stack():
     (other order and mix) within 35%."""
     from semi_structured_sparse_nm_amd.lut import measure_layers, time_stack
     shapes = [L(T=4096, R=2048, K=1024, N=n, M=m) for n, m in ((1, 4), (2, 4), (4, 8), (8, 8))]
-    lut = measure_layers(shapes, reps=10, copies=3)
+    lut = measure_layers(shapes, reps=10)
     assert len(lut) == 4 and all(lut.lookup(s) > 0 for s in shapes)
     calib = [shapes[i] for i in (0, 1, 2, 3, 1, 2)]
     lut.calibrate(calib, time_stack(calib, reps=3))
