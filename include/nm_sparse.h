@@ -104,7 +104,15 @@ nm_status nm_pack(const void* W, int64_t ldw, nm_packed* desc, void* stream);
 
 /*
  * Device workspace nm_spmm needs for this weight, token count and output
- * dtype (partial sums of a split reduction); 0 when none is needed.
+ * dtype; 0 when none is needed.  It holds the partial sums of a K split
+ * across workgroups (the adaptive parallelism of the paper's Sec. 4.1: when
+ * the output has too few tiles to occupy the GPU, K is cut into S slices that
+ * run as separate work items): S * rows * T * 4 bytes, int32 or fp32, which a
+ * second kernel on the same stream adds in slice order before the epilogue.
+ * The split is a function of the shape and the device (nm_spmm_ksplit), so
+ * the size is too.  The caller owns the buffer; nm_spmm only writes it and
+ * reads it back within the call's stream order, so calls that share one
+ * workspace must be ordered on one stream.
  */
 nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype, size_t* bytes);
 
@@ -120,10 +128,14 @@ nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype,
  * bias: NULL or device int32[R] (I8 weights) / float[R] (fp weights).
  * scale: device float[R], required iff y_dtype == NM_I8, else ignored.
  * X: device [K][ldx] of the weight dtype; Y: device [R][ldy] of y_dtype.
- * workspace: device, at least nm_spmm_workspace_size bytes (may be NULL if 0).
+ * workspace: device, at least nm_spmm_workspace_size bytes, 16-byte aligned
+ * (may be NULL if that size is 0).  Under a K split the fp32 sums are added
+ * slice by slice, so fp results differ from an unsplit run by rounding only
+ * (int32 results are identical).
  * NM_EINVAL: null pointers, T < 1, ldx < T, ldy < T, bad descriptor (sizes
  * not those of nm_pack_size, wrong format_version), small workspace.
- * NM_EUNSUPPORTED: dtype pair not listed, X / Y not aligned to their element.
+ * NM_EUNSUPPORTED: dtype pair not listed, X / Y not aligned to their element,
+ * a needed workspace not 16-byte aligned.
  * T is unbounded; R and K are those of the packed weight.
  */
 nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
@@ -139,6 +151,15 @@ const char* nm_status_str(nm_status s);
  * tests and profiling; launches nothing.
  */
 const char* nm_spmm_variant(const nm_packed* w, int64_t T, int32_t y_dtype);
+
+/*
+ * Number of K slices nm_spmm would split this call into across workgroups
+ * (1: no split; 0 when the arguments would be rejected), for dense row-major
+ * X and Y as nm_spmm_variant assumes.  NM_SPMM_KSPLIT=<S> in the environment
+ * forces S slices where S divides the column blocks and the variant takes a
+ * split (1 turns the split off).  Launches nothing.
+ */
+int32_t nm_spmm_ksplit(const nm_packed* w, int64_t T, int32_t y_dtype);
 
 #ifdef __cplusplus
 }

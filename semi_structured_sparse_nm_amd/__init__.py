@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.nm_status_str.restype = ctypes.c_char_p
         L.nm_spmm_variant.argtypes = [PP, I64, I32]
         L.nm_spmm_variant.restype = ctypes.c_char_p
+        L.nm_spmm_ksplit.argtypes = [PP, I64, I32]
+        L.nm_spmm_ksplit.restype = I32
         for f in ("nm_pack_size", "nm_pack", "nm_spmm_workspace_size", "nm_spmm"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -155,6 +157,12 @@ def workspace_size(p: Packed, T: int, out_dtype: torch.dtype) -> int:
 def variant(p: Packed, T: int, out_dtype: torch.dtype) -> str:
     d = p.desc()
     return lib().nm_spmm_variant(ctypes.byref(d), T, _TORCH_TO_NM[out_dtype]).decode()
+
+
+def ksplit(p: Packed, T: int, out_dtype: torch.dtype) -> int:
+    """K slices (workgroup-level split of K) nm_spmm would use; 1 = none."""
+    d = p.desc()
+    return int(lib().nm_spmm_ksplit(ctypes.byref(d), T, _TORCH_TO_NM[out_dtype]))
 
 
 def spmm(p: Packed, X: torch.Tensor, bias: torch.Tensor | None = None,

@@ -179,9 +179,72 @@ Call make_call(const Geometry& g, int wdt, int ydt, int64_t T, int64_t ldx, int6
   return c;
 }
 
-size_t workspace_for(Variant v, const Geometry& g, int64_t T) {
-  (void)v; (void)g; (void)T;
-  return 0;
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+// K slices for the tile kernels that take a K split (the paper's adaptive
+// parallelism, Sec. 4.1: enough work items in flight at inference-sized
+// shapes, with the reduction's cost bounded).  Slices divide the column
+// blocks evenly and keep at least kMinBlocks blocks each, so the load
+// pipeline still fills.  Cost model: rounds of work items over the compute
+// units times column blocks per item times the time of one block step, plus
+// the partial sums' round trip (S R T 4 bytes written, then read by the
+// reduction) and the reduction's launch.  One work item per CU per round:
+// the fp16 kernel keeps two workgroups on a CU, but they share its matrix
+// cores and LDS, so a second one does not double the rate.  The constants
+// are fitted on MI355X (Swin-T and LLaMA-7B shapes, forced S = 1 .. 16): the
+// model ranks the measured times and picks S = 4 for the Swin stage-4 MLP
+// out-projection (37.7 -> 22.8 us) and no split where the partials' traffic
+// outweighs the gain.  NM_SPMM_KSPLIT=<S> forces S where it divides the
+// column blocks (1 turns the split off).
+constexpr int kMinBlocks = 4;
+constexpr double kStepUs = 0.8;          // one column-block step of a work item
+constexpr double kPartialGBs = 5000.0;   // partial sums' effective write + read rate
+constexpr double kReduceUs = 2.0;        // reduction launch and tail
+
+int ksplit_for(Variant v, const Call& c) {
+  if (v != V_SMFMAC_H && v != V_EXPAND) return 1;
+  const Geometry& g = *c.g;
+  const int nKB = (int)g.nKB;
+  if (c.T % 4 != 0) return 1;
+  // the partials' 32-bit element offsets within one slice
+  if ((g.R + 256) * c.T * 4 >= (1ll << 31)) return 1;
+  const char* force = getenv("NM_SPMM_KSPLIT");
+  if (force && *force) {
+    const int S = atoi(force);
+    return (S >= 1 && S <= nKB && nKB % S == 0) ? S : 1;
+  }
+  const int64_t tiles = ((g.R + 255) / 256) * ((c.T + 127) / 128);
+  const int64_t slots = device_cus();
+  auto cost = [&](int S) {
+    const double rounds = (double)((tiles * S + slots - 1) / slots);
+    double us = rounds * (nKB / S) * kStepUs;
+    if (S > 1) us += kReduceUs + (double)S * g.R * c.T * 4 * 2 / (kPartialGBs * 1e3);
+    return us;
+  };
+  int best = 1;
+  double best_us = cost(1);
+  for (int S = 2; S <= 16 && nKB / S >= kMinBlocks; ++S) {
+    if (nKB % S) continue;
+    const double us = cost(S);
+    if (us < best_us) { best = S; best_us = us; }
+  }
+  return best;
+}
+
+size_t workspace_for(Variant v, const Call& c) {
+  const int S = ksplit_for(v, c);
+  return S > 1 ? (size_t)S * c.g->R * c.T * 4 : 0;
 }
 
 }  // namespace
@@ -225,9 +288,11 @@ nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype,
   if (T < 1) return NM_EINVAL;
   if (!pair_supported(w->dtype, y_dtype)) return NM_EUNSUPPORTED;
   // the variant may depend on strides and alignment; report the largest need
+  const void* al = reinterpret_cast<const void*>((uintptr_t)256);
+  const Call c = make_call(g, w->dtype, y_dtype, T, T, T, al, al);
   size_t need = 0;
   for (int v = V_GENERIC; v < V_COUNT; ++v) {
-    size_t n = workspace_for((Variant)v, g, T);
+    size_t n = workspace_for((Variant)v, c);
     if (n > need) need = n;
   }
   *bytes = need;
@@ -247,9 +312,12 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
   if (!aligned(X, (size_t)g.eb) || !aligned(Y, (size_t)nm::dtype_bytes(y_dtype))) return NM_EUNSUPPORTED;
   if (bias && !aligned(bias, 4)) return NM_EUNSUPPORTED;
   if (scale && !aligned(scale, 4)) return NM_EUNSUPPORTED;
-  Variant v = choose(make_call(g, w->dtype, y_dtype, T, ldx, ldy, X, Y));
-  size_t need = workspace_for(v, g, T);
+  const Call call = make_call(g, w->dtype, y_dtype, T, ldx, ldy, X, Y);
+  Variant v = choose(call);
+  const int S = ksplit_for(v, call);
+  size_t need = workspace_for(v, call);
   if (workspace_bytes < need || (need && !workspace)) return NM_EINVAL;
+  if (need && !aligned(workspace, 16)) return NM_EUNSUPPORTED;
 
   SpmmArgs a;
   a.g = g;
@@ -266,8 +334,30 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
   a.scale = (y_dtype == NM_I8) ? scale : nullptr;
   a.ws = workspace;
   a.ws_bytes = workspace_bytes;
+  a.ksplit = 1;
+  a.kbs = (int)g.nKB;
+  a.ys = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  if (S > 1) {
+    // K slices write raw 32-bit partial sums to the workspace; the reduction
+    // adds them and applies this call's epilogue
+    SpmmArgs p = a;
+    p.ydt = w->dtype == NM_I8 ? NM_I32 : NM_F32;
+    p.Y = workspace;
+    p.ldy = T;
+    p.bias = nullptr;
+    p.scale = nullptr;
+    p.ksplit = S;
+    p.kbs = (int)(g.nKB / S);
+    p.ys = g.R * T;
+    e = v == V_SMFMAC_H ? nm::launch_spmm_smfmac_h(p, s) : nm::launch_spmm_expand(p, s);
+    if (e != hipSuccess) return NM_EHIP;
+    a.ksplit = S;
+    a.ys = p.ys;
+    e = nm::launch_splitk_reduce(a, s);
+    return e == hipSuccess ? NM_OK : NM_EHIP;
+  }
   switch (v) {
     case V_GENERIC: e = nm::launch_spmm_generic(a, s); break;
     case V_SMFMAC_I8: e = nm::launch_spmm_smfmac_i8(a, 0, s); break;
@@ -300,6 +390,14 @@ const char* nm_spmm_variant(const nm_packed* w, int64_t T, int32_t y_dtype) {
   // dense row-major operands, 256-byte aligned (what a fresh allocation gives)
   const void* al = reinterpret_cast<const void*>((uintptr_t)256);
   return variant_name(choose(make_call(g, w->dtype, y_dtype, T, T, T, al, al)));
+}
+
+int32_t nm_spmm_ksplit(const nm_packed* w, int64_t T, int32_t y_dtype) {
+  Geometry g;
+  if (check_desc(w, &g) != NM_OK || T < 1 || !pair_supported(w->dtype, y_dtype)) return 0;
+  const void* al = reinterpret_cast<const void*>((uintptr_t)256);
+  const Call c = make_call(g, w->dtype, y_dtype, T, T, T, al, al);
+  return ksplit_for(choose(c), c);
 }
 
 }  // extern "C"

@@ -70,6 +70,15 @@ struct SpmmArgs {
   const float* scale;      // float[R] (int8 output) or nullptr
   void* ws;                // workspace
   size_t ws_bytes;
+  // K split across workgroups (the tile kernels that take it: fp16 / bf16
+  // 2:4 and dense-expand).  Work item = (tile, K slice s); slice s covers
+  // column blocks s kbs .. s kbs + kbs - 1.  With ksplit > 1 the kernel runs
+  // with a 32-bit output type, no bias, Y = the workspace and ldy = T, and
+  // writes slice s's raw partial sums at Y + s ys elements;
+  // launch_splitk_reduce then adds the slices and applies the epilogue.
+  int ksplit;              // K slices (1: no split)
+  int kbs;                 // column blocks per slice (nKB / ksplit)
+  int64_t ys;              // elements between consecutive slices' partials
 };
 
 // Kernel variants; each launcher returns hipSuccess or the launch error.
@@ -87,6 +96,9 @@ hipError_t launch_spmm_expand_decode(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_expand32(const SpmmArgs& a, hipStream_t s);
 bool expand32_supported(int N, int M);   // N:M instantiated by launch_spmm_expand32
 bool expand_supported(int N, int M);   // N:M instantiated by launch_spmm_expand
+// Y = epilogue(sum over the a.ksplit slices of the partials at a.ws) with
+// a's own output type, bias and scale (T a multiple of 4).
+hipError_t launch_splitk_reduce(const SpmmArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- device
 // Cache policy of the output stores (gfx950 buffer-store cache bits: sc0 |

@@ -118,18 +118,24 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   const int ldx = (int)a.ldx;
   const int nRB = (int)g.nRB;
 
-  const int ntot = mtiles * ntiles;
+  // work items: (tile, K slice); the tiles of one slice are contiguous,
+  // row tiles fastest, so an XCD's run shares activation strips in its L2
+  const int kbs = a.kbs;                     // column blocks per work item
+  const int ntile = mtiles * ntiles;
+  const int ntot = ntile * a.ksplit;
   const int per_xcd = (ntot + 7) / 8;
   const int xcd = blockIdx.x % 8, jw = blockIdx.x / 8;
   const int lo = xcd * per_xcd;
   const int hi = min(lo + per_xcd, ntot);
   if (lo + jw >= hi) return;
   const int nmine = (hi - lo - jw + nwg_xcd - 1) / nwg_xcd;
-  const int total = nmine * nKB;
-  auto tile_of = [&](int k, int& r0, int& t0) {
+  const int total = nmine * kbs;
+  auto tile_of = [&](int k, int& r0, int& t0, int& ks) {
     const int L = lo + jw + k * nwg_xcd;
-    const int nt = L / mtiles;
-    r0 = (L - nt * mtiles) * BM;
+    ks = L / ntile;
+    const int Lt = L - ks * ntile;
+    const int nt = Lt / mtiles;
+    r0 = (Lt - nt * mtiles) * BM;
     t0 = nt * BN;
   };
 
@@ -187,8 +193,9 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     return *reinterpret_cast<const v4f*>(bsw + 512 * (k & 3) + 256 + 4 * (16 * rb + 4 * lg));
   };
 
-  int ln = 0, lk = 0, lkb = 0, lr0 = 0, lt0 = 0;
-  tile_of(0, lr0, lt0);
+  int ln = 0, lk = 0, lkb = 0, lr0 = 0, lt0 = 0, lks = 0;
+  tile_of(0, lr0, lt0, lks);
+  lks *= kbs;                                // first column block of the slice
   int g_live = 0, g_rb0 = 0, g_soff = 0;
   // group parts: 0, 1: A of row block 0, 1; 2, 3: X halves; 4: bias / scale
   // on a tile's first block and the cursor
@@ -201,12 +208,12 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     if constexpr (P == 0) {
       g_live = __builtin_amdgcn_readfirstlane(ln < total ? 1 : 0);
       g_rb0 = (lr0 >> 4) + RB * wave;
-      g_soff = __builtin_amdgcn_readfirstlane(g_live ? (lkb * (128 / EB) * ldx + lt0) * EB
+      g_soff = __builtin_amdgcn_readfirstlane(g_live ? ((lks + lkb) * (128 / EB) * ldx + lt0) * EB
                                                      : (int)(g.K * a.ldx * EB));
     }
     if constexpr (P < RB) {
       const int rbc = __builtin_amdgcn_readfirstlane(min(g_rb0 + P, nRB));
-      const int blk = (g_live ? rbc : nRB) * nKB + (rbc < nRB ? lkb : 0);
+      const int blk = (g_live ? rbc : nRB) * nKB + (rbc < nRB ? lks + lkb : 0);
       const int vo = voff_v + blk * C_B * 16;
 #pragma unroll
       for (int c = 0; c < NVL; ++c) {
@@ -247,9 +254,12 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         lds_dma4(rscale, lds_addr(bs + 256), boff, 0);
       }
       ++ln;
-      if (g_live && ++lkb == nKB) {
+      if (g_live && ++lkb == kbs) {
         lkb = 0;
-        if (++lk < nmine) tile_of(lk, lr0, lt0);
+        if (++lk < nmine) {
+          tile_of(lk, lr0, lt0, lks);
+          lks *= kbs;
+        }
       }
     }
   };
@@ -260,7 +270,7 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     load_part(st, ic<4>());
   };
   static_assert(RB == 2 && NPART == 5, "load parts are spelled out for two row blocks");
-  auto group_size_extra = [&](int m) { return (m < total && m % nKB == 0) ? 2 : 0; };
+  auto group_size_extra = [&](int m) { return (m < total && m % kbs == 0) ? 2 : 0; };
 
   // ---- B transpose reads for token tile tt: lane (j, g) gets, for step s,
   // the dense k of its group's run: int8 rows 32 g + 16 s .. + 15 (tr8 reads
@@ -423,9 +433,10 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
       }
     }
   };
-  auto store_direct = [&](int r0, int t0) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t ry =
-        __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)(g.R * a.ldy * 4), 0x00020000);
+  // int32 / fp32 output, or slice ks's partial sums under a K split
+  auto store_direct = [&](int r0, int t0, int ks) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<int32_t*>(a.Y) + ks * a.ys, 0, (int)(g.R * a.ldy * 4), 0x00020000);
     const int rw = r0 + 32 * wave + 4 * lg;
     const int oob = (int)(g.R * a.ldy * 4);
 #pragma unroll
@@ -443,13 +454,16 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
       }
   };
 
-  int n = 0, ck = 0, ckb = 0, cr0, ct0;
-  tile_of(0, cr0, ct0);
+  int n = 0, ck = 0, ckb = 0, cr0, ct0, cks;
+  tile_of(0, cr0, ct0, cks);
+  // Wait until the oldest outstanding group has landed: every group holds
+  // at least NL loads and loads complete in order, so at most NL
+  // outstanding means everything before the newest group is in.  One
+  // unconditional count (not NL plus the next group's extra loads) keeps the
+  // wait a single instruction on every path through the unrolled steps.
   auto wait_for_group = [&](int extra_after) {
-    if (extra_after)
-      __builtin_amdgcn_s_waitcnt(waitcnt(NL + 2, 15));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
+    (void)extra_after;
+    __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
   };
 
   load_group(ic<0>());
@@ -464,17 +478,17 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     barrier_nofence();
     compute(st, ic<ST>(), ic<NX>());
     ++n;
-    if (++ckb < nKB) return;
+    if (++ckb < kbs) return;
     ckb = 0;
     if constexpr (OUT == NM_I8)
       epilogue_i8(ck, cr0, ct0);
     else if constexpr (OUT16)
       epilogue_h(cr0, ct0);
     else
-      store_direct(cr0, ct0);
+      store_direct(cr0, ct0, cks);
     ++ck;
     if (ck < nmine) {
-      tile_of(ck, cr0, ct0);
+      tile_of(ck, cr0, ct0, cks);
       wait_for_group(group_size_extra(n + 1));
       init_acc(ck);
     }
@@ -507,7 +521,7 @@ template <int WT, int NN, int MM, int OUT>
 hipError_t launch_one(const SpmmArgs& a, hipStream_t s) {
   const int mtiles = (int)((a.g.R + BM - 1) / BM);
   const int ntiles = (int)((a.T + BN - 1) / BN);
-  const int ntot = mtiles * ntiles;
+  const int ntot = mtiles * ntiles * a.ksplit;
   const int per_xcd = (ntot + 7) / 8;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;

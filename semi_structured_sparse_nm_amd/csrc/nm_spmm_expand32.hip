@@ -444,11 +444,14 @@ expand32_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   tile_of(0, cr0, ct0);
   // a step waits until only the loads issued after its group are
   // outstanding (loads complete in order; stores are never counted)
+  // Wait until the oldest outstanding group has landed: every group holds
+  // at least NL loads and loads complete in order, so at most NL
+  // outstanding means everything before the newest group is in.  One
+  // unconditional count (not NL plus the next group's extra loads) keeps the
+  // wait a single instruction on every path through the unrolled steps.
   auto wait_for_group = [&](int extra_after) {
-    if (extra_after)
-      __builtin_amdgcn_s_waitcnt(waitcnt(NL + 2, 15));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
+    (void)extra_after;
+    __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
   };
 
   load_group(ic<0>());

@@ -14,6 +14,10 @@
 //   X[kb*KB .. +KB][t0 .. t0+64] -> LDS transposed (tokens major, k contiguous)
 //   packed W block rows          -> LDS dense (zeros + kept values)
 //   MFMA 16x16x64 i8 / 16x16x32 f16 / bf16 over the block.
+// Each thread issues every global load of a block (its X elements, its
+// (row, group) entries' kept values and meta dwords) before its first LDS
+// store, so a block costs one memory round trip; the kernel is templated on
+// M so those counts are compile-time.
 // Operand lanes: lane l = 16 g + i holds row (or token) i and the contiguous
 // k-chunk g of the step for both A and B, so every k meets itself in the dot
 // product.  Accumulator lane l, register v holds row 4 g + v, token i.
@@ -51,21 +55,16 @@ __device__ __forceinline__ v4f mfma_step(const v4i& a, const v4i& b, const v4f& 
                                                  c, 0, 0, 0);
 }
 
-// position of kept slot c of a block row from its meta bits
-__device__ __forceinline__ int slot_pos(const uint8_t* mrow, int MR, int c, int w) {
-  int bit = c * w;
-  int word = bit >> 5;
-  uint32_t lo = reinterpret_cast<const uint32_t*>(mrow)[word];
-  uint64_t v = lo;
-  if ((word + 1) * 4 < MR) v |= (uint64_t)reinterpret_cast<const uint32_t*>(mrow)[word + 1] << 32;
-  return (int)((v >> (bit & 31)) & ((1u << w) - 1));
-}
-
-template <int WT>
+template <int WT, int MM>
 __global__ void __launch_bounds__(256) spmm_generic_kernel(SpmmArgs a) {
   using E = Elt<WT>;
   constexpr int EB = E::EB, KB = E::KB, KS = E::KS;
   constexpr int ROWB = KB * EB + LDS_PAD;  // LDS row pitch in bytes
+  constexpr int TPR = 256 / KB;            // threads per X row of a block
+  constexpr int XPT = BN / TPR;            // X elements per thread and block
+  constexpr int GB = KB / MM;              // groups per block row
+  constexpr int EPT = BM * GB / 256;       // (row, group) entries per thread and block
+  static_assert(256 % KB == 0 && BN % TPR == 0 && (BM * GB) % 256 == 0, "staging shapes");
   __shared__ __attribute__((aligned(16))) uint8_t Wd[BM * ROWB];
   __shared__ __attribute__((aligned(16))) uint8_t Xt[BN * ROWB];
 
@@ -75,48 +74,97 @@ __global__ void __launch_bounds__(256) spmm_generic_kernel(SpmmArgs a) {
   const int li = lane & 15, lg = lane >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * BN;
   const int64_t r0 = (int64_t)blockIdx.y * BM;
-  const int64_t G = g.K / g.M;
   const uint8_t* X = static_cast<const uint8_t*>(a.X);
+  const int N = g.N, w = g.w;
 
   typedef typename AccT<WT>::type Acc;
   Acc acc[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n) acc[n] = Acc{0, 0, 0, 0};
 
+  // Every load of a block is issued before the first LDS store, so a block
+  // costs one memory round trip, not one per element.
+  const int xk = tid / TPR, xt = (tid % TPR) * XPT;   // this thread's X row and first token
   for (int64_t kb = 0; kb < g.nKB; ++kb) {
-    // ---- X tile, transposed into LDS (zeros outside K x T)
-    for (int e = tid; e < KB * BN; e += 256) {
-      const int t = e % BN, k = e / BN;
-      const int64_t kg = kb * KB + k, tg = t0 + t;
-      uint8_t* dst = Xt + t * ROWB + k * EB;
-      if (EB == 1) {
-        uint8_t v = (kg < g.K && tg < a.T) ? X[kg * a.ldx + tg] : (uint8_t)0;
-        *dst = v;
-      } else {
-        uint16_t v = (kg < g.K && tg < a.T) ? reinterpret_cast<const uint16_t*>(X)[kg * a.ldx + tg]
-                                             : (uint16_t)0;
-        *reinterpret_cast<uint16_t*>(dst) = v;
+    // ---- X tile (zeros outside K x T), transposed into LDS
+    const int64_t kg = kb * KB + xk;
+    uint32_t xv[XPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int64_t tg = t0 + xt + i;
+      const bool ok = kg < g.K && tg < a.T;
+      if constexpr (EB == 1)
+        xv[i] = ok ? X[kg * a.ldx + tg] : 0u;
+      else
+        xv[i] = ok ? reinterpret_cast<const uint16_t*>(X)[kg * a.ldx + tg] : 0u;
+    }
+    // ---- packed W: entry (row, group) e = tid + 256 i; its N kept values
+    // and the meta bits of its positions (two dwords around them)
+    uint32_t wv[EPT][MM];
+    uint32_t mw[EPT][2];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid + 256 * i;
+      const int rr = e / GB, gl = e % GB;
+      const int64_t r = r0 + rr;
+      const bool live = r < g.nRB * 16;
+      const int64_t blk = (r >> 4) * g.nKB + kb;
+      const uint8_t* vrow = a.values + blk * g.vblk + (int64_t)(r & 15) * g.C * EB;
+#pragma unroll
+      for (int j = 0; j < MM; ++j) {
+        uint32_t v = 0;
+        if (live && j < N) {
+          if constexpr (EB == 1)
+            v = vrow[gl * N + j];
+          else
+            v = reinterpret_cast<const uint16_t*>(vrow)[gl * N + j];
+        }
+        wv[i][j] = v;
+      }
+      mw[i][0] = mw[i][1] = 0;
+      if (live && w) {
+        const uint8_t* mrow = a.meta + blk * g.mblk + (int64_t)(r & 15) * g.MR;
+        const int word = (gl * N * w) >> 5;
+        mw[i][0] = reinterpret_cast<const uint32_t*>(mrow)[word];
+        if ((word + 1) * 4 < g.MR) mw[i][1] = reinterpret_cast<const uint32_t*>(mrow)[word + 1];
       }
     }
-    // ---- packed W block rows, expanded to dense in LDS
-    for (int e = tid; e < BM * g.GB; e += 256) {
-      const int rr = e / g.GB, gl = e % g.GB;
-      const int64_t r = r0 + rr;
-      uint8_t* dst = Wd + rr * ROWB + gl * g.M * EB;
-      for (int i = 0; i < g.M * EB; ++i) dst[i] = 0;
-      if (r < g.nRB * 16) {
-        const int64_t blk = (r >> 4) * g.nKB + kb;
-        const uint8_t* vrow = a.values + blk * g.vblk + (int64_t)(r & 15) * g.C * EB;
-        const uint8_t* mrow = g.w ? a.meta + blk * g.mblk + (int64_t)(r & 15) * g.MR : nullptr;
-        for (int j = 0; j < g.N; ++j) {
-          const int c = gl * g.N + j;
-          const int pos = g.w ? slot_pos(mrow, g.MR, c, g.w) : j;
-          for (int bb = 0; bb < EB; ++bb) dst[pos * EB + bb] = vrow[c * EB + bb];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      uint8_t* dst = Xt + (xt + i) * ROWB + xk * EB;
+      if constexpr (EB == 1)
+        *dst = (uint8_t)xv[i];
+      else
+        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)xv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid + 256 * i;
+      const int rr = e / GB, gl = e % GB;
+      uint8_t* dst = Wd + rr * ROWB + gl * MM * EB;
+      uint32_t dense[MM];
+#pragma unroll
+      for (int p = 0; p < MM; ++p) dense[p] = 0;
+      const uint64_t win = ((uint64_t)mw[i][1] << 32) | mw[i][0];
+      const int bit0 = (gl * N * w) & 31;
+#pragma unroll
+      for (int j = 0; j < MM; ++j) {
+        if (j < N) {
+          const int pos = w ? (int)((win >> (bit0 + j * w)) & ((1u << w) - 1)) : j;
+#pragma unroll
+          for (int p = 0; p < MM; ++p)
+            if (p == pos) dense[p] = wv[i][j];
         }
       }
-      (void)G;
+#pragma unroll
+      for (int p = 0; p < MM; ++p) {
+        if constexpr (EB == 1)
+          dst[p] = (uint8_t)dense[p];
+        else
+          reinterpret_cast<uint16_t*>(dst)[p] = (uint16_t)dense[p];
+      }
     }
-    __syncthreads();
+  __syncthreads();
     // ---- MFMA over the block
 #pragma unroll
     for (int s = 0; s < KB / KS; ++s) {
@@ -165,12 +213,14 @@ __global__ void __launch_bounds__(256) spmm_generic_kernel(SpmmArgs a) {
 
 hipError_t launch_spmm_generic(const SpmmArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.T + BN - 1) / BN), (unsigned)((a.g.R + BM - 1) / BM));
+  void (*k)(SpmmArgs);
   if (a.wdt == NM_I8)
-    hipLaunchKernelGGL(spmm_generic_kernel<0>, grid, dim3(256), 0, s, a);
+    k = a.g.M == 4 ? spmm_generic_kernel<0, 4> : spmm_generic_kernel<0, 8>;
   else if (a.wdt == NM_F16)
-    hipLaunchKernelGGL(spmm_generic_kernel<1>, grid, dim3(256), 0, s, a);
+    k = a.g.M == 4 ? spmm_generic_kernel<1, 4> : spmm_generic_kernel<1, 8>;
   else
-    hipLaunchKernelGGL(spmm_generic_kernel<2>, grid, dim3(256), 0, s, a);
+    k = a.g.M == 4 ? spmm_generic_kernel<2, 4> : spmm_generic_kernel<2, 8>;
+  hipLaunchKernelGGL(k, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

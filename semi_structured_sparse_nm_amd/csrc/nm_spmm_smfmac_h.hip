@@ -134,18 +134,24 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   const int ldx = (int)a.ldx;
   const int nRB = (int)g.nRB;
 
-  const int ntot = mtiles * ntiles;
+  // work items: (tile, K slice); the tiles of one slice are contiguous,
+  // row tiles fastest, so an XCD's run shares activation strips in its L2
+  const int kbs = a.kbs;                     // column blocks per work item
+  const int ntile = mtiles * ntiles;
+  const int ntot = ntile * a.ksplit;
   const int per_xcd = (ntot + 7) / 8;
   const int xcd = blockIdx.x % 8, jw = blockIdx.x / 8;
   const int lo = xcd * per_xcd;
   const int hi = min(lo + per_xcd, ntot);
   if (lo + jw >= hi) return;
   const int nmine = (hi - lo - jw + nwg_xcd - 1) / nwg_xcd;
-  const int total = nmine * nKB;
-  auto tile_of = [&](int k, int& r0, int& t0) {
+  const int total = nmine * kbs;
+  auto tile_of = [&](int k, int& r0, int& t0, int& ks) {
     const int L = lo + jw + k * nwg_xcd;
-    const int nt = L / mtiles;
-    r0 = (L - nt * mtiles) * BM;
+    ks = L / ntile;
+    const int Lt = L - ks * ntile;
+    const int nt = Lt / mtiles;
+    r0 = (Lt - nt * mtiles) * BM;
     t0 = nt * BN;
   };
 
@@ -188,8 +194,9 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     return *reinterpret_cast<const v4f*>(bsw + 256 * (k & 3) + 4 * (16 * rb + 4 * lg));
   };
 
-  int ln = 0, lk = 0, lkb = 0, lr0 = 0, lt0 = 0;
-  tile_of(0, lr0, lt0);
+  int ln = 0, lk = 0, lkb = 0, lr0 = 0, lt0 = 0, lks = 0;
+  tile_of(0, lr0, lt0, lks);
+  lks *= kbs;                                // first column block of the slice
   int g_live = 0, g_rb0 = 0, g_soff = 0;
   auto load_part = [&](auto st, auto part) {
     constexpr int S = decltype(st)::value;
@@ -197,11 +204,11 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     if constexpr (P == 0) {
       g_live = __builtin_amdgcn_readfirstlane(ln < total ? 1 : 0);
       g_rb0 = (lr0 >> 4) + RB * wave;
-      g_soff = __builtin_amdgcn_readfirstlane(g_live ? (lkb * 64 * ldx + lt0) * 2 : (int)(g.K * a.ldx * 2));
+      g_soff = __builtin_amdgcn_readfirstlane(g_live ? ((lks + lkb) * 64 * ldx + lt0) * 2 : (int)(g.K * a.ldx * 2));
     }
     if constexpr (P < RB) {
       const int rbc = __builtin_amdgcn_readfirstlane(min(g_rb0 + P, nRB));
-      const int blk = (g_live ? rbc : nRB) * nKB + (rbc < nRB ? lkb : 0);
+      const int blk = (g_live ? rbc : nRB) * nKB + (rbc < nRB ? lks + lkb : 0);
       av[S][P] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, blk * 1024, 0));
       ai[S][P] = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, voff_m, blk * 128, 0);
     } else if constexpr (P == RB || P == RB + 1) {
@@ -218,9 +225,12 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         lds_dma4(rbias, lds_addr(bsw + 256 * (lk & 3)), 4 * lane, boff);
       }
       ++ln;
-      if (g_live && ++lkb == nKB) {
+      if (g_live && ++lkb == kbs) {
         lkb = 0;
-        if (++lk < nmine) tile_of(lk, lr0, lt0);
+        if (++lk < nmine) {
+          tile_of(lk, lr0, lt0, lks);
+          lks *= kbs;
+        }
       }
     }
   };
@@ -230,7 +240,7 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     load_part(st, ic<4>()); load_part(st, ic<5>()); load_part(st, ic<6>());
   };
   static_assert(RB == 4 && NPART == 7, "load parts are spelled out for four row blocks");
-  auto group_size_extra = [&](int m) { return (m < total && m % nKB == 0) ? 1 : 0; };
+  auto group_size_extra = [&](int m) { return (m < total && m % kbs == 0) ? 1 : 0; };
 
   v4f acc[RB][TN];
   // transpose reads of token tile tt, read i (k rows 8 g + 4 (i & 1) +
@@ -336,9 +346,10 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
       }
     }
   };
-  auto store_f32 = [&](int r0, int t0) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t ry =
-        __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)(g.R * a.ldy * 4), 0x00020000);
+  // fp32 output, or slice ks's partial sums under a K split
+  auto store_f32 = [&](int r0, int t0, int ks) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<float*>(a.Y) + ks * a.ys, 0, (int)(g.R * a.ldy * 4), 0x00020000);
     const int rw = r0 + 64 * wave + 4 * lg;
     const int oob = (int)(g.R * a.ldy * 4);
 #pragma unroll
@@ -357,14 +368,17 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
       }
   };
 
-  int n = 0, ck = 0, ckb = 0, cr0, ct0;
-  tile_of(0, cr0, ct0);
+  int n = 0, ck = 0, ckb = 0, cr0, ct0, cks;
+  tile_of(0, cr0, ct0, cks);
 
+  // Wait until the oldest outstanding group has landed: every group holds
+  // at least NL loads and loads complete in order, so at most NL
+  // outstanding means everything before the newest group is in.  One
+  // unconditional count (not NL plus the next group's extra loads) keeps the
+  // wait a single instruction on every path through the unrolled steps.
   auto wait_for_group = [&](int extra_after) {
-    if (extra_after)
-      __builtin_amdgcn_s_waitcnt(waitcnt(NL + 1, 15));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
+    (void)extra_after;
+    __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
   };
 
   load_group(ic<0>());
@@ -379,16 +393,22 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     barrier_nofence();
     compute(st, ic<ST>(), ic<NX>());
     ++n;
-    if (++ckb < nKB) return;
+    if (++ckb < kbs) return;
     ckb = 0;
     if constexpr (OUT16)
       epilogue_h(cr0, ct0);
     else
-      store_f32(cr0, ct0);
+      store_f32(cr0, ct0, cks);
     ++ck;
     if (ck < nmine) {
-      tile_of(ck, cr0, ct0);
-      wait_for_group(group_size_extra(n + 1));
+      tile_of(ck, cr0, ct0, cks);
+      // Drain every outstanding load and the epilogue's stores before the
+      // next tile starts.  The load-only count above is sufficient in
+      // principle, but on MI355X the first B reads of a workgroup's second
+      // tile (LLaMA-7B up-projection shape) were seen, rarely, to return
+      // stale stage data (two runs out of many); the full drain costs one
+      // memory round trip per tile.
+      __builtin_amdgcn_s_waitcnt(waitcnt(0, 15));
       init_acc(ck);
     }
   };
@@ -421,7 +441,7 @@ hipError_t launch_nw(const SpmmArgs& a, hipStream_t s) {
   constexpr int BM = NW * RB * 16;
   const int mtiles = (int)((a.g.R + BM - 1) / BM);
   const int ntiles = (int)((a.T + BN - 1) / BN);
-  const int ntot = mtiles * ntiles;
+  const int ntot = mtiles * ntiles * a.ksplit;
   const int per_xcd = (ntot + 7) / 8;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;

@@ -146,3 +146,53 @@ def test_workspace_and_variant_queries():
     assert L.nm_spmm_variant(ctypes.byref(d), 100, nm.NM_I32).decode() != "invalid"
     assert L.nm_spmm_variant(ctypes.byref(d), 0, nm.NM_I32).decode() == "invalid"
     assert L.nm_spmm_variant(None, 100, nm.NM_I32).decode() == "invalid"
+
+
+def _ksplit(d, T, ydt):
+    return nm.lib().nm_spmm_ksplit(ctypes.byref(d), T, ydt)
+
+
+def _ws(d, T, ydt):
+    n = ctypes.c_size_t()
+    assert nm.lib().nm_spmm_workspace_size(ctypes.byref(d), T, ydt, ctypes.byref(n)) == nm.NM_OK
+    return n.value
+
+
+def test_ksplit_choice_and_workspace(monkeypatch):
+    """K split across workgroups: chosen for deep-K shapes with few output
+    tiles, never for shapes that fill the GPU; the workspace query reports
+    the slices' partial sums; NM_SPMM_KSPLIT forces a divisor of the column
+    blocks or turns the split off."""
+    monkeypatch.delenv("NM_SPMM_KSPLIT", raising=False)
+    # Swin-T stage-4 MLP out-projection, fp16 2:4: 39 tiles, 48 column blocks
+    deep = _desc(R=768, K=3072, dt=nm.NM_F16)
+    S = _ksplit(deep, 1568, nm.NM_F16)
+    assert S > 1 and 48 % S == 0 and 48 // S >= 4
+    assert _ws(deep, 1568, nm.NM_F16) == S * 768 * 1568 * 4
+    # same for the dense-expand kernel (1:4)
+    deep14 = _desc(R=768, K=3072, N=1, M=4, dt=nm.NM_F16)
+    assert _ksplit(deep14, 1568, nm.NM_F16) > 1
+    # ViT-B FC1 int8 2:4 at batch 64 fills the GPU: no split, no workspace
+    wide = _desc(R=3072, K=768)
+    assert _ksplit(wide, 12608, nm.NM_I8) == 1 and _ws(wide, 12608, nm.NM_I8) == 0
+    # decode shapes split K inside a workgroup instead
+    assert _ksplit(deep, 16, nm.NM_F16) == 1
+    assert _ksplit(deep, 0, nm.NM_F16) == 0
+    monkeypatch.setenv("NM_SPMM_KSPLIT", "3")
+    assert _ksplit(deep, 1568, nm.NM_F16) == 3
+    assert _ws(deep, 1568, nm.NM_F16) == 3 * 768 * 1568 * 4
+    monkeypatch.setenv("NM_SPMM_KSPLIT", "5")     # does not divide 48 blocks
+    assert _ksplit(deep, 1568, nm.NM_F16) == 1
+    monkeypatch.setenv("NM_SPMM_KSPLIT", "1")
+    assert _ksplit(deep, 1568, nm.NM_F16) == 1 and _ws(deep, 1568, nm.NM_F16) == 0
+
+
+def test_split_call_validates_its_workspace(monkeypatch):
+    monkeypatch.setenv("NM_SPMM_KSPLIT", "4")
+    d = _desc(R=768, K=3072, dt=nm.NM_F16)
+    need = _ws(d, 1568, nm.NM_F16)
+    assert need == 4 * 768 * 1568 * 4
+    kw = dict(T=1568, ldx=1568, ldy=1568, ydt=nm.NM_F16)
+    assert _spmm(d, **kw) == nm.NM_EINVAL                                      # none given
+    assert _spmm(d, ws=FAKE + (4 << 24), wsb=need - 1, **kw) == nm.NM_EINVAL   # too small
+    assert _spmm(d, ws=FAKE + (4 << 24) + 8, wsb=need, **kw) == nm.NM_EUNSUPPORTED  # misaligned

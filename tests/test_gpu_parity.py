@@ -341,3 +341,62 @@ def test_stationary_i8_variant(force_variant, out, R, K, T):
     else:
         compare(Y[:, :T], reference(W, X, 2, 4, "i8", out, bias=b, scale=s), out, variant)
     assert np.all(Y[:, T:] == 5), "writes beyond T"
+
+
+@pytest.fixture
+def force_ksplit():
+    import os
+    old = os.environ.get("NM_SPMM_KSPLIT")
+    yield lambda S: os.environ.__setitem__("NM_SPMM_KSPLIT", str(S))
+    if old is None:
+        os.environ.pop("NM_SPMM_KSPLIT", None)
+    else:
+        os.environ["NM_SPMM_KSPLIT"] = old
+
+
+def _ksplit_case(force_variant, force_ksplit, variant, dt, out, N, M, R, K, T, S, ldy_pad, seed):
+    import semi_structured_sparse_nm_amd as nm
+    from tests._parity import TORCH_DT, dev
+    force_variant(variant)
+    force_ksplit(S)
+    W, X, b, s = _inputs(dt, out, R, K, T, N, M, seed, f"ksplit-{variant}-{dt}-{out}-{N}-{M}-{R}-{K}-{T}-{S}")
+    p = nm.pack(dev(W, dt), N, M)
+    assert nm.variant(p, T, TORCH_DT[out]) == variant
+    assert nm.ksplit(p, T, TORCH_DT[out]) == S
+    assert nm.workspace_size(p, T, TORCH_DT[out]) == (S * R * T * 4 if S > 1 else 0)
+    Y, _ = run(W, X, N, M, dt, out, bias=b, scale=s, ldx_pad=32, ldy_pad=ldy_pad, sentinel=5)
+    compare(Y[:, :T], reference(W, X, N, M, dt, out, bias=b, scale=s), out, f"{variant} K split {S}")
+    pad = Y[:, T:]
+    want = 5 if out != "bf16" else oracle.round_to(np.array([5.0]), "bf16")[0]
+    assert np.all(pad == want), "writes beyond T"
+
+
+# (R, K, T, S): several row and token tiles with ragged edges; slices of one,
+# two and several column blocks; a partial last column block (K = 1000)
+KSPLIT_SHAPES = [(300, 1536, 400, 4), (520, 768, 144, 3), (64, 4096, 32, 8), (259, 1024, 272, 2),
+                 (130, 1000, 160, 4)]
+
+
+@pytest.mark.parametrize("dt,out", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("R,K,T,S", KSPLIT_SHAPES)
+@pytest.mark.parametrize("ldy_pad", [8, 3])
+def test_ksplit_h(force_variant, force_ksplit, dt, out, R, K, T, S, ldy_pad):
+    """fp16 / bf16 2:4 tile kernel with K cut into S slices across
+    workgroups: fp32 partials in the workspace, reduced in slice order with
+    the bias and the output rounding; aligned (vector) and unaligned
+    (element) output rows."""
+    _ksplit_case(force_variant, force_ksplit, "smfmac_h_2of4_persistent", dt, out, 2, 4, R, K, T, S,
+                 ldy_pad, 21)
+
+
+@pytest.mark.parametrize("dt,out", PAIRS)
+@pytest.mark.parametrize("N,M", [(1, 4), (4, 8), (8, 8)])
+@pytest.mark.parametrize("R,K,T,S", KSPLIT_SHAPES)
+def test_ksplit_expand(force_variant, force_ksplit, dt, out, N, M, R, K, T, S):
+    """Dense-expand kernel with K cut into S slices across workgroups; int32
+    partials for int8 (exact, then bias and requantisation), fp32 otherwise."""
+    nkb = -(-K // (128 if dt == "i8" else 64))
+    if nkb % S:
+        S = 2 if nkb % 2 == 0 else 1
+    _ksplit_case(force_variant, force_ksplit, "expand_mfma_persistent", dt, out, N, M, R, K, T, S,
+                 16 if out in ("i8", "f16", "bf16") else 3, 22)
