@@ -395,14 +395,14 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   int n = 0, ck = 0, ckb = 0, cr0, ct0;
   tile_of(0, cr0, ct0);
 
-  // Wait until the oldest outstanding group has landed: every group holds
-  // at least NL loads and loads complete in order, so at most NL
-  // outstanding means everything before the newest group is in.  One
-  // unconditional count (not NL plus the next group's extra loads) keeps the
-  // wait a single instruction on every path through the unrolled steps.
+  // wait until L(m) has landed, given the group issued after it (its
+  // size: NL, plus 2 when it starts a live tile); loads complete in order,
+  // and an epilogue's stores issued since only make the wait longer
   auto wait_for_group = [&](int extra_after) {
-    (void)extra_after;
-    __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
+    if (extra_after)
+      __builtin_amdgcn_s_waitcnt(waitcnt(NL + 2, 15));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
   };
 
   load_group(ic<0>());
