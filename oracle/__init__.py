@@ -58,6 +58,8 @@ def _load():
         L.orc_spmm_dense.argtypes = [P, P, I64, I64, I64, I, P, P]
         L.orc_spmm_direct.argtypes = [P, P, P, I64, I64, I64, I, I, I, P, I64, P, P, I]
         L.orc_requant_i8.argtypes = [P, I64, I64, P, P, P]
+        L.orc_gelu.argtypes = [P, I64, P]
+        L.orc_requant_gelu_i8.argtypes = [P, I64, I64, P, P, ctypes.c_float, ctypes.c_double, P, P]
         L.orc_read_packed.argtypes = [P, P, I64, I64, I, I, I, P, P]
         L.orc_check_padding.argtypes = [P, P, I64, I64, I, I, I]
         L.orc_check_padding.restype = ctypes.c_int64
@@ -148,6 +150,35 @@ def requant_i8(acc, bias=None, scale=None):
     return y
 
 
+def gelu(x):
+    """x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)) in float64 (the fused FC1
+    activation; the pages name none, this is the reading adopted)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    _ok(_load().orc_gelu(_ptr(x), x.size, _ptr(y)), "gelu")
+    return y
+
+
+# half-integer distance under which an int8 GELU decision is taken as open:
+# a binary32 evaluation (erf within a few ulps, three roundings) moves v by
+# at most ~1e-6 |v| <= 1.3e-4 for |v| <= 128.5, so 2e-4 covers it
+GELU_I8_TOL = 2e-4
+
+
+def requant_gelu_i8(acc, bias=None, scale=None, out_scale: float = 1.0, tol: float = GELU_I8_TOL):
+    """sat_int8(rne(gelu(f32(acc + bias[r]) * scale[r]) * out_scale)) and the
+    mask of decisions within `tol` of a half-integer."""
+    acc = np.ascontiguousarray(acc, dtype=np.int64)
+    R, T = acc.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.int32)
+    s = np.ascontiguousarray(scale, dtype=np.float32)
+    y = np.empty((R, T), dtype=np.int8)
+    near = np.empty((R, T), dtype=np.uint8)
+    _ok(_load().orc_requant_gelu_i8(_ptr(acc), R, T, _ptr(b), _ptr(s), float(out_scale), float(tol),
+                                    _ptr(y), _ptr(near)), "requant_gelu_i8")
+    return y, near.astype(bool)
+
+
 def read_packed(values, meta, R: int, K: int, N: int, M: int, dt: str):
     """Decode the GPU library's blocked packed layout into (vals, idx)."""
     values = np.ascontiguousarray(values).view(np.uint8)
@@ -204,14 +235,18 @@ def round_to(acc_f64, out: str):
 
 
 def reference(W, X, N: int, M: int, dt: str, out: str, bias=None, scale=None, rows=None,
-              nthreads: int = 0):
+              nthreads: int = 0, act: str = "none", out_scale: float = 1.0):
     """Whole chain: select -> direct compressed product -> epilogue.
 
     i8 inputs: out 'i32' gives acc + bias (int32 range), out 'i8' the
     requantised int8.  fp inputs: fp64 acc (+ bias) rounded once to `out`; with
     out == 'f64' the unrounded value.  `rows` restricts the output to those
     rows (bias/scale are then indexed by the original row numbers).
+    act == 'gelu': fp outputs take gelu of the fp64 value before rounding;
+    int8 outputs return (codes, open-decision mask) of requant_gelu_i8.
     """
+    if act not in ("none", "gelu"):
+        raise ValueError(act)
     R, K = W.shape
     vals, idx = compress(W, N, M, dt)
     acc = spmm_direct(vals, idx, X, R, K, N, M, dt, rows=rows, nthreads=nthreads)
@@ -223,8 +258,12 @@ def reference(W, X, N: int, M: int, dt: str, out: str, bias=None, scale=None, ro
             assert np.all(np.abs(y) < 2**31), "int32 range exceeded"
             return y.astype(np.int32)
         if out == "i8":
+            if act == "gelu":
+                return requant_gelu_i8(acc, b, np.asarray(scale, dtype=np.float32)[sel], out_scale)
             return requant_i8(acc, b, np.asarray(scale, dtype=np.float32)[sel])
         raise ValueError(out)
     if bias is not None:
         acc = acc + np.asarray(bias, dtype=np.float32).astype(np.float64)[sel][:, None]
+    if act == "gelu":
+        acc = gelu(acc)
     return acc if out == "f64" else round_to(acc, out)

@@ -248,6 +248,51 @@ int orc_requant_i8(const int64_t* acc, int64_t R, int64_t T, const int32_t* bias
 }
 
 /*
+ * GELU activation for the fused FC1 epilogue (the pages name no activation;
+ * the reading adopted is the exact Gaussian-error linear unit of the ViT /
+ * Swin MLP):  gelu(x) = x * Phi(x) = 0.5 * x * (1 + erf(x / sqrt(2))),
+ * evaluated in binary64 with the C library's erf.
+ */
+static double gelu64(double x) { return 0.5 * x * (1.0 + erf(x / sqrt(2.0))); }
+
+int orc_gelu(const double* x, int64_t n, double* y) {
+  if (n < 0) return -1;
+  for (int64_t i = 0; i < n; ++i) y[i] = gelu64(x[i]);
+  return 0;
+}
+
+/*
+ * int8 output with the activation between dequantisation and
+ * requantisation (reading adopted for a fused GELU on an int8 layer):
+ *   p = f32(acc + bias[r]) * scale[r]          (binary32, one rounding each,
+ *                                               as in orc_requant_i8)
+ *   v = gelu(p) * out_scale                    (exact value, binary64)
+ *   y = saturate_[-128,127]( round_half_even(v) )
+ * A fast path evaluates gelu and the second product in binary32 with its own
+ * erf, so its rounding decision may differ where v lies within a few binary32
+ * ulps of a half-integer; near[r][t] = 1 marks every v within `tol` of a
+ * half-integer (the caller accepts either neighbouring code there).
+ */
+int orc_requant_gelu_i8(const int64_t* acc, int64_t R, int64_t T, const int32_t* bias,
+                        const float* scale, float out_scale, double tol, int8_t* y, uint8_t* near) {
+  if (R < 0 || T < 0 || !scale) return -1;
+  for (int64_t r = 0; r < R; ++r)
+    for (int64_t t = 0; t < T; ++t) {
+      int64_t a = acc[r * T + t] + (bias ? (int64_t)bias[r] : 0);
+      float f = (float)a;
+      volatile float p = f * scale[r];
+      double v = gelu64((double)p) * (double)out_scale;
+      double q = nearbyint(v);
+      if (q > 127.0) q = 127.0;
+      if (q < -128.0) q = -128.0;
+      y[r * T + t] = (int8_t)q;
+      double fr = v - floor(v);
+      near[r * T + t] = (uint8_t)(fabs(fr - 0.5) <= tol);
+    }
+  return 0;
+}
+
+/*
  * orc_read_packed: decode the GPU library's packed weight layout into the
  * canonical (vals, idx) form of orc_compress.  Written from the layout's
  * prose description, independently of the packer:
