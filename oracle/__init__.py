@@ -159,9 +159,9 @@ def gelu(x):
     return y
 
 
-# half-integer distance under which an int8 GELU decision is taken as open:
-# a binary32 evaluation (erf within a few ulps, three roundings) moves v by
-# at most ~1e-6 |v| <= 1.3e-4 for |v| <= 128.5, so 2e-4 covers it
+# smallest half-integer distance under which an int8 GELU decision is taken
+# as open; the C side widens it per element to four times the error bound of
+# a binary32 evaluation with an erf accurate to 6e-7 (see orc_requant_gelu_i8)
 GELU_I8_TOL = 2e-4
 
 

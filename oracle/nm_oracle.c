@@ -268,10 +268,14 @@ int orc_gelu(const double* x, int64_t n, double* y) {
  *                                               as in orc_requant_i8)
  *   v = gelu(p) * out_scale                    (exact value, binary64)
  *   y = saturate_[-128,127]( round_half_even(v) )
- * A fast path evaluates gelu and the second product in binary32 with its own
- * erf, so its rounding decision may differ where v lies within a few binary32
- * ulps of a half-integer; near[r][t] = 1 marks every v within `tol` of a
- * half-integer (the caller accepts either neighbouring code there).
+ * A fast path evaluates gelu and the second product in binary32 with an erf
+ * of absolute error up to 6e-7 (e.g. the rational approximation of
+ * Abramowitz & Stegun eq. 7.1.26, 1.5e-7, plus binary32 rounding), so its
+ * gelu is off by at most 2.5e-7 |p| + 2.4e-7 |gelu(p)| and its v by that
+ * times out_scale plus one rounding (6e-8 |v|); its rounding decision may
+ * therefore differ where v lies that close to a half-integer.  near[r][t] = 1
+ * marks every v within max(tol, 4 x that bound) of a half-integer (the
+ * caller accepts either neighbouring code there).
  */
 int orc_requant_gelu_i8(const int64_t* acc, int64_t R, int64_t T, const int32_t* bias,
                         const float* scale, float out_scale, double tol, int8_t* y, uint8_t* near) {
@@ -286,8 +290,12 @@ int orc_requant_gelu_i8(const int64_t* acc, int64_t R, int64_t T, const int32_t*
       if (q > 127.0) q = 127.0;
       if (q < -128.0) q = -128.0;
       y[r * T + t] = (int8_t)q;
+      double g = gelu64((double)p);
+      double band = 4.0 * (fabs((double)out_scale) * (2.5e-7 * fabs((double)p) + 2.4e-7 * fabs(g)) +
+                           6e-8 * fabs(v));
+      if (band < tol) band = tol;
       double fr = v - floor(v);
-      near[r * T + t] = (uint8_t)(fabs(fr - 0.5) <= tol);
+      near[r * T + t] = (uint8_t)(fabs(fr - 0.5) <= band);
     }
   return 0;
 }
