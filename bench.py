@@ -320,6 +320,99 @@ def run_lut(args):
         json.dump({"result": out, "lut": json.loads(lut.to_json())}, open(args.details, "w"), indent=1)
 
 
+def run_chain(args):
+    """The ViT-B MLP in int8 on the device: FC1 (3072 x 768, 2:4) with GELU
+    fused and requantised to int8, whose [3072][T] output is FC2's (768 x
+    3072, 2:4) activation as it stands, T = 12608.  Timed as HIP-graph
+    replays over rotated operand sets (>= 1 GiB, every set with its own
+    packed weights): the two-layer chain, FC1 with GELU alone, FC1 with the
+    plain requantisation alone (the activation's cost is the difference) and
+    FC2 alone.  Inputs follow nm_inputs.mlp_chain; parity of this
+    configuration is covered by the tests (sampled token columns at full
+    size)."""
+    import torch
+
+    import nm_inputs
+    import semi_structured_sparse_nm_amd as nm
+
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T = nm_inputs.VIT_B_TOKENS
+    c = nm_inputs.mlp_chain(3072, 768, T, 2, 4, 0, "vitb_mlp")
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    p1, p2 = nm.pack(d(c.W1), 2, 4), nm.pack(d(c.W2), 2, 4)
+    X0, b1, s1, b2, s2 = d(c.X), d(c.b1), d(c.s_deq1), d(c.b2), d(c.scale2)
+    foot = 3072 * 768 // 2 * 5 // 4 + 768 * 3072 // 2 * 5 // 4 + 768 * T + 3072 * T + 768 * T
+    nsets = max(2, math.ceil(args.rotate_gib * 2**30 / foot))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+
+    def clone(p):
+        return nm.Packed(p.rows, p.K, p.N, p.M, p.dtype, p.values.clone(),
+                         None if p.meta is None else p.meta.clone(), p.format_version)
+
+    sets = []
+    for i in range(nsets):
+        X = X0 if i == 0 else X0[:, torch.randperm(T, device=dev, generator=gen)].contiguous()
+        sets.append((clone(p1), clone(p2), X, torch.empty((3072, T), dtype=torch.int8, device=dev),
+                     torch.empty((768, T), dtype=torch.int8, device=dev)))
+    torch.cuda.synchronize()
+
+    def fc1(j, act="gelu"):
+        q1, q2, X, H, Y = sets[j % nsets]
+        nm.spmm(q1, X, bias=b1, scale=s1, out_dtype=torch.int8, out=H, act=act, out_scale=c.os1)
+
+    def fc2(j):
+        q1, q2, X, H, Y = sets[j % nsets]
+        nm.spmm(q2, H, bias=b2, scale=s2, out_dtype=torch.int8, out=Y)
+
+    def graph_us(fn, reps):
+        for j in range(nsets):
+            fn(j)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                for j in range(reps):
+                    fn(j)
+        torch.cuda.current_stream().wait_stream(st)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    reps = max(nsets, 20)
+    chain = graph_us(lambda j: (fc1(j), fc2(j)), reps)
+    fc1_gelu = graph_us(fc1, reps)
+    fc1_plain = graph_us(lambda j: fc1(j, "none"), reps)
+    fc2_us = graph_us(fc2, reps)
+    L1 = nm_inputs.Layer("vitb_fc1_2of4_gelu", 3072, 768, T, 2, 4, "i8", "i8")
+    L2 = nm_inputs.Layer("vitb_fc2_2of4", 768, 3072, T, 2, 4, "i8", "i8")
+    roof, dense = 0.0, 0.0
+    for L in (L1, L2):
+        ops, nbytes, dn = nm_inputs.ops_and_bytes(L)
+        roof += max(nbytes / (HBM_PEAK_GBS * 1e9), ops / (MFMA_PEAK_TOPS["i8"] * 1e12)) * 1e6
+        dense += dn
+    out = {"chain": "vitb_mlp_fc1_gelu_fc2_int8_2of4", "tokens": T, "rotated_sets": nsets,
+           "chain_us": round(chain, 2), "fc1_gelu_us": round(fc1_gelu, 2), "fc1_plain_us": round(fc1_plain, 2),
+           "gelu_cost_us": round(fc1_gelu - fc1_plain, 2), "fc2_us": round(fc2_us, 2),
+           "kernels": {"fc1_gelu": nm.variant(p1, T, torch.int8, act="gelu"),
+                       "fc1_plain": nm.variant(p1, T, torch.int8), "fc2": nm.variant(p2, T, torch.int8)},
+           "sum_roof_us": round(roof, 2), "roofline_fraction": round(roof / chain, 4),
+           "dense_equivalent_TOPS": round(dense / (chain * 1e-6) / 1e12, 1)}
+    if args.details:
+        json.dump(out, open(args.details, "w"), indent=1)
+    print(json.dumps(out), flush=True)
+
+
 def run_search(args):
     """Latency-constrained layer-wise N:M search over the 48 ViT-B layers
     (choices 1:4, 2:4, 4:8, 8:8): latencies from a freshly measured look-up
@@ -404,6 +497,8 @@ def main():
                          "stacks of other N:M draws")
     ap.add_argument("--search", action="store_true",
                     help="latency-constrained layer-wise N:M search over the ViT-B stack, solutions timed")
+    ap.add_argument("--chain", action="store_true",
+                    help="time the int8 ViT-B MLP: FC1 with GELU fused, chained into FC2 on the device")
     ap.add_argument("--sweep", default="",
                     help="comma-separated workload sets to time layer by layer (1, 2, 3, 5)")
     args = ap.parse_args()
@@ -423,6 +518,9 @@ def main():
         return
     if args.search:
         run_search(args)
+        return
+    if args.chain:
+        run_chain(args)
         return
 
     import numpy as np

@@ -49,6 +49,9 @@ typedef enum {
 
 typedef enum { NM_I8 = 0, NM_F16 = 1, NM_BF16 = 2, NM_I32 = 3, NM_F32 = 4 } nm_dtype;
 
+/* Activation fused into nm_spmm_act's epilogue. */
+typedef enum { NM_ACT_NONE = 0, NM_ACT_GELU = 1 } nm_act;
+
 #define NM_FORMAT_VERSION 1u
 
 /*
@@ -142,6 +145,29 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
                   int32_t y_dtype, const void* bias, const float* scale, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/*
+ * nm_spmm with an activation fused into the epilogue, for the MLP's first
+ * linear layer (the pages' workloads spend their time in the four linear
+ * layers of each Transformer block, Sec. 1; the activation between the two
+ * MLP layers is not described there -- GELU(x) = x Phi(x) =
+ * 0.5 x (1 + erf(x / sqrt 2)), the ViT / Swin activation, is the reading
+ * adopted).  Arguments as nm_spmm, plus:
+ *   act: NM_ACT_NONE (exactly nm_spmm) or NM_ACT_GELU.
+ *   out_scale: with an activation and y_dtype == NM_I8, the requantisation
+ *     splits in two around it:
+ *       y = sat_[-128,127](rne(act(f32(acc + bias[r]) * scale[r]) * out_scale))
+ *     (scale[r] dequantises to the layer's real output, out_scale quantises
+ *     the activation's output); ignored otherwise.  Computed in binary32, so
+ *     where the exact value lies within a few binary32 ulps of a half-integer
+ *     either neighbouring code may result.
+ * fp outputs: y = round_to_y(act(acc + bias[r])), act in binary32.
+ * NM_EUNSUPPORTED: act not listed, or an activation with y_dtype == NM_I32
+ * (raw accumulators); NM_EINVAL: out_scale not finite.
+ */
+nm_status nm_spmm_act(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
+                      int32_t y_dtype, const void* bias, const float* scale, int32_t act, float out_scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* nm_status_str(nm_status s);
 
@@ -152,14 +178,18 @@ const char* nm_status_str(nm_status s);
  */
 const char* nm_spmm_variant(const nm_packed* w, int64_t T, int32_t y_dtype);
 
+/* The same for nm_spmm_act with activation `act` (which kernels carry it
+ * can change the choice). */
+const char* nm_spmm_variant_act(const nm_packed* w, int64_t T, int32_t y_dtype, int32_t act);
+
 /*
- * Number of K slices nm_spmm would split this call into across workgroups
- * (1: no split; 0 when the arguments would be rejected), for dense row-major
- * X and Y as nm_spmm_variant assumes.  NM_SPMM_KSPLIT=<S> in the environment
+ * Number of K slices nm_spmm_act (nm_spmm: act = NM_ACT_NONE) would split
+ * this call into across workgroups (1: no split; 0 when the arguments would
+ * be rejected), for dense row-major X and Y as nm_spmm_variant assumes.  NM_SPMM_KSPLIT=<S> in the environment
  * forces S slices where S divides the column blocks and the variant takes a
  * split (1 turns the split off).  Launches nothing.
  */
-int32_t nm_spmm_ksplit(const nm_packed* w, int64_t T, int32_t y_dtype);
+int32_t nm_spmm_ksplit(const nm_packed* w, int64_t T, int32_t y_dtype, int32_t act);
 
 #ifdef __cplusplus
 }

@@ -90,6 +90,52 @@ def quant_layer(R: int, K: int, T: int, N: int, M: int, seed: int, *names,
     return QuantLayer(W=qw, X=qx, bias=bias, scale=scale, s_w=s_w, s_x=s_x)
 
 
+@dataclass
+class MlpChain:
+    """Two int8 layers of a Transformer MLP with GELU between them:
+    h = sat(rne(gelu(f32(W1 X + b1) * s_deq1[r]) * os1)), Y = requant(W2 h + b2, scale2)."""
+    W1: np.ndarray
+    X: np.ndarray
+    b1: np.ndarray
+    s_deq1: np.ndarray
+    os1: float
+    W2: np.ndarray
+    b2: np.ndarray
+    scale2: np.ndarray
+
+
+def mlp_chain(R1: int, K1: int, T: int, N: int, M: int, seed: int, *names,
+              w_sigma: float = 0.02, x_sigma: float = 1.0, b_sigma: float = 0.02) -> MlpChain:
+    """Synthetic int8 MLP (ViT-B FC1 -> GELU -> FC2: R1 = 3072, K1 = 768),
+    calibrated statically from input statistics (no pass over outputs).
+
+    FC1 as quant_layer; its dequantising scale is the real one,
+    s_deq1[r] = f32(s_w1[r] s_x), so FC1's real output p has per-row standard
+    deviation sigma_p[r] = s_deq1[r] sqrt((N/M) sum_k q_w1^2 mean(q_x^2)).
+    The hidden activation is quantised per tensor with s_h = 4 max_r sigma_p / 127
+    (os1 = 1 / s_h).  FC2: W2 [K1][R1] ~ N(0, w_sigma^2) quantised per row;
+    bias2 in the units s_w2 s_h; its requantising scale takes E[h^2] ~
+    mean_r sigma_p^2 / (2 s_h^2) (GELU passes about the positive half) in
+    quant_layer's formula."""
+    fc1 = quant_layer(R1, K1, T, N, M, seed, *names, "fc1", w_sigma=w_sigma, x_sigma=x_sigma,
+                      b_sigma=b_sigma)
+    s_deq1 = (fc1.s_w * fc1.s_x).astype(np.float32)
+    ex2 = float(np.mean(fc1.X.astype(np.float64) ** 2))
+    sig_p = s_deq1.astype(np.float64) * np.sqrt((N / M) * (fc1.W.astype(np.float64) ** 2).sum(axis=1) * ex2)
+    s_h = 4.0 * float(sig_p.max()) / 127.0
+    w2 = rng(seed, *names, "fc2", "W").standard_normal((K1, R1)) * w_sigma
+    bf2 = rng(seed, *names, "fc2", "bias").standard_normal(K1) * b_sigma
+    s_w2 = np.abs(w2).max(axis=1) / 127.0
+    s_w2[s_w2 == 0] = 1.0
+    qw2 = np.clip(np.rint(w2 / s_w2[:, None]), -127, 127).astype(np.int8)
+    b2 = np.rint(bf2 / (s_w2 * s_h)).astype(np.int32)
+    eh2 = float(np.mean(sig_p ** 2)) / (2.0 * s_h * s_h)
+    row = (N / M) * (qw2.astype(np.float64) ** 2).sum(axis=1) * eh2
+    scale2 = (127.0 / (4.0 * np.sqrt(row) + 1.0)).astype(np.float32)
+    return MlpChain(W1=fc1.W, X=fc1.X, b1=fc1.bias, s_deq1=s_deq1, os1=1.0 / s_h, W2=qw2, b2=b2,
+                    scale2=scale2)
+
+
 # ------------------------------------------------------------------ workloads
 @dataclass(frozen=True)
 class Layer:

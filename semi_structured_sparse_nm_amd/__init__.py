@@ -68,8 +68,12 @@ def lib() -> ctypes.CDLL:
         L.nm_status_str.restype = ctypes.c_char_p
         L.nm_spmm_variant.argtypes = [PP, I64, I32]
         L.nm_spmm_variant.restype = ctypes.c_char_p
-        L.nm_spmm_ksplit.argtypes = [PP, I64, I32]
+        L.nm_spmm_ksplit.argtypes = [PP, I64, I32, I32]
         L.nm_spmm_ksplit.restype = I32
+        L.nm_spmm_variant_act.argtypes = [PP, I64, I32, I32]
+        L.nm_spmm_variant_act.restype = ctypes.c_char_p
+        L.nm_spmm_act.argtypes = [PP, P, I64, I64, P, I64, I32, P, P, I32, ctypes.c_float, P, SZ, P]
+        L.nm_spmm_act.restype = ctypes.c_int
         for f in ("nm_pack_size", "nm_pack", "nm_spmm_workspace_size", "nm_spmm"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -154,21 +158,27 @@ def workspace_size(p: Packed, T: int, out_dtype: torch.dtype) -> int:
     return n.value
 
 
-def variant(p: Packed, T: int, out_dtype: torch.dtype) -> str:
+ACTS = {"none": 0, "gelu": 1}
+
+
+def variant(p: Packed, T: int, out_dtype: torch.dtype, act: str = "none") -> str:
     d = p.desc()
-    return lib().nm_spmm_variant(ctypes.byref(d), T, _TORCH_TO_NM[out_dtype]).decode()
+    return lib().nm_spmm_variant_act(ctypes.byref(d), T, _TORCH_TO_NM[out_dtype], ACTS[act]).decode()
 
 
-def ksplit(p: Packed, T: int, out_dtype: torch.dtype) -> int:
+def ksplit(p: Packed, T: int, out_dtype: torch.dtype, act: str = "none") -> int:
     """K slices (workgroup-level split of K) nm_spmm would use; 1 = none."""
     d = p.desc()
-    return int(lib().nm_spmm_ksplit(ctypes.byref(d), T, _TORCH_TO_NM[out_dtype]))
+    return int(lib().nm_spmm_ksplit(ctypes.byref(d), T, _TORCH_TO_NM[out_dtype], ACTS[act]))
 
 
 def spmm(p: Packed, X: torch.Tensor, bias: torch.Tensor | None = None,
          scale: torch.Tensor | None = None, out_dtype: torch.dtype | None = None,
-         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """nm_spmm: Y[R, T] = epilogue((mask . W) @ X) with X [K, T] (tokens contiguous)."""
+         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+         act: str = "none", out_scale: float = 1.0) -> torch.Tensor:
+    """nm_spmm (nm_spmm_act with `act` != "none"): Y[R, T] =
+    epilogue((mask . W) @ X) with X [K, T] (tokens contiguous); act "gelu"
+    fuses GELU into the epilogue (int8 output: out_scale requantises it)."""
     if X.dim() != 2 or X.stride(1) != 1:
         raise ValueError("X must be a 2-D tensor with unit stride along T")
     if X.shape[0] != p.K:
@@ -184,10 +194,10 @@ def spmm(p: Packed, X: torch.Tensor, bias: torch.Tensor | None = None,
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     d = p.desc()
-    st = lib().nm_spmm(ctypes.byref(d), X.data_ptr(), X.stride(0), T, out.data_ptr(), out.stride(0),
-                       _TORCH_TO_NM[out_dtype], None if bias is None else bias.data_ptr(),
-                       None if scale is None else scale.data_ptr(),
-                       None if workspace is None else workspace.data_ptr(),
-                       0 if workspace is None else workspace.numel(), _stream(X.device))
-    _check(st, "nm_spmm")
+    st = lib().nm_spmm_act(ctypes.byref(d), X.data_ptr(), X.stride(0), T, out.data_ptr(), out.stride(0),
+                           _TORCH_TO_NM[out_dtype], None if bias is None else bias.data_ptr(),
+                           None if scale is None else scale.data_ptr(), ACTS[act], float(out_scale),
+                           None if workspace is None else workspace.data_ptr(),
+                           0 if workspace is None else workspace.numel(), _stream(X.device))
+    _check(st, "nm_spmm_act" if act != "none" else "nm_spmm")
     return out

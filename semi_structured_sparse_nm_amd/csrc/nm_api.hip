@@ -83,9 +83,13 @@ struct Call {
   int64_t T, ldx, ldy;
   const void* X;
   const void* Y;
+  int act;
 };
 
 bool eligible(Variant v, const Call& c) {
+  // the 256 x 128 int8 kernel and the 32 x 32-fragment dense-expand kernel
+  // (tested alternatives, forced only) carry no fused activation
+  if (c.act != NM_ACT_NONE && (v == V_SMFMAC_I8 || v == V_EXPAND32)) return false;
   switch (v) {
     case V_GENERIC: return true;
     case V_SMFMAC_I8:
@@ -120,11 +124,13 @@ bool eligible(Variant v, const Call& c) {
              c.ldx % 8 == 0 && aligned(c.X, 16) && (c.g->K + 64) * c.ldx * 2 < (1ll << 31) &&
              c.g->values_bytes() < (1ull << 31);
     case V_EXPAND:
-      // an instantiated N:M other than 2:4; whole 16-token tiles; X rows in
+      // an instantiated N:M other than 2:4 (2:4 too with an activation, as
+      // a fallback for it); whole 16-token tiles; X rows in
       // whole 16-byte pieces; 32-bit buffer offsets that do not wrap for the
       // rows a tile reaches past K and R (up to 128 k and 256 rows); 8- and
       // 16-bit output stored as 16-byte row pieces
-      return nm::expand_supported(c.g->N, c.g->M) && !(c.g->N == 2 && c.g->M == 4) && c.T % 16 == 0 &&
+      return nm::expand_supported(c.g->N, c.g->M) && !(c.g->N == 2 && c.g->M == 4 && c.act == NM_ACT_NONE) &&
+             c.T % 16 == 0 &&
              c.ldx % (16 / c.g->eb) == 0 && aligned(c.X, 16) && (c.g->K + 128) * c.ldx * c.g->eb < (1ll << 31) &&
              c.g->values_bytes() + 1024 < (1ull << 31) && c.g->meta_bytes() + 1024 < (1ull << 31) &&
              (c.g->R + 256) * c.ldy * 4 < (1ll << 31) &&
@@ -173,9 +179,9 @@ Variant choose(const Call& c) {
 }
 
 Call make_call(const Geometry& g, int wdt, int ydt, int64_t T, int64_t ldx, int64_t ldy, const void* X,
-               const void* Y) {
+               const void* Y, int act = NM_ACT_NONE) {
   Call c;
-  c.g = &g; c.wdt = wdt; c.ydt = ydt; c.T = T; c.ldx = ldx; c.ldy = ldy; c.X = X; c.Y = Y;
+  c.g = &g; c.wdt = wdt; c.ydt = ydt; c.T = T; c.ldx = ldx; c.ldy = ldy; c.X = X; c.Y = Y; c.act = act;
   return c;
 }
 
@@ -299,20 +305,23 @@ nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype,
   return NM_OK;
 }
 
-nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
-                  int32_t y_dtype, const void* bias, const float* scale, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+nm_status nm_spmm_act(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
+                      int32_t y_dtype, const void* bias, const float* scale, int32_t act, float out_scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   Geometry g;
   nm_status st = check_desc(w, &g);
   if (st != NM_OK) return st;
   if (w->format_version != NM_FORMAT_VERSION) return NM_EINVAL;
   if (!X || !Y || T < 1 || ldx < T || ldy < T) return NM_EINVAL;
   if (!pair_supported(w->dtype, y_dtype)) return NM_EUNSUPPORTED;
+  if (act != NM_ACT_NONE && act != NM_ACT_GELU) return NM_EUNSUPPORTED;
+  if (act != NM_ACT_NONE && y_dtype == NM_I32) return NM_EUNSUPPORTED;
+  if (!(out_scale - out_scale == 0.0f)) return NM_EINVAL;   // not finite
   if (y_dtype == NM_I8 && !scale) return NM_EINVAL;
   if (!aligned(X, (size_t)g.eb) || !aligned(Y, (size_t)nm::dtype_bytes(y_dtype))) return NM_EUNSUPPORTED;
   if (bias && !aligned(bias, 4)) return NM_EUNSUPPORTED;
   if (scale && !aligned(scale, 4)) return NM_EUNSUPPORTED;
-  const Call call = make_call(g, w->dtype, y_dtype, T, ldx, ldy, X, Y);
+  const Call call = make_call(g, w->dtype, y_dtype, T, ldx, ldy, X, Y, act);
   Variant v = choose(call);
   const int S = ksplit_for(v, call);
   size_t need = workspace_for(v, call);
@@ -337,6 +346,8 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
   a.ksplit = 1;
   a.kbs = (int)g.nKB;
   a.ys = 0;
+  a.act = act;
+  a.out_scale = out_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (S > 1) {
@@ -348,6 +359,7 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
     p.ldy = T;
     p.bias = nullptr;
     p.scale = nullptr;
+    p.act = NM_ACT_NONE;
     p.ksplit = S;
     p.kbs = (int)(g.nKB / S);
     p.ys = g.R * T;
@@ -374,6 +386,13 @@ nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, voi
   return e == hipSuccess ? NM_OK : NM_EHIP;
 }
 
+nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
+                  int32_t y_dtype, const void* bias, const float* scale, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return nm_spmm_act(w, X, ldx, T, Y, ldy, y_dtype, bias, scale, NM_ACT_NONE, 1.0f, workspace, workspace_bytes,
+                     stream);
+}
+
 const char* nm_status_str(nm_status s) {
   switch (s) {
     case NM_OK: return "NM_OK: success";
@@ -384,19 +403,25 @@ const char* nm_status_str(nm_status s) {
   }
 }
 
-const char* nm_spmm_variant(const nm_packed* w, int64_t T, int32_t y_dtype) {
+const char* nm_spmm_variant_act(const nm_packed* w, int64_t T, int32_t y_dtype, int32_t act) {
   Geometry g;
   if (check_desc(w, &g) != NM_OK || T < 1 || !pair_supported(w->dtype, y_dtype)) return "invalid";
+  if ((act != NM_ACT_NONE && act != NM_ACT_GELU) || (act != NM_ACT_NONE && y_dtype == NM_I32)) return "invalid";
   // dense row-major operands, 256-byte aligned (what a fresh allocation gives)
   const void* al = reinterpret_cast<const void*>((uintptr_t)256);
-  return variant_name(choose(make_call(g, w->dtype, y_dtype, T, T, T, al, al)));
+  return variant_name(choose(make_call(g, w->dtype, y_dtype, T, T, T, al, al, act)));
 }
 
-int32_t nm_spmm_ksplit(const nm_packed* w, int64_t T, int32_t y_dtype) {
+const char* nm_spmm_variant(const nm_packed* w, int64_t T, int32_t y_dtype) {
+  return nm_spmm_variant_act(w, T, y_dtype, NM_ACT_NONE);
+}
+
+int32_t nm_spmm_ksplit(const nm_packed* w, int64_t T, int32_t y_dtype, int32_t act) {
   Geometry g;
   if (check_desc(w, &g) != NM_OK || T < 1 || !pair_supported(w->dtype, y_dtype)) return 0;
+  if ((act != NM_ACT_NONE && act != NM_ACT_GELU) || (act != NM_ACT_NONE && y_dtype == NM_I32)) return 0;
   const void* al = reinterpret_cast<const void*>((uintptr_t)256);
-  const Call c = make_call(g, w->dtype, y_dtype, T, T, T, al, al);
+  const Call c = make_call(g, w->dtype, y_dtype, T, T, T, al, al, act);
   return ksplit_for(choose(c), c);
 }
 

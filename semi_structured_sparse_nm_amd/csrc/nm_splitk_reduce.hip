@@ -45,7 +45,10 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(SpmmArgs a, int64_t 
         const float sc = a.scale[r];
         uint32_t packed = 0;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) packed |= (uint32_t)(requant_i8(s[v], sc) & 0xFF) << (8 * v);
+        for (int v = 0; v < 4; ++v) {
+          const int q = a.act ? requant_act_i8<true>(s[v], sc, a.out_scale) : requant_i8(s[v], sc);
+          packed |= (uint32_t)(q & 0xFF) << (8 * v);
+        }
         int8_t* y = static_cast<int8_t*>(a.Y) + o;
         if constexpr (VEC) {
           *reinterpret_cast<uint32_t*>(y) = packed;
@@ -56,6 +59,10 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(SpmmArgs a, int64_t 
       }
     } else {
       if (a.bias) s += static_cast<const float*>(a.bias)[r];
+      if (a.act) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s[v] = gelu_f32(s[v]);
+      }
       if constexpr (OUT == NM_F32) {
         float* y = static_cast<float*>(a.Y) + o;
         if constexpr (VEC) {

@@ -351,7 +351,9 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   // holds wave row 16 rb + 4 g + v; a lane's 8 rows of one token are one
   // chunk (8 bytes int8, 16 bytes 16-bit) at chunk position g ^ f(t).
   uint8_t* const os = ostage + ((OUT == NM_I8 || OUT16) ? wave * 2048 : 0);
-  auto epilogue_i8 = [&](int k, int r0, int t0) __attribute__((always_inline)) {
+  auto epilogue_i8 = [&](int k, int r0, int t0, auto actc) __attribute__((always_inline)) {
+    constexpr bool ACT = decltype(actc)::value != 0;
+    const float osc = a.out_scale;
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)(g.R * a.ldy), 0x00020000);
     const int oob = (int)(g.R * a.ldy);
     // token t (0..63 of the half) is a 32-byte row, f(t) = ((t >> 4) & 1) << 1;
@@ -374,7 +376,7 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
           uint32_t bb[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            float f = __fmul_rn((float)acc[rb][tt][v], sv[v]);
+            float f = i8_pre<ACT>(acc[rb][tt][v], sv[v], osc);
             f = __builtin_amdgcn_fmed3f(f, -128.0f, 127.0f);
             bb[v] = __builtin_bit_cast(uint32_t, f + 12582912.0f);
           }
@@ -396,7 +398,8 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
       }
     }
   };
-  auto epilogue_h = [&](int r0, int t0) __attribute__((always_inline)) {
+  auto epilogue_h = [&](int r0, int t0, auto actc) __attribute__((always_inline)) {
+    constexpr bool ACT = decltype(actc)::value != 0;
     const __amdgpu_buffer_rsrc_t ry =
         __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)(g.R * a.ldy * 2), 0x00020000);
     const int oob = (int)(g.R * a.ldy * 2);
@@ -414,10 +417,10 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
         const int tt = 2 * u4 + w;
-        const uint32_t d0 = pack2<OUT>(acc[0][tt][0], acc[0][tt][1]);
-        const uint32_t d1 = pack2<OUT>(acc[0][tt][2], acc[0][tt][3]);
-        const uint32_t d2 = pack2<OUT>(acc[1][tt][0], acc[1][tt][1]);
-        const uint32_t d3 = pack2<OUT>(acc[1][tt][2], acc[1][tt][3]);
+        const uint32_t d0 = pack2<OUT>(fp_act<ACT>(acc[0][tt][0]), fp_act<ACT>(acc[0][tt][1]));
+        const uint32_t d1 = pack2<OUT>(fp_act<ACT>(acc[0][tt][2]), fp_act<ACT>(acc[0][tt][3]));
+        const uint32_t d2 = pack2<OUT>(fp_act<ACT>(acc[1][tt][0]), fp_act<ACT>(acc[1][tt][1]));
+        const uint32_t d3 = pack2<OUT>(fp_act<ACT>(acc[1][tt][2]), fp_act<ACT>(acc[1][tt][3]));
         *reinterpret_cast<v4i*>(os + wb + 1024 * w) = v4i{(int)d0, (int)d1, (int)d2, (int)d3};
       }
       const int tok = t0 + 32 * u4 + 8 * lg;
@@ -434,7 +437,8 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     }
   };
   // int32 / fp32 output, or slice ks's partial sums under a K split
-  auto store_direct = [&](int r0, int t0, int ks) __attribute__((always_inline)) {
+  auto store_direct = [&](int r0, int t0, int ks, auto actc) __attribute__((always_inline)) {
+    constexpr bool ACT = decltype(actc)::value != 0 && !I8;
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<int32_t*>(a.Y) + ks * a.ys, 0, (int)(g.R * a.ldy * 4), 0x00020000);
     const int rw = r0 + 32 * wave + 4 * lg;
@@ -446,7 +450,12 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         const int t = t0 + 16 * tt + li;
         // whole-vector cast (a bit cast of one element of a vector lvalue
         // reads element 0)
-        const v4i ai4 = __builtin_bit_cast(v4i, acc[rb][tt]);
+        Acc x = acc[rb][tt];
+        if constexpr (ACT) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) x[v] = gelu_f32(x[v]);
+        }
+        const v4i ai4 = __builtin_bit_cast(v4i, x);
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           __builtin_amdgcn_raw_buffer_store_b32(ai4[v], ry,
@@ -480,12 +489,22 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     ++n;
     if (++ckb < kbs) return;
     ckb = 0;
-    if constexpr (OUT == NM_I8)
-      epilogue_i8(ck, cr0, ct0);
-    else if constexpr (OUT16)
-      epilogue_h(cr0, ct0);
-    else
-      store_direct(cr0, ct0, cks);
+    if constexpr (OUT == NM_I8) {
+      if (a.act)
+        epilogue_i8(ck, cr0, ct0, ic<1>());
+      else
+        epilogue_i8(ck, cr0, ct0, ic<0>());
+    } else if constexpr (OUT16) {
+      if (a.act)
+        epilogue_h(cr0, ct0, ic<1>());
+      else
+        epilogue_h(cr0, ct0, ic<0>());
+    } else {
+      if (a.act)
+        store_direct(cr0, ct0, cks, ic<1>());
+      else
+        store_direct(cr0, ct0, cks, ic<0>());
+    }
     ++ck;
     if (ck < nmine) {
       tile_of(ck, cr0, ct0, cks);

@@ -215,7 +215,8 @@ __global__ void __launch_bounds__(NWD * 64) expand_decode_kernel(SpmmArgs a) {
         for (int w = 0; w < NWD; ++w) y += red[w * 64 + ln][v];
         if (a.bias) y += static_cast<const int*>(a.bias)[r];
         if constexpr (OUT == NM_I8)
-          static_cast<int8_t*>(a.Y)[o] = (int8_t)requant_i8(y, a.scale[r]);
+          static_cast<int8_t*>(a.Y)[o] = (int8_t)(a.act ? requant_act_i8<true>(y, a.scale[r], a.out_scale)
+                                                        : requant_i8(y, a.scale[r]));
         else
           static_cast<int*>(a.Y)[o] = y;
       } else {
@@ -223,6 +224,7 @@ __global__ void __launch_bounds__(NWD * 64) expand_decode_kernel(SpmmArgs a) {
 #pragma unroll
         for (int w = 0; w < NWD; ++w) y += red[w * 64 + ln][v];
         if (a.bias) y += static_cast<const float*>(a.bias)[r];
+        if (a.act) y = gelu_f32(y);
         if constexpr (OUT == NM_F32)
           static_cast<float*>(a.Y)[o] = y;
         else if constexpr (OUT == NM_F16)

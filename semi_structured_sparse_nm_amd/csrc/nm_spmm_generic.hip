@@ -194,10 +194,12 @@ __global__ void __launch_bounds__(256) spmm_generic_kernel(SpmmArgs a) {
         if (a.ydt == NM_I32)
           static_cast<int32_t*>(a.Y)[o] = x;
         else
-          static_cast<int8_t*>(a.Y)[o] = (int8_t)requant_i8(x, a.scale[r]);
+          static_cast<int8_t*>(a.Y)[o] = (int8_t)(a.act ? requant_act_i8<true>(x, a.scale[r], a.out_scale)
+                                                        : requant_i8(x, a.scale[r]));
       } else {
         float x = acc[n][v];
         if (a.bias) x += static_cast<const float*>(a.bias)[r];
+        if (a.act) x = gelu_f32(x);
         if (a.ydt == NM_F32)
           static_cast<float*>(a.Y)[o] = x;
         else if (a.ydt == NM_F16)

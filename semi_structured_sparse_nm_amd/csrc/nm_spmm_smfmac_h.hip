@@ -111,7 +111,10 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{lo, hi}), v2bf));
 }
 
-template <int NW, int WT, int OUT>
+// ACT: the fused activation, a template parameter so that the plain
+// epilogue's kernel is unchanged by it (as a runtime branch its registers
+// made the main loop spill)
+template <int NW, int WT, int OUT, bool ACT = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -301,7 +304,8 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   // Staging: token t (0..31) is a 128-byte row of 64 positions (2 bytes);
   // position 16 g + 4 rb + v holds row 16 rb + 4 g + v of the wave; 16-byte
   // chunk c of token t is stored at c ^ f(t).
-  auto epilogue_h = [&](int r0, int t0) __attribute__((always_inline)) {
+  auto epilogue_h = [&](int r0, int t0, auto actc) __attribute__((always_inline)) {
+    constexpr bool EACT = decltype(actc)::value != 0;
     const __amdgpu_buffer_rsrc_t ry =
         __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)(g.R * a.ldy * 2), 0x00020000);
     const int oob = (int)(g.R * a.ldy * 2);
@@ -327,8 +331,8 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         uint32_t d[8];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          d[2 * rb] = pack2<OUT>(acc[rb][tt][0], acc[rb][tt][1]);
-          d[2 * rb + 1] = pack2<OUT>(acc[rb][tt][2], acc[rb][tt][3]);
+          d[2 * rb] = pack2<OUT>(fp_act<EACT>(acc[rb][tt][0]), fp_act<EACT>(acc[rb][tt][1]));
+          d[2 * rb + 1] = pack2<OUT>(fp_act<EACT>(acc[rb][tt][2]), fp_act<EACT>(acc[rb][tt][3]));
         }
         *reinterpret_cast<v4i*>(os + wbase + 2048 * w) = v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
         *reinterpret_cast<v4i*>(os + wbase + 2048 * w + 16) = v4i{(int)d[4], (int)d[5], (int)d[6], (int)d[7]};
@@ -347,7 +351,8 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     }
   };
   // fp32 output, or slice ks's partial sums under a K split
-  auto store_f32 = [&](int r0, int t0, int ks) __attribute__((always_inline)) {
+  auto store_f32 = [&](int r0, int t0, int ks, auto actc) __attribute__((always_inline)) {
+    constexpr bool EACT = decltype(actc)::value != 0;
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<float*>(a.Y) + ks * a.ys, 0, (int)(g.R * a.ldy * 4), 0x00020000);
     const int rw = r0 + 64 * wave + 4 * lg;
@@ -359,7 +364,9 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         const int t = t0 + 16 * tt + li;
         // whole-vector cast: a bit cast of one element of a vector lvalue
         // reads element 0 (observed miscompile)
-        const v4i ai4 = __builtin_bit_cast(v4i, acc[rb][tt]);
+        const v4f x = acc[rb][tt];
+        const v4i ai4 = __builtin_bit_cast(v4i, v4f{fp_act<EACT>(x[0]), fp_act<EACT>(x[1]), fp_act<EACT>(x[2]),
+                                                    fp_act<EACT>(x[3])});
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           __builtin_amdgcn_raw_buffer_store_b32(
@@ -396,9 +403,9 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     if (++ckb < kbs) return;
     ckb = 0;
     if constexpr (OUT16)
-      epilogue_h(cr0, ct0);
+      epilogue_h(cr0, ct0, ic<ACT ? 1 : 0>());
     else
-      store_f32(cr0, ct0, cks);
+      store_f32(cr0, ct0, cks, ic<ACT ? 1 : 0>());
     ++ck;
     if (ck < nmine) {
       tile_of(ck, cr0, ct0, cks);
@@ -449,12 +456,23 @@ hipError_t launch_nw(const SpmmArgs& a, hipStream_t s) {
   if (nwg_xcd > per_xcd) nwg_xcd = per_xcd;
   if (nwg_xcd < 1) nwg_xcd = 1;
   const int grid = 8 * nwg_xcd;
-  if (a.ydt == NM_F32)
+  if (a.act) {
+    if (a.ydt == NM_F32)
+      hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_F32, true>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles,
+                         nwg_xcd);
+    else if (WT == NM_F16)
+      hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_F16, true>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles,
+                         nwg_xcd);
+    else
+      hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_BF16, true>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles,
+                         nwg_xcd);
+  } else if (a.ydt == NM_F32) {
     hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_F32>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles, nwg_xcd);
-  else if (WT == NM_F16)
+  } else if (WT == NM_F16) {
     hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_F16>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles, nwg_xcd);
-  else
+  } else {
     hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_BF16>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles, nwg_xcd);
+  }
   return hipGetLastError();
 }
 

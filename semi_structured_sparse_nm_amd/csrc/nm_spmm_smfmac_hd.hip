@@ -165,6 +165,7 @@ __global__ void __launch_bounds__(NWD * 64) smfmac_hd_kernel(SpmmArgs a) {
     const int64_t r = (int64_t)rb * 16 + row;
     if (r < g.R && tok < a.T) {
       if (a.bias) y += static_cast<const float*>(a.bias)[r];
+      if (a.act) y = gelu_f32(y);
       const int64_t o = r * a.ldy + tok;
       if constexpr (OUT == NM_F32)
         static_cast<float*>(a.Y)[o] = y;

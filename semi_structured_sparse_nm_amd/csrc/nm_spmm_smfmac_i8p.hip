@@ -103,7 +103,9 @@ constexpr int TN = 8;              // token tiles (16 tokens) per wave
 constexpr int BN = TN * 16;        // 128 tokens per tile
 constexpr int STAGE = 128 * BN;    // bytes per X stage (16 KB)
 
-template <int NW, bool OUT_I8>
+// ACT: the fused activation, a template parameter so that the plain
+// epilogue's kernel is unchanged by it
+template <int NW, bool OUT_I8, bool ACT = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   // device pass only (device-only types and builtins)
@@ -317,6 +319,7 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   // f(t) = bit 2 of t | (bit 4 of t) << 1.
   uint8_t* const os = ostage + (OUT_I8 ? wave * 4096 : 0);
   auto epilogue_i8 = [&](int k, int r0, int t0) __attribute__((always_inline)) {
+    const float osc = a.out_scale;
     // writes: token 16 u + li (u = 0..3), chunk lg
     int wb[2];
   #pragma unroll
@@ -347,7 +350,7 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
           uint32_t b[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            float f = __fmul_rn((float)acc[rb][tt][v], sv[v]);
+            float f = i8_pre<ACT>(acc[rb][tt][v], sv[v], osc);
             f = __builtin_amdgcn_fmed3f(f, -128.0f, 127.0f);
             b[v] = __builtin_bit_cast(uint32_t, f + 12582912.0f);
           }
@@ -479,7 +482,10 @@ hipError_t launch_nw(const SpmmArgs& a, hipStream_t s) {
   if (nwg_xcd > per_xcd) nwg_xcd = per_xcd;
   if (nwg_xcd < 1) nwg_xcd = 1;
   const int grid = 8 * nwg_xcd;
-  if (a.ydt == NM_I8)
+  if (a.ydt == NM_I8 && a.act)
+    hipLaunchKernelGGL((smfmac_i8p_kernel<NW, true, true>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles,
+                       nwg_xcd);
+  else if (a.ydt == NM_I8)
     hipLaunchKernelGGL((smfmac_i8p_kernel<NW, true>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles, nwg_xcd);
   else
     hipLaunchKernelGGL((smfmac_i8p_kernel<NW, false>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles, nwg_xcd);

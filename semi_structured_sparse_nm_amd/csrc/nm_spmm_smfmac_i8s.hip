@@ -272,18 +272,20 @@ smfmac_i8s_kernel(SpmmArgs a, int mtiles, int ntiles) {
   // f(t) = ((t >> 4) & 1) << 1 over 8-byte chunks; reads: lane 16 G + 2 i + h
   // reads token 16 G + 8 j + i, chunk (2 s + h) ^ 2 (G & 1); output lane l
   // then holds position 16 s + l, tokens 16 G + 8 j .. + 7.
-  auto requant4 = [&](int rb, int tt) {
+  auto requant4 = [&](int rb, int tt, auto actc) {
+    constexpr bool ACT = decltype(actc)::value != 0;
+    const float osc = a.out_scale;
     const v4f sv = scale_vec(rb);
     uint32_t bb[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float f = __fmul_rn((float)acc[rb][tt][v], sv[v]);
+      float f = i8_pre<ACT>(acc[rb][tt][v], sv[v], osc);
       f = __builtin_amdgcn_fmed3f(f, -128.0f, 127.0f);
       bb[v] = __builtin_bit_cast(uint32_t, f + 12582912.0f);
     }
     return (int)(__builtin_amdgcn_perm(bb[1], bb[0], 0x0c0c0400u) | __builtin_amdgcn_perm(bb[3], bb[2], 0x04000c0cu));
   };
-  auto epilogue_i8 = [&](int r0, int t0) __attribute__((always_inline)) {
+  auto epilogue_i8 = [&](int r0, int t0, auto actc) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)(g.R * a.ldy), 0x00020000);
     const int oob = (int)(g.R * a.ldy);
     const int rw0 = r0 + 16 * RB * wr, tw0 = t0 + 16 * TN * wt;
@@ -296,7 +298,7 @@ smfmac_i8s_kernel(SpmmArgs a, int mtiles, int ntiles) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int tt = 4 * h + u;
-        *reinterpret_cast<v2i*>(os + ((512 * u + wb) ^ (16 * (u & 1)))) = v2i{requant4(0, tt), requant4(1, tt)};
+        *reinterpret_cast<v2i*>(os + ((512 * u + wb) ^ (16 * (u & 1)))) = v2i{requant4(0, tt, actc), requant4(1, tt, actc)};
       }
       // every lane stores; pieces past T go past the buffer's end (dropped)
       const int tok = tw0 + 64 * h + 16 * lg;
@@ -344,10 +346,14 @@ smfmac_i8s_kernel(SpmmArgs a, int mtiles, int ntiles) {
 
   for (int k = 0; k < nmine; ++k) {
     steps_from(steps_from, ic<0>());
-    if constexpr (OUT_I8)
-      epilogue_i8(crb * BM, ct0);
-    else
+    if constexpr (OUT_I8) {
+      if (a.act)
+        epilogue_i8(crb * BM, ct0, ic<1>());
+      else
+        epilogue_i8(crb * BM, ct0, ic<0>());
+    } else {
       store_i32(crb * BM, ct0);
+    }
     if (k + 1 < nmine) {
       const int prb = crb;
       tile_of(k + 1, crb, ct0);

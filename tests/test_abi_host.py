@@ -148,8 +148,8 @@ def test_workspace_and_variant_queries():
     assert L.nm_spmm_variant(None, 100, nm.NM_I32).decode() == "invalid"
 
 
-def _ksplit(d, T, ydt):
-    return nm.lib().nm_spmm_ksplit(ctypes.byref(d), T, ydt)
+def _ksplit(d, T, ydt, act=0):
+    return nm.lib().nm_spmm_ksplit(ctypes.byref(d), T, ydt, act)
 
 
 def _ws(d, T, ydt):
@@ -196,3 +196,37 @@ def test_split_call_validates_its_workspace(monkeypatch):
     assert _spmm(d, **kw) == nm.NM_EINVAL                                      # none given
     assert _spmm(d, ws=FAKE + (4 << 24), wsb=need - 1, **kw) == nm.NM_EINVAL   # too small
     assert _spmm(d, ws=FAKE + (4 << 24) + 8, wsb=need, **kw) == nm.NM_EUNSUPPORTED  # misaligned
+
+
+def _spmm_act(d, act, out_scale=1.0, X=FAKE + (2 << 24), ldx=100, T=100, Y=FAKE + (3 << 24), ldy=100,
+              ydt=nm.NM_I8, scale=FAKE + (5 << 24)):
+    return nm.lib().nm_spmm_act(ctypes.byref(d), X, ldx, T, Y, ldy, ydt, None, scale, act, out_scale,
+                                None, 0, None)
+
+
+def test_activation_validation_and_variant_choice():
+    """nm_spmm_act rejects unknown activations, an activation on raw int32
+    accumulators and a non-finite output scale before any launch; the
+    activation leaves the kernel choice as it is (every default kernel
+    carries it)."""
+    d = _desc()
+    assert _spmm_act(d, 2) == nm.NM_EUNSUPPORTED
+    assert _spmm_act(d, -1) == nm.NM_EUNSUPPORTED
+    assert _spmm_act(d, 1, ydt=nm.NM_I32) == nm.NM_EUNSUPPORTED
+    assert _spmm_act(d, 1, out_scale=float("inf")) == nm.NM_EINVAL
+    assert _spmm_act(d, 1, out_scale=float("nan")) == nm.NM_EINVAL
+    assert _spmm_act(d, 1, ydt=nm.NM_I8, scale=None) == nm.NM_EINVAL
+    L = nm.lib()
+    va = lambda d, T, y, a: L.nm_spmm_variant_act(ctypes.byref(d), T, y, a).decode()
+    fc1 = _desc(R=3072, K=768)
+    assert va(fc1, 12608, nm.NM_I8, 0) == "smfmac_i8_2of4_persistent"
+    assert va(fc1, 12608, nm.NM_I8, 1) == "smfmac_i8_2of4_persistent"
+    assert va(_desc(R=2304, K=768), 12608, nm.NM_I8, 1) == "smfmac_i8_2of4_stationary"
+    deep = _desc(R=3072, K=3072, N=1, M=4)
+    assert va(deep, 12608, nm.NM_I8, 1) == "expand_mfma_persistent"
+    assert va(fc1, 12608, nm.NM_I32, 1) == "invalid"
+    assert va(fc1, 12608, nm.NM_I8, 7) == "invalid"
+    assert L.nm_spmm_variant(ctypes.byref(fc1), 12608, nm.NM_I8).decode() == va(fc1, 12608, nm.NM_I8, 0)
+    f16 = _desc(R=3072, K=768, dt=nm.NM_F16)
+    assert va(f16, 1568, nm.NM_F16, 1) == "smfmac_h_2of4_persistent"
+    assert va(f16, 16, nm.NM_F16, 1) == "smfmac_h_2of4_decode"

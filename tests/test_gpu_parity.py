@@ -400,3 +400,160 @@ def test_ksplit_expand(force_variant, force_ksplit, dt, out, N, M, R, K, T, S):
         S = 2 if nkb % 2 == 0 else 1
     _ksplit_case(force_variant, force_ksplit, "expand_mfma_persistent", dt, out, N, M, R, K, T, S,
                  16 if out in ("i8", "f16", "bf16") else 3, 22)
+
+
+# ---------------------------------------------------------------- fused GELU
+# int8: the dequantising scale maps the layer's int8 output range onto about
+# [-4, 4] (so the activation's curved part is exercised), out_scale maps it back
+GELU_SPAN = 4.0
+
+
+def _gelu_case(force_variant, variant, dt, out, N, M, R, K, T, seed, S=None, force_ksplit=None):
+    import semi_structured_sparse_nm_amd as nm
+    from tests._parity import TORCH_DT, compare_i8_open, dev
+    force_variant(variant)
+    if S is not None:
+        force_ksplit(S)
+    W, X, b, s = _inputs(dt, out, R, K, T, N, M, seed, f"gelu-{variant}-{dt}-{out}-{N}-{M}-{R}-{K}-{T}")
+    p = nm.pack(dev(W, dt), N, M)
+    # nm_spmm_variant assumes dense rows (ldx = T); the run pads X rows to a
+    # multiple of 16 elements, which the forced kernels need
+    if T % 16 == 0:
+        assert nm.variant(p, T, TORCH_DT[out], act="gelu") == variant
+    if S is not None:
+        assert nm.ksplit(p, T, TORCH_DT[out], act="gelu") == S
+    narrow = out in ("i8", "f16", "bf16")
+    pad = dict(ldx_pad=(-T) % 16 + 16, ldy_pad=16 if narrow else 3, sentinel=5)
+    if dt == "i8":
+        sd = (np.asarray(s, np.float32) * np.float32(GELU_SPAN / 127.0)).astype(np.float32)
+        osc = 127.0 / GELU_SPAN
+        Y, _ = run(W, X, N, M, dt, out, bias=b, scale=sd, act="gelu", out_scale=osc, **pad)
+        ref, near = reference(W, X, N, M, dt, out, bias=b, scale=sd, act="gelu", out_scale=osc)
+        compare_i8_open(Y[:, :T], ref, near, f"{variant} gelu")
+    else:
+        Y, _ = run(W, X, N, M, dt, out, bias=b, act="gelu", **pad)
+        compare(Y[:, :T], reference(W, X, N, M, dt, out, bias=b, act="gelu"), out, f"{variant} gelu")
+    want = 5 if out != "bf16" else oracle.round_to(np.array([5.0]), "bf16")[0]
+    assert np.all(Y[:, T:] == want), "writes beyond T"
+
+
+GELU_FP = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")]
+GELU_SHAPES = [(300, 192, 144), (259, 1280, 272)]
+
+
+@pytest.mark.parametrize("R,K,T", [(300, 192, 144), (259, 1024, 272), (520, 768, 400)])
+def test_gelu_i8_stationary(force_variant, R, K, T):
+    """int8 2:4 weight-stationary kernel (K <= 1024) with GELU fused between
+    the dequantising and the requantising scale."""
+    _gelu_case(force_variant, "smfmac_i8_2of4_stationary", "i8", "i8", 2, 4, R, K, T, 31)
+
+
+@pytest.mark.parametrize("dt,out", [("i8", "i8")] + GELU_FP)
+@pytest.mark.parametrize("N,M", [(2, 4), (1, 4), (4, 8)])
+@pytest.mark.parametrize("R,K,T", GELU_SHAPES)
+def test_gelu_expand(force_variant, dt, out, N, M, R, K, T):
+    """Dense-expand tile kernel with GELU fused; 2:4 included (with an
+    activation it carries the int8 2:4 shapes the stationary kernel cannot)."""
+    _gelu_case(force_variant, "expand_mfma_persistent", dt, out, N, M, R, K, T, 32)
+
+
+@pytest.mark.parametrize("dt,out", GELU_FP)
+@pytest.mark.parametrize("R,K,T", GELU_SHAPES)
+def test_gelu_h(force_variant, dt, out, R, K, T):
+    _gelu_case(force_variant, "smfmac_h_2of4_persistent", dt, out, 2, 4, R, K, T, 33)
+
+
+@pytest.mark.parametrize("dt,out", [("i8", "i8")] + GELU_FP)
+@pytest.mark.parametrize("N,M", [(2, 4), (4, 8)])
+@pytest.mark.parametrize("R,K,T", [(40, 512, 8), (33, 1280, 16)])
+def test_gelu_decode(force_variant, dt, out, N, M, R, K, T):
+    variant = "smfmac_h_2of4_decode" if (dt != "i8" and (N, M) == (2, 4)) else "expand_mfma_decode"
+    _gelu_case(force_variant, variant, dt, out, N, M, R, K, T, 34)
+
+
+@pytest.mark.parametrize("dt,out", [("i8", "i8"), ("f16", "f16"), ("bf16", "f32")])
+@pytest.mark.parametrize("R,K,T", [(70, 192, 197), (17, 64, 5)])
+def test_gelu_generic(force_variant, dt, out, R, K, T):
+    _gelu_case(force_variant, "generic_dense_expand", dt, out, 2, 4, R, K, T, 35)
+
+
+@pytest.mark.parametrize("variant,dt,out", [("expand_mfma_persistent", "i8", "i8"),
+                                            ("expand_mfma_persistent", "f16", "f16"),
+                                            ("smfmac_h_2of4_persistent", "bf16", "bf16"),
+                                            ("smfmac_h_2of4_persistent", "f16", "f32")])
+def test_gelu_ksplit(force_variant, force_ksplit, variant, dt, out):
+    """K split with GELU: the slices' partials are raw; the reduction applies
+    bias, the activation and the output rounding or requantisation."""
+    _gelu_case(force_variant, variant, dt, out, 2, 4, 300, 1536, 400, 36, S=4, force_ksplit=force_ksplit)
+
+
+@pytest.mark.parametrize("R1,K1,T", [(3072, 768, 400), (520, 192, 144)])
+def test_mlp_chain_fc1_gelu_fc2_int8(R1, K1, T):
+    """ViT-B MLP in int8 without leaving the device: FC1 (2:4) with GELU
+    fused requantises to int8, and its [R1][T] output is FC2's [K][T]
+    activation as it stands.  FC1 against the oracle (closed decisions
+    exact, open ones within a code); FC2 against the oracle chain, exact in
+    every token column where both FC1 results agree, and elsewhere within the
+    bound a one-code change of its inputs allows."""
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    from tests._parity import compare_i8_open
+    c = nm_inputs.mlp_chain(R1, K1, T, 2, 4, 0, f"chain-{R1}-{K1}-{T}")
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    p1, p2 = nm.pack(d(c.W1), 2, 4), nm.pack(d(c.W2), 2, 4)
+    h = nm.spmm(p1, d(c.X), bias=d(c.b1), scale=d(c.s_deq1), out_dtype=torch.int8, act="gelu",
+                out_scale=c.os1)
+    y = nm.spmm(p2, h, bias=d(c.b2), scale=d(c.scale2), out_dtype=torch.int8)
+    torch.cuda.synchronize()
+    h_gpu, y_gpu = h.cpu().numpy(), y.cpu().numpy()
+    h_ref, near = oracle.reference(c.W1, c.X, 2, 4, "i8", "i8", bias=c.b1, scale=c.s_deq1, act="gelu",
+                                   out_scale=c.os1)
+    ndiff = compare_i8_open(h_gpu, h_ref, near, "fc1 gelu")
+    y_ref = oracle.reference(c.W2, h_ref, 2, 4, "i8", "i8", bias=c.b2, scale=c.scale2)
+    cols = (h_gpu != h_ref).any(axis=0)
+    assert ndiff == int((h_gpu != h_ref).sum())
+    assert np.array_equal(y_gpu[:, ~cols], y_ref[:, ~cols])
+    if cols.any():
+        vals, idx = oracle.compress(c.W2, 2, 4, "i8")
+        wm = np.abs(oracle.decompress(vals, idx, c.W2.shape[0], c.W2.shape[1], 2, 4, "i8").astype(np.int64))
+        dh = np.abs(h_gpu[:, cols].astype(np.int64) - h_ref[:, cols].astype(np.int64))
+        bound = np.ceil((wm @ dh) * c.scale2[:, None].astype(np.float64)) + 1
+        assert np.all(np.abs(y_gpu[:, cols].astype(np.int64) - y_ref[:, cols]) <= bound)
+    # the hidden activations are not degenerate (they use the int8 range)
+    assert (np.abs(h_ref.astype(np.int64)) > 10).mean() > 0.05
+
+
+def test_mlp_chain_full_size_sampled_columns():
+    """The ViT-B MLP at batch 64 (T = 12608) in the launch configuration the
+    chain benchmark times; token columns are independent, so the oracle chain
+    on 48 sampled columns (the first, the last, the rest seeded) checks them
+    exactly, under the same rule as the small chain test."""
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    from tests._parity import compare_i8_open
+    T = nm_inputs.VIT_B_TOKENS
+    c = nm_inputs.mlp_chain(3072, 768, T, 2, 4, 0, "vitb_mlp")
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    p1, p2 = nm.pack(d(c.W1), 2, 4), nm.pack(d(c.W2), 2, 4)
+    h = nm.spmm(p1, d(c.X), bias=d(c.b1), scale=d(c.s_deq1), out_dtype=torch.int8, act="gelu",
+                out_scale=c.os1)
+    y = nm.spmm(p2, h, bias=d(c.b2), scale=d(c.scale2), out_dtype=torch.int8)
+    torch.cuda.synchronize()
+    cols = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(3).integers(0, T, 46)]))
+    h_gpu, y_gpu = h.cpu().numpy()[:, cols], y.cpu().numpy()[:, cols]
+    Xs = np.ascontiguousarray(c.X[:, cols])
+    h_ref, near = oracle.reference(c.W1, Xs, 2, 4, "i8", "i8", bias=c.b1, scale=c.s_deq1, act="gelu",
+                                   out_scale=c.os1)
+    compare_i8_open(h_gpu, h_ref, near, "fc1 gelu full size")
+    y_ref = oracle.reference(c.W2, h_ref, 2, 4, "i8", "i8", bias=c.b2, scale=c.scale2)
+    agree = ~(h_gpu != h_ref).any(axis=0)
+    assert agree.sum() >= len(cols) // 2
+    assert np.array_equal(y_gpu[:, agree], y_ref[:, agree])
+
+
+@pytest.mark.parametrize("variant", ["smfmac_i8_2of4_persistent", "smfmac_i8_2of4_persistent_w8"])
+@pytest.mark.parametrize("R,K,T", [(300, 192, 144), (520, 768, 400), (259, 1280, 272)])
+def test_gelu_i8_persistent(force_variant, variant, R, K, T):
+    """int8 2:4 persistent kernels (the ViT-B FC1 default) with GELU fused
+    between the dequantising and the requantising scale."""
+    _gelu_case(force_variant, variant, "i8", "i8", 2, 4, R, K, T, 37)
