@@ -53,17 +53,28 @@ def _traffic(kernel_name: str, launches_per_step: int = 1):
         rec = json.load(open(path)).get(kernel_name)
     except ValueError:
         return None
-    if not rec or rec.get("source_sha") != _source_sha():
+    if not rec or rec.get("source_sha") != _source_sha(kernel_name):
         return None
     return rec.get("bytes_per_launch")
 
 
-def _source_sha() -> str:
+# the source files a kernel variant is built from (its counters go stale
+# when one of them changes); variants not listed hash every source
+KERNEL_SOURCES = {
+    "smfmac_i8_2of4_persistent": ["semi_structured_sparse_nm_amd/csrc/nm_spmm_smfmac_i8p.hip",
+                                  "semi_structured_sparse_nm_amd/csrc/nm_common.hpp", "include/nm_sparse.h"],
+}
+
+
+def _source_sha(kernel_name: str = "") -> str:
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "semi_structured_sparse_nm_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        h.update(f.encode())
-        h.update(open(os.path.join(csrc, f), "rb").read())
+    files = KERNEL_SOURCES.get(kernel_name)
+    if files is None:
+        csrc = os.path.join("semi_structured_sparse_nm_amd", "csrc")
+        files = [os.path.join(csrc, f) for f in sorted(os.listdir(os.path.join(ROOT, csrc)))]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
 
