@@ -52,6 +52,11 @@ typedef enum { NM_I8 = 0, NM_F16 = 1, NM_BF16 = 2, NM_I32 = 3, NM_F32 = 4 } nm_d
 /* Activation fused into nm_spmm_act's epilogue. */
 typedef enum { NM_ACT_NONE = 0, NM_ACT_GELU = 1 } nm_act;
 
+/* Operand layouts: X [K][T] and Y [R][T] (tokens contiguous, as nm_spmm
+ * takes them), or the PyTorch-linear layout X [T][K] and Y [T][R] (the
+ * reduction and output dimensions contiguous), which nm_spmm_tk takes. */
+typedef enum { NM_LAYOUT_KT = 0, NM_LAYOUT_TK = 1 } nm_layout;
+
 #define NM_FORMAT_VERSION 1u
 
 /*
@@ -168,6 +173,17 @@ nm_status nm_spmm_act(const nm_packed* w, const void* X, int64_t ldx, int64_t T,
                       int32_t y_dtype, const void* bias, const float* scale, int32_t act, float out_scale,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * nm_spmm_act in the PyTorch-linear layout: Yt = epilogue(Xt . (mask (.) W)^T)
+ * with Xt [T][ldx] (row t holds token t's K activations, K contiguous) and Yt
+ * [T][ldy] (row t holds token t's R outputs), so a linear layer's input and
+ * output need no transposes.  Same arithmetic, epilogues, activations and
+ * errors as nm_spmm_act; ldx >= K and ldy >= R (NM_EINVAL otherwise).
+ */
+nm_status nm_spmm_tk(const nm_packed* w, const void* Xt, int64_t ldx, int64_t T, void* Yt, int64_t ldy,
+                     int32_t y_dtype, const void* bias, const float* scale, int32_t act, float out_scale,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* nm_status_str(nm_status s);
 
@@ -181,6 +197,9 @@ const char* nm_spmm_variant(const nm_packed* w, int64_t T, int32_t y_dtype);
 /* The same for nm_spmm_act with activation `act` (which kernels carry it
  * can change the choice). */
 const char* nm_spmm_variant_act(const nm_packed* w, int64_t T, int32_t y_dtype, int32_t act);
+
+/* The same for nm_spmm_tk (dense rows: ldx = K, ldy = R). */
+const char* nm_spmm_variant_tk(const nm_packed* w, int64_t T, int32_t y_dtype, int32_t act);
 
 /*
  * Number of K slices nm_spmm_act (nm_spmm: act = NM_ACT_NONE) would split

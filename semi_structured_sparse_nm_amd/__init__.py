@@ -74,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.nm_spmm_variant_act.restype = ctypes.c_char_p
         L.nm_spmm_act.argtypes = [PP, P, I64, I64, P, I64, I32, P, P, I32, ctypes.c_float, P, SZ, P]
         L.nm_spmm_act.restype = ctypes.c_int
+        L.nm_spmm_tk.argtypes = [PP, P, I64, I64, P, I64, I32, P, P, I32, ctypes.c_float, P, SZ, P]
+        L.nm_spmm_tk.restype = ctypes.c_int
+        L.nm_spmm_variant_tk.argtypes = [PP, I64, I32, I32]
+        L.nm_spmm_variant_tk.restype = ctypes.c_char_p
         for f in ("nm_pack_size", "nm_pack", "nm_spmm_workspace_size", "nm_spmm"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -166,6 +170,11 @@ def variant(p: Packed, T: int, out_dtype: torch.dtype, act: str = "none") -> str
     return lib().nm_spmm_variant_act(ctypes.byref(d), T, _TORCH_TO_NM[out_dtype], ACTS[act]).decode()
 
 
+def variant_tk(p: Packed, T: int, out_dtype: torch.dtype, act: str = "none") -> str:
+    d = p.desc()
+    return lib().nm_spmm_variant_tk(ctypes.byref(d), T, _TORCH_TO_NM[out_dtype], ACTS[act]).decode()
+
+
 def ksplit(p: Packed, T: int, out_dtype: torch.dtype, act: str = "none") -> int:
     """K slices (workgroup-level split of K) nm_spmm would use; 1 = none."""
     d = p.desc()
@@ -200,4 +209,34 @@ def spmm(p: Packed, X: torch.Tensor, bias: torch.Tensor | None = None,
                            None if workspace is None else workspace.data_ptr(),
                            0 if workspace is None else workspace.numel(), _stream(X.device))
     _check(st, "nm_spmm_act" if act != "none" else "nm_spmm")
+    return out
+
+
+def linear(p: Packed, Xt: torch.Tensor, bias: torch.Tensor | None = None,
+           scale: torch.Tensor | None = None, out_dtype: torch.dtype | None = None,
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+           act: str = "none", out_scale: float = 1.0) -> torch.Tensor:
+    """nm_spmm_tk, the PyTorch-linear layout: Yt[T, R] = epilogue(Xt @ (mask . W)^T)
+    with Xt [T, K] (K contiguous), as torch.nn.functional.linear takes it."""
+    if Xt.dim() != 2 or Xt.stride(1) != 1:
+        raise ValueError("Xt must be a 2-D tensor with unit stride along K")
+    if Xt.shape[1] != p.K:
+        raise ValueError(f"Xt has {Xt.shape[1]} columns, the weight has K={p.K}")
+    T = Xt.shape[0]
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else default_out_dtype(p.dtype)
+    if out is None:
+        out = torch.empty((T, p.rows), dtype=out_dtype, device=Xt.device)
+    if out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (T, p.rows):
+        raise ValueError("out must be [T, R] with unit stride along R")
+    need = workspace_size(p, T, out_dtype)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=Xt.device)
+    d = p.desc()
+    st = lib().nm_spmm_tk(ctypes.byref(d), Xt.data_ptr(), Xt.stride(0), T, out.data_ptr(), out.stride(0),
+                          _TORCH_TO_NM[out_dtype], None if bias is None else bias.data_ptr(),
+                          None if scale is None else scale.data_ptr(), ACTS[act], float(out_scale),
+                          None if workspace is None else workspace.data_ptr(),
+                          0 if workspace is None else workspace.numel(), _stream(Xt.device))
+    _check(st, "nm_spmm_tk")
     return out

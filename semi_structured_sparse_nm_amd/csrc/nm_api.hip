@@ -84,12 +84,15 @@ struct Call {
   const void* X;
   const void* Y;
   int act;
+  int layout;
 };
 
 bool eligible(Variant v, const Call& c) {
   // the 256 x 128 int8 kernel and the 32 x 32-fragment dense-expand kernel
   // (tested alternatives, forced only) carry no fused activation
   if (c.act != NM_ACT_NONE && (v == V_SMFMAC_I8 || v == V_EXPAND32)) return false;
+  // the [T][K] layout: the generic kernel only
+  if (c.layout == NM_LAYOUT_TK) return v == V_GENERIC;
   switch (v) {
     case V_GENERIC: return true;
     case V_SMFMAC_I8:
@@ -179,9 +182,10 @@ Variant choose(const Call& c) {
 }
 
 Call make_call(const Geometry& g, int wdt, int ydt, int64_t T, int64_t ldx, int64_t ldy, const void* X,
-               const void* Y, int act = NM_ACT_NONE) {
+               const void* Y, int act = NM_ACT_NONE, int layout = NM_LAYOUT_KT) {
   Call c;
   c.g = &g; c.wdt = wdt; c.ydt = ydt; c.T = T; c.ldx = ldx; c.ldy = ldy; c.X = X; c.Y = Y; c.act = act;
+  c.layout = layout;
   return c;
 }
 
@@ -305,14 +309,20 @@ nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype,
   return NM_OK;
 }
 
-nm_status nm_spmm_act(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
-                      int32_t y_dtype, const void* bias, const float* scale, int32_t act, float out_scale,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+nm_status spmm_call(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
+                    int32_t y_dtype, const void* bias, const float* scale, int32_t act, float out_scale,
+                    int layout, void* workspace, size_t workspace_bytes, void* stream) {
   Geometry g;
   nm_status st = check_desc(w, &g);
   if (st != NM_OK) return st;
   if (w->format_version != NM_FORMAT_VERSION) return NM_EINVAL;
-  if (!X || !Y || T < 1 || ldx < T || ldy < T) return NM_EINVAL;
+  if (!X || !Y || T < 1) return NM_EINVAL;
+  if (layout == NM_LAYOUT_KT && (ldx < T || ldy < T)) return NM_EINVAL;
+  if (layout == NM_LAYOUT_TK && (ldx < g.K || ldy < g.R)) return NM_EINVAL;
   if (!pair_supported(w->dtype, y_dtype)) return NM_EUNSUPPORTED;
   if (act != NM_ACT_NONE && act != NM_ACT_GELU) return NM_EUNSUPPORTED;
   if (act != NM_ACT_NONE && y_dtype == NM_I32) return NM_EUNSUPPORTED;
@@ -321,7 +331,7 @@ nm_status nm_spmm_act(const nm_packed* w, const void* X, int64_t ldx, int64_t T,
   if (!aligned(X, (size_t)g.eb) || !aligned(Y, (size_t)nm::dtype_bytes(y_dtype))) return NM_EUNSUPPORTED;
   if (bias && !aligned(bias, 4)) return NM_EUNSUPPORTED;
   if (scale && !aligned(scale, 4)) return NM_EUNSUPPORTED;
-  const Call call = make_call(g, w->dtype, y_dtype, T, ldx, ldy, X, Y, act);
+  const Call call = make_call(g, w->dtype, y_dtype, T, ldx, ldy, X, Y, act, layout);
   Variant v = choose(call);
   const int S = ksplit_for(v, call);
   size_t need = workspace_for(v, call);
@@ -348,6 +358,7 @@ nm_status nm_spmm_act(const nm_packed* w, const void* X, int64_t ldx, int64_t T,
   a.ys = 0;
   a.act = act;
   a.out_scale = out_scale;
+  a.layout = layout;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (S > 1) {
@@ -386,6 +397,24 @@ nm_status nm_spmm_act(const nm_packed* w, const void* X, int64_t ldx, int64_t T,
   return e == hipSuccess ? NM_OK : NM_EHIP;
 }
 
+}  // namespace
+
+extern "C" {
+
+nm_status nm_spmm_act(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
+                      int32_t y_dtype, const void* bias, const float* scale, int32_t act, float out_scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return spmm_call(w, X, ldx, T, Y, ldy, y_dtype, bias, scale, act, out_scale, NM_LAYOUT_KT, workspace,
+                   workspace_bytes, stream);
+}
+
+nm_status nm_spmm_tk(const nm_packed* w, const void* Xt, int64_t ldx, int64_t T, void* Yt, int64_t ldy,
+                     int32_t y_dtype, const void* bias, const float* scale, int32_t act, float out_scale,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return spmm_call(w, Xt, ldx, T, Yt, ldy, y_dtype, bias, scale, act, out_scale, NM_LAYOUT_TK, workspace,
+                   workspace_bytes, stream);
+}
+
 nm_status nm_spmm(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
                   int32_t y_dtype, const void* bias, const float* scale, void* workspace,
                   size_t workspace_bytes, void* stream) {
@@ -414,6 +443,14 @@ const char* nm_spmm_variant_act(const nm_packed* w, int64_t T, int32_t y_dtype, 
 
 const char* nm_spmm_variant(const nm_packed* w, int64_t T, int32_t y_dtype) {
   return nm_spmm_variant_act(w, T, y_dtype, NM_ACT_NONE);
+}
+
+const char* nm_spmm_variant_tk(const nm_packed* w, int64_t T, int32_t y_dtype, int32_t act) {
+  Geometry g;
+  if (check_desc(w, &g) != NM_OK || T < 1 || !pair_supported(w->dtype, y_dtype)) return "invalid";
+  if ((act != NM_ACT_NONE && act != NM_ACT_GELU) || (act != NM_ACT_NONE && y_dtype == NM_I32)) return "invalid";
+  const void* al = reinterpret_cast<const void*>((uintptr_t)256);
+  return variant_name(choose(make_call(g, w->dtype, y_dtype, T, g.K, g.R, al, al, act, NM_LAYOUT_TK)));
 }
 
 int32_t nm_spmm_ksplit(const nm_packed* w, int64_t T, int32_t y_dtype, int32_t act) {

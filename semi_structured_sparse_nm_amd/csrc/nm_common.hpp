@@ -84,6 +84,9 @@ struct SpmmArgs {
   // sat(rne(act(f32(acc + bias) * scale[r]) * out_scale)).
   int act;
   float out_scale;
+  // operand layout: NM_LAYOUT_KT (X [K][ldx], Y [R][ldy]) or NM_LAYOUT_TK
+  // (X [T][ldx] with K contiguous, Y [T][ldy] with R contiguous)
+  int layout;
 };
 
 // Kernel variants; each launcher returns hipSuccess or the launch error.

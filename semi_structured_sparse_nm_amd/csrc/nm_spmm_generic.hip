@@ -55,7 +55,9 @@ __device__ __forceinline__ v4f mfma_step(const v4i& a, const v4i& b, const v4f& 
                                                  c, 0, 0, 0);
 }
 
-template <int WT, int MM>
+// TK: the PyTorch-linear layout, X [T][ldx] with K contiguous and Y [T][ldy]
+// with R contiguous; otherwise X [K][ldx] and Y [R][ldy].
+template <int WT, int MM, bool TK>
 __global__ void __launch_bounds__(256) spmm_generic_kernel(SpmmArgs a) {
   using E = Elt<WT>;
   constexpr int EB = E::EB, KB = E::KB, KS = E::KS;
@@ -84,19 +86,25 @@ __global__ void __launch_bounds__(256) spmm_generic_kernel(SpmmArgs a) {
 
   // Every load of a block is issued before the first LDS store, so a block
   // costs one memory round trip, not one per element.
-  const int xk = tid / TPR, xt = (tid % TPR) * XPT;   // this thread's X row and first token
+  // [K][T]: this thread's X row and first token (tokens contiguous);
+  // [T][K]: its token and first k (a contiguous run of XPT k)
+  constexpr int TPT = 256 / BN;            // threads per token in the [T][K] layout
+  static_assert(KB % TPT == 0 && KB / TPT == XPT, "[T][K] staging shape");
+  const int xk = TK ? (tid % TPT) * XPT : tid / TPR;
+  const int xt = TK ? tid / TPT : (tid % TPR) * XPT;
   for (int64_t kb = 0; kb < g.nKB; ++kb) {
-    // ---- X tile (zeros outside K x T), transposed into LDS
-    const int64_t kg = kb * KB + xk;
+    // ---- X tile (zeros outside K x T), token-major in LDS
     uint32_t xv[XPT];
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const int64_t tg = t0 + xt + i;
+      const int64_t kg = kb * KB + xk + (TK ? i : 0);
+      const int64_t tg = t0 + xt + (TK ? 0 : i);
       const bool ok = kg < g.K && tg < a.T;
+      const int64_t off = TK ? tg * a.ldx + kg : kg * a.ldx + tg;
       if constexpr (EB == 1)
-        xv[i] = ok ? X[kg * a.ldx + tg] : 0u;
+        xv[i] = ok ? X[off] : 0u;
       else
-        xv[i] = ok ? reinterpret_cast<const uint16_t*>(X)[kg * a.ldx + tg] : 0u;
+        xv[i] = ok ? reinterpret_cast<const uint16_t*>(X)[off] : 0u;
     }
     // ---- packed W: entry (row, group) e = tid + 256 i; its N kept values
     // and the meta bits of its positions (two dwords around them)
@@ -131,7 +139,7 @@ __global__ void __launch_bounds__(256) spmm_generic_kernel(SpmmArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      uint8_t* dst = Xt + (xt + i) * ROWB + xk * EB;
+      uint8_t* dst = TK ? Xt + xt * ROWB + (xk + i) * EB : Xt + (xt + i) * ROWB + xk * EB;
       if constexpr (EB == 1)
         *dst = (uint8_t)xv[i];
       else
@@ -187,7 +195,7 @@ __global__ void __launch_bounds__(256) spmm_generic_kernel(SpmmArgs a) {
       const int64_t r = r0 + wave * 16 + lg * 4 + v;
       const int64_t t = t0 + n * 16 + li;
       if (r >= g.R || t >= a.T) continue;
-      const int64_t o = r * a.ldy + t;
+      const int64_t o = TK ? t * a.ldy + r : r * a.ldy + t;
       if constexpr (WT == 0) {
         int x = acc[n][v];
         if (a.bias) x += static_cast<const int32_t*>(a.bias)[r];
@@ -216,12 +224,22 @@ __global__ void __launch_bounds__(256) spmm_generic_kernel(SpmmArgs a) {
 hipError_t launch_spmm_generic(const SpmmArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.T + BN - 1) / BN), (unsigned)((a.g.R + BM - 1) / BM));
   void (*k)(SpmmArgs);
-  if (a.wdt == NM_I8)
-    k = a.g.M == 4 ? spmm_generic_kernel<0, 4> : spmm_generic_kernel<0, 8>;
-  else if (a.wdt == NM_F16)
-    k = a.g.M == 4 ? spmm_generic_kernel<1, 4> : spmm_generic_kernel<1, 8>;
-  else
-    k = a.g.M == 4 ? spmm_generic_kernel<2, 4> : spmm_generic_kernel<2, 8>;
+  const bool m4 = a.g.M == 4;
+  if (a.layout == NM_LAYOUT_TK) {
+    if (a.wdt == NM_I8)
+      k = m4 ? spmm_generic_kernel<0, 4, true> : spmm_generic_kernel<0, 8, true>;
+    else if (a.wdt == NM_F16)
+      k = m4 ? spmm_generic_kernel<1, 4, true> : spmm_generic_kernel<1, 8, true>;
+    else
+      k = m4 ? spmm_generic_kernel<2, 4, true> : spmm_generic_kernel<2, 8, true>;
+  } else {
+    if (a.wdt == NM_I8)
+      k = m4 ? spmm_generic_kernel<0, 4, false> : spmm_generic_kernel<0, 8, false>;
+    else if (a.wdt == NM_F16)
+      k = m4 ? spmm_generic_kernel<1, 4, false> : spmm_generic_kernel<1, 8, false>;
+    else
+      k = m4 ? spmm_generic_kernel<2, 4, false> : spmm_generic_kernel<2, 8, false>;
+  }
   hipLaunchKernelGGL(k, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

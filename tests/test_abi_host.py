@@ -230,3 +230,21 @@ def test_activation_validation_and_variant_choice():
     f16 = _desc(R=3072, K=768, dt=nm.NM_F16)
     assert va(f16, 1568, nm.NM_F16, 1) == "smfmac_h_2of4_persistent"
     assert va(f16, 16, nm.NM_F16, 1) == "smfmac_h_2of4_decode"
+
+
+def test_tk_layout_validation():
+    """nm_spmm_tk checks its strides against K and R (not T) before any
+    launch and shares nm_spmm_act's other checks."""
+    L = nm.lib()
+    d = _desc(R=32, K=64)
+
+    def tk(ldx=64, T=100, ldy=32, ydt=nm.NM_I32, act=0, X=FAKE + (2 << 24), Y=FAKE + (3 << 24)):
+        return L.nm_spmm_tk(ctypes.byref(d), X, ldx, T, Y, ldy, ydt, None, None, act, 1.0, None, 0, None)
+
+    assert tk(ldx=63) == nm.NM_EINVAL
+    assert tk(ldy=31) == nm.NM_EINVAL
+    assert tk(T=0) == nm.NM_EINVAL
+    assert tk(X=None) == nm.NM_EINVAL
+    assert tk(act=1) == nm.NM_EUNSUPPORTED          # activation on raw int32
+    assert tk(ydt=nm.NM_I8) == nm.NM_EINVAL         # scale required
+    assert L.nm_spmm_variant_tk(ctypes.byref(d), 100, nm.NM_I32, 0).decode() == "generic_dense_expand"

@@ -557,3 +557,50 @@ def test_gelu_i8_persistent(force_variant, variant, R, K, T):
     """int8 2:4 persistent kernels (the ViT-B FC1 default) with GELU fused
     between the dequantising and the requantising scale."""
     _gelu_case(force_variant, variant, "i8", "i8", 2, 4, R, K, T, 37)
+
+
+# ---------------------------------------------------------------- [T][K] layout
+def _tk_case(dt, out, N, M, R, K, T, seed, act="none"):
+    """nm_spmm_tk on padded row strides: Yt [T][R] against the oracle's
+    [R][T] result, element by element; nothing written past R."""
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    from tests._parity import TORCH_DT, compare_i8_open, dev, host
+    W, X, b, s = _inputs(dt, out, R, K, T, N, M, seed, f"tk-{dt}-{out}-{N}-{M}-{R}-{K}-{T}-{act}")
+    p = nm.pack(dev(W, dt), N, M)
+    Xfull = torch.zeros((T, K + 24), dtype=TORCH_DT[dt], device="cuda")
+    Xfull[:, :K] = dev(np.ascontiguousarray(X.T), dt)
+    Yfull = torch.full((T, R + 16), 5, dtype=TORCH_DT[out], device="cuda")
+    kw = {}
+    sd, osc = s, 1.0
+    if dt == "i8" and act == "gelu":
+        sd = (np.asarray(s, np.float32) * np.float32(GELU_SPAN / 127.0)).astype(np.float32)
+        osc = 127.0 / GELU_SPAN
+    bias = None if b is None else torch.from_numpy(np.asarray(b)).cuda()
+    scale = None if sd is None else torch.from_numpy(np.asarray(sd, np.float32)).cuda()
+    nm.linear(p, Xfull[:, :K], bias=bias, scale=scale, out_dtype=TORCH_DT[out], out=Yfull[:, :R], act=act,
+              out_scale=osc)
+    torch.cuda.synchronize()
+    Y = host(Yfull, out)
+    Yt = np.ascontiguousarray(Y[:, :R].T)
+    if dt == "i8" and act == "gelu":
+        ref, near = reference(W, X, N, M, dt, out, bias=b, scale=sd, act=act, out_scale=osc)
+        compare_i8_open(Yt, ref, near, "tk gelu")
+    else:
+        compare(Yt, reference(W, X, N, M, dt, out, bias=b, scale=sd, act=act), out, f"tk {N}:{M}")
+    want = 5 if out != "bf16" else oracle.round_to(np.array([5.0]), "bf16")[0]
+    assert np.all(Y[:, R:] == want), "writes beyond R"
+
+
+@pytest.mark.parametrize("dt,out", PAIRS)
+@pytest.mark.parametrize("N,M", [(2, 4), (1, 4), (3, 4), (4, 8), (8, 8)])
+@pytest.mark.parametrize("R,K,T", [(17, 8, 1), (300, 200, 37), (259, 1288, 144)])
+def test_tk_layout(dt, out, N, M, R, K, T):
+    """The PyTorch-linear layout (X [T][K], Y [T][R]) for every dtype pair,
+    several N:M, ragged rows, tokens and column blocks, padded strides."""
+    _tk_case(dt, out, N, M, R, K, T, 41)
+
+
+@pytest.mark.parametrize("dt,out", [("i8", "i8"), ("f16", "f16"), ("bf16", "f32")])
+def test_tk_layout_gelu(dt, out):
+    _tk_case(dt, out, 2, 4, 300, 200, 37, 42, act="gelu")
