@@ -508,6 +508,9 @@ def main():
                          "stacks of other N:M draws")
     ap.add_argument("--search", action="store_true",
                     help="latency-constrained layer-wise N:M search over the ViT-B stack, solutions timed")
+    ap.add_argument("--layout", choices=["kt", "tk"], default="kt",
+                    help="operand layout of the default benchmark: X [K][T] (kt) or the PyTorch-linear "
+                         "X [T][K], Y [T][R] (tk)")
     ap.add_argument("--chain", action="store_true",
                     help="time the int8 ViT-B MLP: FC1 with GELU fused, chained into FC2 on the device")
     ap.add_argument("--sweep", default="",
@@ -586,16 +589,20 @@ def main():
         pv = p.values.clone()
         pm = None if p.meta is None else p.meta.clone()
         ps = nm.Packed(p.rows, p.K, p.N, p.M, p.dtype, pv, pm, p.format_version)
-        Xi = X0.clone()
-        Yi = torch.empty((L.R, L.T), dtype=odt, device=dev)
+        tk = args.layout == "tk"
+        Xi = X0.t().contiguous() if tk else X0.clone()
+        Yi = torch.empty((L.T, L.R) if tk else (L.R, L.T), dtype=odt, device=dev)
         sets.append((ps, Xi, Yi))
     need = nm.workspace_size(p, L.T, odt)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    variant = nm.variant(p, L.T, odt)
+    variant = nm.variant_tk(p, L.T, odt) if args.layout == "tk" else nm.variant(p, L.T, odt)
 
     def step(i):
         ps, Xi, Yi = sets[i % nsets]
-        nm.spmm(ps, Xi, bias=bias, scale=scale, out_dtype=odt, out=Yi, workspace=ws)
+        if args.layout == "tk":
+            nm.linear(ps, Xi, bias=bias, scale=scale, out_dtype=odt, out=Yi, workspace=ws)
+        else:
+            nm.spmm(ps, Xi, bias=bias, scale=scale, out_dtype=odt, out=Yi, workspace=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -647,7 +654,7 @@ def main():
         ps, Xi, Yi = sets[0]
         step(0)
         torch.cuda.synchronize()
-        got = Yi[torch.from_numpy(rows).to(dev)].cpu()
+        got = (Yi.t() if args.layout == "tk" else Yi)[torch.from_numpy(rows).to(dev)].cpu()
         if L.out == "bf16":
             got = got.view(torch.int16).numpy().view(np.uint16)
             got = oracle.to_f64(got, "bf16")
@@ -690,7 +697,7 @@ def main():
         "config": {"workload": L.name, "R": L.R, "K": L.K, "T": L.T, "N": L.N, "M": L.M,
                    "in": L.dt, "out": L.out,
                    "epilogue": "bias+requant" if L.out == "i8" else "none",
-                   "parallelism": "single-gpu"},
+                   "parallelism": "single-gpu", "layout": "T x K" if args.layout == "tk" else "K x T"},
         "roofline": roof, "cpu_baseline": cpu,
         "kernel": variant, "rotation_sets": nsets, "launch": "hip-graph" if graphed else "eager", "warm_ms_per_step": round(warm_ms, 5),
         "effective_GBps": round(nbytes / t_s / 1e9, 1), "pack_ms": round(pack_ms, 4),

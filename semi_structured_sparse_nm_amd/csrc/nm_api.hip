@@ -58,6 +58,7 @@ enum Variant {
   V_EXPAND_DECODE,  // any N:M, decode shapes (T <= 16): K split across 8 waves, dense MFMA
   V_SMFMAC_I8S,     // int8 2:4, K <= 1024: weights held in registers, workgroups walk token strips
   V_EXPAND32,       // as V_EXPAND with 32 x 32 dense MFMA (forced only: measured slower)
+  V_SMFMAC_I8TK,    // int8 2:4 persistent, [T][K] layout (X [T][K], Y [T][R])
   V_COUNT
 };
 
@@ -73,6 +74,7 @@ const char* variant_name(Variant v) {
     case V_EXPAND_DECODE: return "expand_mfma_decode";
     case V_SMFMAC_I8S: return "smfmac_i8_2of4_stationary";
     case V_EXPAND32: return "expand_mfma32_persistent";
+    case V_SMFMAC_I8TK: return "smfmac_i8_2of4_tk";
     default: return "invalid";
   }
 }
@@ -91,8 +93,8 @@ bool eligible(Variant v, const Call& c) {
   // the 256 x 128 int8 kernel and the 32 x 32-fragment dense-expand kernel
   // (tested alternatives, forced only) carry no fused activation
   if (c.act != NM_ACT_NONE && (v == V_SMFMAC_I8 || v == V_EXPAND32)) return false;
-  // the [T][K] layout: the generic kernel only
-  if (c.layout == NM_LAYOUT_TK) return v == V_GENERIC;
+  // the [T][K] layout has kernels of its own (and the generic one)
+  if ((c.layout == NM_LAYOUT_TK) != (v == V_SMFMAC_I8TK) && v != V_GENERIC) return false;
   switch (v) {
     case V_GENERIC: return true;
     case V_SMFMAC_I8:
@@ -154,6 +156,15 @@ bool eligible(Variant v, const Call& c) {
              aligned(c.X, 16) && (c.g->K + 128) * c.ldx * c.g->eb < (1ll << 31) &&
              c.g->values_bytes() + 2048 < (1ull << 31) && c.g->meta_bytes() + 1024 < (1ull << 31) &&
              c.g->R * c.ldy < (1ll << 40);
+    case V_SMFMAC_I8TK:
+      // int8 2:4 in the [T][K] layout; token rows in whole 16-byte pieces;
+      // 32-bit buffer offsets that do not wrap for the tokens a tile reaches
+      // past T; R a multiple of 16, so a 16-row output piece never crosses
+      // into the next token's row
+      return c.wdt == NM_I8 && c.g->N == 2 && c.g->M == 4 && c.ldx % 16 == 0 && aligned(c.X, 16) &&
+             (c.T + 128) * c.ldx < (1ll << 31) && c.g->values_bytes() < (1ull << 31) && c.g->R % 16 == 0 &&
+             (c.T + 128) * c.ldy * 4 < (1ll << 31) && aligned(c.Y, 16) &&
+             ((c.ydt == NM_I8 && c.ldy % 16 == 0) || (c.ydt == NM_I32 && c.ldy % 4 == 0));
     default: return false;
   }
 }
@@ -164,6 +175,7 @@ Variant choose(const Call& c) {
     for (int v = V_GENERIC; v < V_COUNT; ++v)
       if (strcmp(force, variant_name((Variant)v)) == 0 && eligible((Variant)v, c)) return (Variant)v;
   }
+  if (eligible(V_SMFMAC_I8TK, c)) return V_SMFMAC_I8TK;
   // decode shapes (few tokens): K split inside a workgroup per 16-row block
   if (eligible(V_SMFMAC_HD, c)) return V_SMFMAC_HD;
   if (eligible(V_EXPAND_DECODE, c)) return V_EXPAND_DECODE;
@@ -392,6 +404,7 @@ nm_status spmm_call(const nm_packed* w, const void* X, int64_t ldx, int64_t T, v
     case V_EXPAND32: e = nm::launch_spmm_expand32(a, s); break;
     case V_EXPAND_DECODE: e = nm::launch_spmm_expand_decode(a, s); break;
     case V_SMFMAC_I8S: e = nm::launch_spmm_smfmac_i8s(a, s); break;
+    case V_SMFMAC_I8TK: e = nm::launch_spmm_smfmac_i8tk(a, s); break;
     default: return NM_EINVAL;
   }
   return e == hipSuccess ? NM_OK : NM_EHIP;

@@ -95,6 +95,7 @@ hipError_t launch_pack(const void* W, int64_t ldw, const Geometry& g, int wdt, u
 hipError_t launch_spmm_generic(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8(const SpmmArgs& a, int cfg, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8p(const SpmmArgs& a, int cfg, hipStream_t s);
+hipError_t launch_spmm_smfmac_i8tk(const SpmmArgs& a, hipStream_t s);   // [T][K] layout
 hipError_t launch_spmm_smfmac_h(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_smfmac_hd(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8s(const SpmmArgs& a, hipStream_t s);

@@ -560,7 +560,7 @@ def test_gelu_i8_persistent(force_variant, variant, R, K, T):
 
 
 # ---------------------------------------------------------------- [T][K] layout
-def _tk_case(dt, out, N, M, R, K, T, seed, act="none"):
+def _tk_case(dt, out, N, M, R, K, T, seed, act="none", xpad=24, variant=None):
     """nm_spmm_tk on padded row strides: Yt [T][R] against the oracle's
     [R][T] result, element by element; nothing written past R."""
     import torch
@@ -568,7 +568,9 @@ def _tk_case(dt, out, N, M, R, K, T, seed, act="none"):
     from tests._parity import TORCH_DT, compare_i8_open, dev, host
     W, X, b, s = _inputs(dt, out, R, K, T, N, M, seed, f"tk-{dt}-{out}-{N}-{M}-{R}-{K}-{T}-{act}")
     p = nm.pack(dev(W, dt), N, M)
-    Xfull = torch.zeros((T, K + 24), dtype=TORCH_DT[dt], device="cuda")
+    if variant is not None and K % 16 == 0:
+        assert nm.variant_tk(p, T, TORCH_DT[out], act=act) == variant
+    Xfull = torch.zeros((T, K + xpad), dtype=TORCH_DT[dt], device="cuda")
     Xfull[:, :K] = dev(np.ascontiguousarray(X.T), dt)
     Yfull = torch.full((T, R + 16), 5, dtype=TORCH_DT[out], device="cuda")
     kw = {}
@@ -604,3 +606,19 @@ def test_tk_layout(dt, out, N, M, R, K, T):
 @pytest.mark.parametrize("dt,out", [("i8", "i8"), ("f16", "f16"), ("bf16", "f32")])
 def test_tk_layout_gelu(dt, out):
     _tk_case(dt, out, 2, 4, 300, 200, 37, 42, act="gelu")
+
+
+@pytest.mark.parametrize("out", ["i8", "i32"])
+@pytest.mark.parametrize("R,K,T", [(256, 192, 144), (3072, 768, 1008), (528, 1280, 272), (16, 128, 16),
+                                   (304, 200, 37)])
+def test_tk_fast_i8(force_variant, out, R, K, T):
+    """The int8 2:4 persistent kernel of the [T][K] layout: several row and
+    token tiles, tokens past T, K not a multiple of 128 (a token row's bytes
+    past K meet zero weights), 16-byte-aligned padded strides."""
+    force_variant("smfmac_i8_2of4_tk")
+    _tk_case("i8", out, 2, 4, R, K, T, 43, xpad=(-K) % 16 + 16, variant="smfmac_i8_2of4_tk")
+
+
+def test_tk_fast_i8_gelu(force_variant):
+    force_variant("smfmac_i8_2of4_tk")
+    _tk_case("i8", "i8", 2, 4, 528, 768, 400, 44, act="gelu", xpad=16, variant="smfmac_i8_2of4_tk")
