@@ -43,6 +43,19 @@ nm_status check_desc(const nm_packed* w, Geometry* out) {
   return NM_OK;
 }
 
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
 // Variant table (the paper's adaptive parallelism, Sec. 4.1: the kernel and
 // its tiling follow the operator's shape).  NM_SPMM_VARIANT=<name> in the
 // environment forces a variant where its requirements hold (tile sweeps).
@@ -184,7 +197,18 @@ Variant choose(const Call& c) {
   // loads; measured on MI355X at T = 12608: R = 768 and 2304 faster (15.6 /
   // 27.7 us against 17.1 / 29.8 us), R = 3072 slower (33.2 against 31.4 us)
   if (eligible(V_SMFMAC_I8S, c) && c.g->R <= 2304) return V_SMFMAC_I8S;
-  if (eligible(V_SMFMAC_I8P, c)) return V_SMFMAC_I8P;
+  // int8 2:4 persistent: 4-wave workgroups (two per CU, two waves per SIMD)
+  // while the 256 x 128 tiles can give every CU two of them; otherwise most
+  // CUs would hold one 4-wave workgroup, one wave per SIMD, and the 8-wave
+  // workgroups (512 x 128 tiles, one per CU) keep two waves per SIMD on
+  // every busy CU.  Measured on MI355X, ViT-B FC2 (R 768, K 3072, T 12608,
+  // 297 tiles): 35.0 against 42.7 us; FC1 (1188 tiles) keeps the 4-wave
+  // kernel (29.8 against 31.6 us).
+  if (eligible(V_SMFMAC_I8P, c)) {
+    const int64_t tiles4 = ((c.g->R + 255) / 256) * ((c.T + 127) / 128);
+    if (tiles4 < 2 * (int64_t)device_cus() && eligible(V_SMFMAC_I8P8, c)) return V_SMFMAC_I8P8;
+    return V_SMFMAC_I8P;
+  }
   if (eligible(V_SMFMAC_H, c)) return V_SMFMAC_H;
   // the 32 x 32-fragment dense-expand kernel is correct but measured 2-10%
   // slower than the 16 x 16 one on every ViT-B, Swin and LLaMA shape (the
@@ -201,18 +225,6 @@ Call make_call(const Geometry& g, int wdt, int ydt, int64_t T, int64_t ldx, int6
   return c;
 }
 
-int device_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cache[dev]) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    cache[dev] = cus;
-  }
-  return cache[dev];
-}
 
 // K slices for the tile kernels that take a K split (the paper's adaptive
 // parallelism, Sec. 4.1: enough work items in flight at inference-sized

@@ -247,4 +247,8 @@ def test_tk_layout_validation():
     assert tk(X=None) == nm.NM_EINVAL
     assert tk(act=1) == nm.NM_EUNSUPPORTED          # activation on raw int32
     assert tk(ydt=nm.NM_I8) == nm.NM_EINVAL         # scale required
-    assert L.nm_spmm_variant_tk(ctypes.byref(d), 100, nm.NM_I32, 0).decode() == "generic_dense_expand"
+    assert L.nm_spmm_variant_tk(ctypes.byref(d), 100, nm.NM_I32, 0).decode() == "smfmac_i8_2of4_tk"
+    # rows not a multiple of 16, other N:M and fp weights take the generic kernel
+    for other in (_desc(R=33, K=64), _desc(R=32, K=64, N=1, M=4), _desc(R=32, K=64, dt=nm.NM_F16)):
+        y = nm.NM_F16 if other.dtype == nm.NM_F16 else nm.NM_I32
+        assert L.nm_spmm_variant_tk(ctypes.byref(other), 100, y, 0).decode() == "generic_dense_expand"
