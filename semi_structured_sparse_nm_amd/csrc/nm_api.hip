@@ -72,6 +72,7 @@ enum Variant {
   V_SMFMAC_I8S,     // int8 2:4, K <= 1024: weights held in registers, workgroups walk token strips
   V_EXPAND32,       // as V_EXPAND with 32 x 32 dense MFMA (forced only: measured slower)
   V_SMFMAC_I8TK,    // int8 2:4 persistent, [T][K] layout (X [T][K], Y [T][R])
+  V_SMFMAC_H8,      // as V_SMFMAC_H with 8-wave workgroups (one per CU)
   V_COUNT
 };
 
@@ -88,6 +89,7 @@ const char* variant_name(Variant v) {
     case V_SMFMAC_I8S: return "smfmac_i8_2of4_stationary";
     case V_EXPAND32: return "expand_mfma32_persistent";
     case V_SMFMAC_I8TK: return "smfmac_i8_2of4_tk";
+    case V_SMFMAC_H8: return "smfmac_h_2of4_persistent_w8";
     default: return "invalid";
   }
 }
@@ -128,6 +130,7 @@ bool eligible(Variant v, const Call& c) {
              c.g->values_bytes() + 8192 < (1ull << 31) && (c.g->R + 256) * c.ldy * 4 < (1ll << 31) &&
              (c.ydt == NM_I32 || (c.ydt == NM_I8 && c.ldy % 16 == 0 && aligned(c.Y, 16)));
     case V_SMFMAC_H:
+    case V_SMFMAC_H8:
       // fp16 / bf16 2:4; X rows in whole 16-byte pieces; 32-bit buffer
       // offsets that do not wrap for the rows a tile reaches past K and R;
       // 16-bit output stored as 16-byte row pieces
@@ -209,6 +212,12 @@ Variant choose(const Call& c) {
     if (tiles4 < 2 * (int64_t)device_cus() && eligible(V_SMFMAC_I8P8, c)) return V_SMFMAC_I8P8;
     return V_SMFMAC_I8P;
   }
+  // fp16 / bf16 2:4: 4-wave workgroups.  The 8-wave instance (two row
+  // blocks per wave, same 256 x 128 tiles) is forced only: each of its waves
+  // reads every B fragment for half the matrix work, and measured on MI355X
+  // it was slower on most few-tile shapes (LLaMA-7B down 154.7 -> 163.7 us,
+  // Swin-T stage 3/4 projections 2-12%), faster only on LLaMA qkvo (61.6 ->
+  // 58.4 us)
   if (eligible(V_SMFMAC_H, c)) return V_SMFMAC_H;
   // the 32 x 32-fragment dense-expand kernel is correct but measured 2-10%
   // slower than the 16 x 16 one on every ViT-B, Swin and LLaMA shape (the
@@ -247,7 +256,7 @@ constexpr double kPartialGBs = 5000.0;   // partial sums' effective write + read
 constexpr double kReduceUs = 2.0;        // reduction launch and tail
 
 int ksplit_for(Variant v, const Call& c) {
-  if (v != V_SMFMAC_H && v != V_EXPAND) return 1;
+  if (v != V_SMFMAC_H && v != V_SMFMAC_H8 && v != V_EXPAND) return 1;
   const Geometry& g = *c.g;
   const int nKB = (int)g.nKB;
   if (c.T % 4 != 0) return 1;
@@ -398,7 +407,9 @@ nm_status spmm_call(const nm_packed* w, const void* X, int64_t ldx, int64_t T, v
     p.ksplit = S;
     p.kbs = (int)(g.nKB / S);
     p.ys = g.R * T;
-    e = v == V_SMFMAC_H ? nm::launch_spmm_smfmac_h(p, s) : nm::launch_spmm_expand(p, s);
+    e = v == V_SMFMAC_H    ? nm::launch_spmm_smfmac_h(p, s)
+        : v == V_SMFMAC_H8 ? nm::launch_spmm_smfmac_h8(p, s)
+                           : nm::launch_spmm_expand(p, s);
     if (e != hipSuccess) return NM_EHIP;
     a.ksplit = S;
     a.ys = p.ys;
@@ -411,6 +422,7 @@ nm_status spmm_call(const nm_packed* w, const void* X, int64_t ldx, int64_t T, v
     case V_SMFMAC_I8P: e = nm::launch_spmm_smfmac_i8p(a, 0, s); break;
     case V_SMFMAC_I8P8: e = nm::launch_spmm_smfmac_i8p(a, 1, s); break;
     case V_SMFMAC_H: e = nm::launch_spmm_smfmac_h(a, s); break;
+    case V_SMFMAC_H8: e = nm::launch_spmm_smfmac_h8(a, s); break;
     case V_SMFMAC_HD: e = nm::launch_spmm_smfmac_hd(a, s); break;
     case V_EXPAND: e = nm::launch_spmm_expand(a, s); break;
     case V_EXPAND32: e = nm::launch_spmm_expand32(a, s); break;

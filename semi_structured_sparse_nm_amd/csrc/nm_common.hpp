@@ -97,6 +97,7 @@ hipError_t launch_spmm_smfmac_i8(const SpmmArgs& a, int cfg, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8p(const SpmmArgs& a, int cfg, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8tk(const SpmmArgs& a, hipStream_t s);   // [T][K] layout
 hipError_t launch_spmm_smfmac_h(const SpmmArgs& a, hipStream_t s);
+hipError_t launch_spmm_smfmac_h8(const SpmmArgs& a, hipStream_t s);   // 8-wave workgroups
 hipError_t launch_spmm_smfmac_hd(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8s(const SpmmArgs& a, hipStream_t s);
 bool smfmac_i8s_supported(int64_t nKB);   // column-block counts launch_spmm_smfmac_i8s instantiates

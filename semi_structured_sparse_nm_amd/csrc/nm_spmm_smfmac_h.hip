@@ -83,7 +83,6 @@ __device__ __forceinline__ v2i lds_tr16(const uint8_t* p) {
       v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p)));
 }
 
-constexpr int RB = 4;              // row blocks (16 rows) per wave
 constexpr int TN = 8;              // token tiles (16 tokens) per wave
 constexpr int BN = TN * 16;        // 128 tokens per tile
 constexpr int STAGE = 64 * 256;    // bytes per X stage: 64 k x 128 tokens x 2 B
@@ -119,6 +118,9 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
 smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr bool OUT16 = OUT != NM_F32;
+  // row blocks (16 rows) per wave: 4 with 4-wave workgroups (two per CU),
+  // 2 with 8-wave workgroups (one per CU); the tile is 256 x 128 either way
+  constexpr int RB = 16 / NW;
   constexpr int BM = NW * RB * 16;
   constexpr int DPW = STAGE / 1024 / NW;     // 1 KB direct-to-LDS loads per wave per block
   constexpr int NL = 2 * RB + DPW;           // loads per group (+1 bias on a tile's first block)
@@ -224,7 +226,7 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
       }
     } else {
       if (g_live && lkb == 0) {
-        const int boff = __builtin_amdgcn_readfirstlane(4 * (lr0 + 64 * wave));
+        const int boff = __builtin_amdgcn_readfirstlane(4 * (lr0 + 16 * RB * wave));
         lds_dma4(rbias, lds_addr(bsw + 256 * (lk & 3)), 4 * lane, boff);
       }
       ++ln;
@@ -240,9 +242,11 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   constexpr int NPART = RB + 3;
   auto load_group = [&](auto st) {
     load_part(st, ic<0>()); load_part(st, ic<1>()); load_part(st, ic<2>()); load_part(st, ic<3>());
-    load_part(st, ic<4>()); load_part(st, ic<5>()); load_part(st, ic<6>());
+    load_part(st, ic<4>());
+    if constexpr (NPART > 5) load_part(st, ic<5>());
+    if constexpr (NPART > 6) load_part(st, ic<6>());
   };
-  static_assert(RB == 4 && NPART == 7, "load parts are spelled out for four row blocks");
+  static_assert(NPART >= 5 && NPART <= 7, "load parts are spelled out for two or four row blocks");
   auto group_size_extra = [&](int m) { return (m < total && m % kbs == 0) ? 1 : 0; };
 
   v4f acc[RB][TN];
@@ -335,7 +339,8 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
           d[2 * rb + 1] = pack2<OUT>(fp_act<EACT>(acc[rb][tt][2]), fp_act<EACT>(acc[rb][tt][3]));
         }
         *reinterpret_cast<v4i*>(os + wbase + 2048 * w) = v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
-        *reinterpret_cast<v4i*>(os + wbase + 2048 * w + 16) = v4i{(int)d[4], (int)d[5], (int)d[6], (int)d[7]};
+        if constexpr (RB > 2)
+          *reinterpret_cast<v4i*>(os + wbase + 2048 * w + 16) = v4i{(int)d[4], (int)d[5], (int)d[6], (int)d[7]};
       }
       const int tok = t0 + 32 * u4 + 8 * lg;
       const bool tok_ok = tok < a.T;
@@ -344,8 +349,10 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         const uint8_t* rp = os + (rbase ^ (32 * s));
         const v2i x0 = lds_tr16(rp);
         const v2i x1 = lds_tr16(rp + 512);
-        const int row = r0 + 64 * wave + orow + 4 * s;
-        const int off = tok_ok ? (row * (int)a.ldy + tok) * 2 : oob;
+        // with two row blocks a wave owns rows 0..31 of the staging layout's
+        // 64; the lanes that read rows 32..63 store nothing
+        const int row = r0 + 16 * RB * wave + orow + 4 * s;
+        const int off = (tok_ok && orow + 4 * s < 16 * RB) ? (row * (int)a.ldy + tok) * 2 : oob;
         __builtin_amdgcn_raw_buffer_store_b128(v4i{x0[0], x0[1], x1[0], x1[1]}, ry, off, 0, kStreamStore);
       }
     }
@@ -355,7 +362,7 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     constexpr bool EACT = decltype(actc)::value != 0;
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<float*>(a.Y) + ks * a.ys, 0, (int)(g.R * a.ldy * 4), 0x00020000);
-    const int rw = r0 + 64 * wave + 4 * lg;
+    const int rw = r0 + 16 * RB * wave + 4 * lg;
     const int oob = (int)(g.R * a.ldy * 4);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -445,7 +452,7 @@ int cu_count(int device) {
 
 template <int NW, int WT>
 hipError_t launch_nw(const SpmmArgs& a, hipStream_t s) {
-  constexpr int BM = NW * RB * 16;
+  constexpr int BM = 256;
   const int mtiles = (int)((a.g.R + BM - 1) / BM);
   const int ntiles = (int)((a.T + BN - 1) / BN);
   const int ntot = mtiles * ntiles * a.ksplit;
@@ -481,6 +488,11 @@ hipError_t launch_nw(const SpmmArgs& a, hipStream_t s) {
 // fp16 / bf16 2:4, 4-wave workgroups (256 x 128 tiles, two per CU)
 hipError_t launch_spmm_smfmac_h(const SpmmArgs& a, hipStream_t s) {
   return a.wdt == NM_F16 ? launch_nw<4, NM_F16>(a, s) : launch_nw<4, NM_BF16>(a, s);
+}
+
+// the same tiles with 8-wave workgroups (one per CU, two waves per SIMD)
+hipError_t launch_spmm_smfmac_h8(const SpmmArgs& a, hipStream_t s) {
+  return a.wdt == NM_F16 ? launch_nw<8, NM_F16>(a, s) : launch_nw<8, NM_BF16>(a, s);
 }
 
 }  // namespace nm

@@ -193,7 +193,7 @@ def test_fast_i8_variants(force_variant, variant, out, R, K, T):
     assert np.all(Y[:, T:] == 5), "writes beyond T"
 
 
-FAST_H = ["smfmac_h_2of4_persistent"]
+FAST_H = ["smfmac_h_2of4_persistent", "smfmac_h_2of4_persistent_w8"]
 
 
 @pytest.mark.parametrize("variant", FAST_H)
@@ -377,16 +377,16 @@ KSPLIT_SHAPES = [(300, 1536, 400, 4), (520, 768, 144, 3), (64, 4096, 32, 8), (25
                  (130, 1000, 160, 4)]
 
 
+@pytest.mark.parametrize("variant", FAST_H)
 @pytest.mark.parametrize("dt,out", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
 @pytest.mark.parametrize("R,K,T,S", KSPLIT_SHAPES)
 @pytest.mark.parametrize("ldy_pad", [8, 3])
-def test_ksplit_h(force_variant, force_ksplit, dt, out, R, K, T, S, ldy_pad):
+def test_ksplit_h(force_variant, force_ksplit, variant, dt, out, R, K, T, S, ldy_pad):
     """fp16 / bf16 2:4 tile kernel with K cut into S slices across
     workgroups: fp32 partials in the workspace, reduced in slice order with
     the bias and the output rounding; aligned (vector) and unaligned
     (element) output rows."""
-    _ksplit_case(force_variant, force_ksplit, "smfmac_h_2of4_persistent", dt, out, 2, 4, R, K, T, S,
-                 ldy_pad, 21)
+    _ksplit_case(force_variant, force_ksplit, variant, dt, out, 2, 4, R, K, T, S, ldy_pad, 21)
 
 
 @pytest.mark.parametrize("dt,out", PAIRS)
@@ -457,10 +457,11 @@ def test_gelu_expand(force_variant, dt, out, N, M, R, K, T):
     _gelu_case(force_variant, "expand_mfma_persistent", dt, out, N, M, R, K, T, 32)
 
 
+@pytest.mark.parametrize("variant", FAST_H)
 @pytest.mark.parametrize("dt,out", GELU_FP)
 @pytest.mark.parametrize("R,K,T", GELU_SHAPES)
-def test_gelu_h(force_variant, dt, out, R, K, T):
-    _gelu_case(force_variant, "smfmac_h_2of4_persistent", dt, out, 2, 4, R, K, T, 33)
+def test_gelu_h(force_variant, variant, dt, out, R, K, T):
+    _gelu_case(force_variant, variant, dt, out, 2, 4, R, K, T, 33)
 
 
 @pytest.mark.parametrize("dt,out", [("i8", "i8")] + GELU_FP)
