@@ -195,21 +195,16 @@ Variant choose(const Call& c) {
   // decode shapes (few tokens): K split inside a workgroup per 16-row block
   if (eligible(V_SMFMAC_HD, c)) return V_SMFMAC_HD;
   if (eligible(V_EXPAND_DECODE, c)) return V_EXPAND_DECODE;
-  // int8 2:4 with K <= 1024: the weight-stationary kernel while a row block
-  // is shared by enough token strips per workgroup to amortise its weight
-  // loads; measured on MI355X at T = 12608: R = 768 and 2304 faster (15.6 /
-  // 27.7 us against 17.1 / 29.8 us), R = 3072 slower (33.2 against 31.4 us)
-  if (eligible(V_SMFMAC_I8S, c) && c.g->R <= 2304) return V_SMFMAC_I8S;
-  // int8 2:4 persistent: 4-wave workgroups (two per CU, two waves per SIMD)
-  // while the 256 x 128 tiles can give every CU two of them; otherwise most
-  // CUs would hold one 4-wave workgroup, one wave per SIMD, and the 8-wave
-  // workgroups (512 x 128 tiles, one per CU) keep two waves per SIMD on
-  // every busy CU.  Measured on MI355X, ViT-B FC2 (R 768, K 3072, T 12608,
-  // 297 tiles): 35.0 against 42.7 us; FC1 (1188 tiles) keeps the 4-wave
-  // kernel (29.8 against 31.6 us).
+  // int8 2:4 persistent: 8-wave workgroups (512 x 128 tiles, one per CU,
+  // two waves per SIMD) unless the 256 x 128 tiles of the 4-wave kernel
+  // (two workgroups per CU) number at least four per CU.  Measured on MI355X
+  // at T = 12608 (4-wave tiles; 4-wave / 8-wave / weight-stationary us):
+  // proj R 768 (297): 17.6 / 15.0 / 15.6; FC2 R 768, K 3072 (297): 43.3 /
+  // 36.5; QKV R 2304 (891): 30.2 / 25.7 / 28.7; FC1 R 3072 (1188): 31.5 /
+  // 33.1.  The weight-stationary kernel is no longer picked (forced only).
   if (eligible(V_SMFMAC_I8P, c)) {
     const int64_t tiles4 = ((c.g->R + 255) / 256) * ((c.T + 127) / 128);
-    if (tiles4 < 2 * (int64_t)device_cus() && eligible(V_SMFMAC_I8P8, c)) return V_SMFMAC_I8P8;
+    if (tiles4 < 4 * (int64_t)device_cus() && eligible(V_SMFMAC_I8P8, c)) return V_SMFMAC_I8P8;
     return V_SMFMAC_I8P;
   }
   // fp16 / bf16 2:4: 4-wave workgroups.  The 8-wave instance (two row

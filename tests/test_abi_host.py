@@ -221,7 +221,7 @@ def test_activation_validation_and_variant_choice():
     fc1 = _desc(R=3072, K=768)
     assert va(fc1, 12608, nm.NM_I8, 0) == "smfmac_i8_2of4_persistent"
     assert va(fc1, 12608, nm.NM_I8, 1) == "smfmac_i8_2of4_persistent"
-    assert va(_desc(R=2304, K=768), 12608, nm.NM_I8, 1) == "smfmac_i8_2of4_stationary"
+    assert va(_desc(R=2304, K=768), 12608, nm.NM_I8, 1) == "smfmac_i8_2of4_persistent_w8"
     deep = _desc(R=3072, K=3072, N=1, M=4)
     assert va(deep, 12608, nm.NM_I8, 1) == "expand_mfma_persistent"
     assert va(fc1, 12608, nm.NM_I32, 1) == "invalid"
@@ -252,3 +252,15 @@ def test_tk_layout_validation():
     for other in (_desc(R=33, K=64), _desc(R=32, K=64, N=1, M=4), _desc(R=32, K=64, dt=nm.NM_F16)):
         y = nm.NM_F16 if other.dtype == nm.NM_F16 else nm.NM_I32
         assert L.nm_spmm_variant_tk(ctypes.byref(other), 100, y, 0).decode() == "generic_dense_expand"
+
+
+def test_int8_workgroup_size_choice():
+    """int8 2:4: 8-wave persistent workgroups unless the 4-wave kernel's
+    256 x 128 tiles number at least four per CU (256 CUs assumed without a
+    GPU): the ViT-B shapes at batch 64."""
+    L = nm.lib()
+    v = lambda R, K, T: L.nm_spmm_variant(ctypes.byref(_desc(R=R, K=K)), T, nm.NM_I8).decode()
+    assert v(3072, 768, 12608) == "smfmac_i8_2of4_persistent"        # FC1: 1188 tiles
+    assert v(2304, 768, 12608) == "smfmac_i8_2of4_persistent_w8"     # QKV: 891
+    assert v(768, 3072, 12608) == "smfmac_i8_2of4_persistent_w8"     # FC2: 297
+    assert v(768, 768, 12608) == "smfmac_i8_2of4_persistent_w8"      # proj: 297
