@@ -64,7 +64,6 @@ __device__ __forceinline__ v2i lds_tr16(const uint8_t* p) {
 }
 
 constexpr int NWD = 8;             // waves per workgroup (K split)
-constexpr int D = 4;               // LDS slots (load groups in flight) per wave
 
 // LDS slot of one column block: X (2 KB: KB rows x 16 tokens), the block's
 // packed values (16 C_B bytes, in 1 KB and 256-byte loads), its meta (16 MRB
@@ -91,8 +90,13 @@ __global__ void __launch_bounds__(NWD * 64) expand_decode_kernel(SpmmArgs a) {
   constexpr int EB = RG::EB;
   typedef typename std::conditional<I8, v4i, v4f>::type Acc;
 
+  // LDS slots (load groups in flight) per wave: three, or two where three
+  // would not let two workgroups share a CU's 160 KB (one starts streaming
+  // while the other drains).  Measured on MI355X (LLaMA-7B T = 16): up 4:8
+  // 21.4 us with four slots and one workgroup per CU, 17.2 us with three.
+  constexpr int D = (80 * 1024) / (NWD * SL::BYTES) >= 3 ? 3 : 2;
+  static_assert(2 * NWD * D * SL::BYTES <= 160 * 1024, "two workgroups per CU");
   __shared__ __attribute__((aligned(1024))) uint8_t slots[NWD * D * SL::BYTES];
-  __shared__ __attribute__((aligned(1024))) Acc red[NWD * 64];
 
   const Geometry& g = a.g;
   const int lane = threadIdx.x & 63;
@@ -200,7 +204,9 @@ __global__ void __launch_bounds__(NWD * 64) expand_decode_kernel(SpmmArgs a) {
   __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));   // nothing lands in LDS after this
 
   // partial sums of the eight waves, added in wave order
-  red[wave * 64 + lane] = acc;
+  // a wave's partial goes to the start of its own slots, which nothing reads
+  // or fills any more
+  reinterpret_cast<Acc*>(ws)[lane] = acc;
   __syncthreads();
   const int t = threadIdx.x;
   if (t < 256) {
@@ -212,7 +218,7 @@ __global__ void __launch_bounds__(NWD * 64) expand_decode_kernel(SpmmArgs a) {
       if constexpr (I8) {
         int y = 0;
 #pragma unroll
-        for (int w = 0; w < NWD; ++w) y += red[w * 64 + ln][v];
+        for (int w = 0; w < NWD; ++w) y += reinterpret_cast<const Acc*>(slots + w * (D * SL::BYTES))[ln][v];
         if (a.bias) y += static_cast<const int*>(a.bias)[r];
         if constexpr (OUT == NM_I8)
           static_cast<int8_t*>(a.Y)[o] = (int8_t)(a.act ? requant_act_i8<true>(y, a.scale[r], a.out_scale)
@@ -222,7 +228,7 @@ __global__ void __launch_bounds__(NWD * 64) expand_decode_kernel(SpmmArgs a) {
       } else {
         float y = 0.f;
 #pragma unroll
-        for (int w = 0; w < NWD; ++w) y += red[w * 64 + ln][v];
+        for (int w = 0; w < NWD; ++w) y += reinterpret_cast<const Acc*>(slots + w * (D * SL::BYTES))[ln][v];
         if (a.bias) y += static_cast<const float*>(a.bias)[r];
         if (a.act) y = gelu_f32(y);
         if constexpr (OUT == NM_F32)

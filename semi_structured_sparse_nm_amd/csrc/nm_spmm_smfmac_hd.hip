@@ -70,15 +70,20 @@ __device__ __forceinline__ v4f smfmac(v4i a, v8i b, v4f c, int idx) {
 }
 
 constexpr int NWD = 8;             // waves per workgroup (K split)
-constexpr int D = 4;               // LDS slots (load groups in flight) per wave
-constexpr int SLOT = 4096;         // bytes per slot: X 2 KB | A 1 KB | index words 256 B
+// LDS slots (load groups in flight) per wave: three slots of 3.25 KB per
+// wave (78 KB per workgroup) let two workgroups share a CU, so one starts
+// streaming while the other drains.  Measured on MI355X (LLaMA-7B T = 16):
+// faster than four slots with one workgroup per CU (up 2:4 17.6 -> 15.0 us)
+// and than six (18.8 us); two slots are within noise of three.
+constexpr int D = 3;
+constexpr int SLOT = 3328;         // bytes per slot: X 2 KB | A 1 KB | index words 256 B
 constexpr int NLG = 4;             // loads per group
 
 template <int WT, int OUT>
 __global__ void __launch_bounds__(NWD * 64) smfmac_hd_kernel(SpmmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(1024))) uint8_t slots[NWD * D * SLOT];
-  __shared__ __attribute__((aligned(1024))) v4f red[NWD * 64];
+  static_assert(NWD * D * SLOT <= 160 * 1024, "LDS");
 
   const Geometry& g = a.g;
   const int lane = threadIdx.x & 63;
@@ -149,8 +154,9 @@ __global__ void __launch_bounds__(NWD * 64) smfmac_hd_kernel(SpmmArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));   // nothing lands in LDS after this
 
-  // partial sums of the eight waves, added in wave order
-  red[wave * 64 + lane] = acc;
+  // partial sums of the eight waves, added in wave order; a wave's partial
+  // goes to the start of its own slots, which nothing reads or fills any more
+  reinterpret_cast<v4f*>(ws)[lane] = acc;
   __syncthreads();
   const int t = threadIdx.x;
   if (t < 256) {
@@ -159,7 +165,7 @@ __global__ void __launch_bounds__(NWD * 64) smfmac_hd_kernel(SpmmArgs a) {
     float y = 0.f;
 #pragma unroll
     for (int w = 0; w < NWD; ++w) {
-      const v4f p = red[w * 64 + ln];
+      const v4f p = reinterpret_cast<const v4f*>(slots + w * (D * SLOT))[ln];
       y += p[v];
     }
     const int64_t r = (int64_t)rb * 16 + row;
