@@ -118,7 +118,13 @@ nm_status nm_pack(const void* W, int64_t ldw, nm_packed* desc, void* stream);
  * run as separate work items): S * rows * T * 4 bytes, int32 or fp32, which a
  * second kernel on the same stream adds in slice order before the epilogue.
  * The split is a function of the shape and the device (nm_spmm_ksplit), so
- * the size is too.  The caller owns the buffer; nm_spmm only writes it and
+ * the size is too.  For a 1:4, 1:8 or 2:8 int8 weight with a large product
+ * (R K T >= 2^31, [K][T] layout) it instead holds a copy of the weight re-packed
+ * into the 2:4 layout (such a pattern is also a 2:4 pattern), which the 2:4
+ * sparse-MFMA kernels then multiply: the 2:4 values_bytes rounded up to 256,
+ * then the 2:4 meta_bytes.  Given less than that (or a workspace not 256-byte
+ * aligned), nm_spmm runs the N:M kernel instead, with the same result.
+ * The caller owns the buffer; nm_spmm only writes it and
  * reads it back within the call's stream order, so calls that share one
  * workspace must be ordered on one stream.
  */
@@ -189,8 +195,11 @@ const char* nm_status_str(nm_status s);
 
 /*
  * Name of the kernel variant nm_spmm would launch for these arguments
- * (static string; "invalid" when the arguments would be rejected).  For
- * tests and profiling; launches nothing.
+ * (static string; "invalid" when the arguments would be rejected).  A 1:4,
+ * 1:8 or 2:8 product re-packed to 2:4 in the workspace is named
+ * "repack24_" + the 2:4 kernel's name (assuming the workspace
+ * nm_spmm_workspace_size asks for).  For tests and profiling; launches
+ * nothing.
  */
 const char* nm_spmm_variant(const nm_packed* w, int64_t T, int32_t y_dtype);
 

@@ -185,12 +185,18 @@ bool eligible(Variant v, const Call& c) {
   }
 }
 
+Variant choose_auto(const Call& c);
+
 Variant choose(const Call& c) {
   const char* force = getenv("NM_SPMM_VARIANT");
   if (force && *force) {
     for (int v = V_GENERIC; v < V_COUNT; ++v)
       if (strcmp(force, variant_name((Variant)v)) == 0 && eligible((Variant)v, c)) return (Variant)v;
   }
+  return choose_auto(c);
+}
+
+Variant choose_auto(const Call& c) {
   if (eligible(V_SMFMAC_I8TK, c)) return V_SMFMAC_I8TK;
   // decode shapes (few tokens): K split inside a workgroup per 16-row block
   if (eligible(V_SMFMAC_HD, c)) return V_SMFMAC_HD;
@@ -285,6 +291,81 @@ size_t workspace_for(Variant v, const Call& c) {
   return S > 1 ? (size_t)S * c.g->R * c.T * 4 : 0;
 }
 
+// ---- 2:4 re-pack.  A 1:4, 1:8 or 2:8 weight is also a 2:4 weight (no
+// group of four columns holds more than two kept members), so its product
+// can run on the 2:4 sparse-MFMA tile kernels: the call first re-packs the
+// weight into the 2:4 layout in the workspace (nm_repack24.hip), then runs
+// the 2:4 kernel on that copy.  The copy costs one small launch (about 2 us
+// on ViT-B shapes) and a few MB of traffic; the int8 2:4 kernels issue half
+// the matrix instructions of the dense-expand ones (whose dense int8 MFMA
+// also runs at about half the sparse one's rate) and expand nothing.
+// Measured on MI355X, ViT-B int8 at T = 12608 (expand -> re-packed, us):
+// 1:4 QKV 33.5 -> 28.1, proj 17.9 -> 17.1, FC1 39.1 -> 35.2, FC2 50.5 ->
+// 37.9; 2:8 QKV 35.4 -> 27.9, proj 18.6 -> 17.2, FC1 43.2 -> 35.1, FC2 55.2
+// -> 38.7.  For fp16 / bf16 it did not pay (Swin-T 1:4: from 4% faster to
+// 24% slower), so it is taken for int8 weights only, in the [K][T] layout,
+// when the product is large enough for the extra launch (R K T >= 2^31) and
+// the 2:4 kernel would run without a K split.
+// NM_SPMM_VARIANT=repack24_<2:4 tile variant> forces it (fp16 / bf16 too)
+// where the 2:4 kernel's requirements hold.
+constexpr double kRepackMinWork = 2147483648.0;
+constexpr const char* kRepackPrefix = "repack24_";
+
+struct Plan {
+  Variant v = V_INVALID;
+  bool repack = false;
+  Geometry g24;              // the 2:4 geometry of the re-packed copy
+};
+
+size_t repack_meta_off(const Geometry& g24) { return (g24.values_bytes() + 255) / 256 * 256; }
+size_t repack_bytes(const Geometry& g24) { return repack_meta_off(g24) + g24.meta_bytes(); }
+
+bool repack_inner(Variant v) {
+  return v == V_SMFMAC_I8P || v == V_SMFMAC_I8P8 || v == V_SMFMAC_H || v == V_SMFMAC_H8;
+}
+
+Plan plan_for(const Call& c) {
+  Plan p;
+  p.v = choose(c);
+  if (!nm::repack24_supported(*c.g) || c.layout != NM_LAYOUT_KT) return p;
+  const char* force = getenv("NM_SPMM_VARIANT");
+  const bool forced = force && *force;
+  const bool forced_rp = forced && strncmp(force, kRepackPrefix, strlen(kRepackPrefix)) == 0;
+  if (forced && !forced_rp) return p;
+  if (!forced_rp && (c.wdt != NM_I8 || p.v != V_EXPAND ||
+                     (double)c.g->R * (double)c.g->K * (double)c.T < kRepackMinWork))
+    return p;
+  const Geometry g24 = Geometry::make(c.g->R, c.g->K, 2, 4, c.g->eb);
+  Call c24 = c;
+  c24.g = &g24;
+  Variant inner = V_INVALID;
+  if (forced_rp) {
+    const char* name = force + strlen(kRepackPrefix);
+    for (int v = V_GENERIC; v < V_COUNT; ++v)
+      if (repack_inner((Variant)v) && strcmp(name, variant_name((Variant)v)) == 0 && eligible((Variant)v, c24))
+        inner = (Variant)v;
+  } else {
+    inner = choose_auto(c24);
+  }
+  // a forced re-pack runs the 2:4 kernel unsplit
+  if (!repack_inner(inner) || (!forced_rp && ksplit_for(inner, c24) != 1)) return p;
+  p.v = inner;
+  p.repack = true;
+  p.g24 = g24;
+  return p;
+}
+
+const char* plan_name(const Plan& p) {
+  if (!p.repack) return variant_name(p.v);
+  switch (p.v) {
+    case V_SMFMAC_I8P: return "repack24_smfmac_i8_2of4_persistent";
+    case V_SMFMAC_I8P8: return "repack24_smfmac_i8_2of4_persistent_w8";
+    case V_SMFMAC_H: return "repack24_smfmac_h_2of4_persistent";
+    case V_SMFMAC_H8: return "repack24_smfmac_h_2of4_persistent_w8";
+    default: return "invalid";
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -333,6 +414,10 @@ nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype,
     size_t n = workspace_for((Variant)v, c);
     if (n > need) need = n;
   }
+  for (int act = NM_ACT_NONE; act <= NM_ACT_GELU; ++act) {
+    const Plan p = plan_for(make_call(g, w->dtype, y_dtype, T, T, T, al, al, act));
+    if (p.repack && repack_bytes(p.g24) > need) need = repack_bytes(p.g24);
+  }
   *bytes = need;
   return NM_OK;
 }
@@ -360,9 +445,16 @@ nm_status spmm_call(const nm_packed* w, const void* X, int64_t ldx, int64_t T, v
   if (bias && !aligned(bias, 4)) return NM_EUNSUPPORTED;
   if (scale && !aligned(scale, 4)) return NM_EUNSUPPORTED;
   const Call call = make_call(g, w->dtype, y_dtype, T, ldx, ldy, X, Y, act, layout);
-  Variant v = choose(call);
-  const int S = ksplit_for(v, call);
-  size_t need = workspace_for(v, call);
+  Plan pl = plan_for(call);
+  // a workspace too small (or not 256-byte aligned) for the 2:4 copy: the
+  // N:M kernel the plan would otherwise have used (same result)
+  if (pl.repack && (!workspace || workspace_bytes < repack_bytes(pl.g24) || !aligned(workspace, 256))) {
+    pl.repack = false;
+    pl.v = choose(call);
+  }
+  Variant v = pl.v;
+  const int S = pl.repack ? 1 : ksplit_for(v, call);
+  size_t need = pl.repack ? repack_bytes(pl.g24) : workspace_for(v, call);
   if (workspace_bytes < need || (need && !workspace)) return NM_EINVAL;
   if (need && !aligned(workspace, 16)) return NM_EUNSUPPORTED;
 
@@ -389,6 +481,15 @@ nm_status spmm_call(const nm_packed* w, const void* X, int64_t ldx, int64_t T, v
   a.layout = layout;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  if (pl.repack) {
+    uint8_t* wv = static_cast<uint8_t*>(workspace);
+    uint8_t* wm = static_cast<uint8_t*>(workspace) + repack_meta_off(pl.g24);
+    e = nm::launch_repack24(g, a.values, a.meta, pl.g24, wv, wm, s);
+    if (e != hipSuccess) return NM_EHIP;
+    a.g = pl.g24;
+    a.values = wv;
+    a.meta = wm;
+  }
   if (S > 1) {
     // K slices write raw 32-bit partial sums to the workspace; the reduction
     // adds them and applies this call's epilogue
@@ -470,7 +571,7 @@ const char* nm_spmm_variant_act(const nm_packed* w, int64_t T, int32_t y_dtype, 
   if ((act != NM_ACT_NONE && act != NM_ACT_GELU) || (act != NM_ACT_NONE && y_dtype == NM_I32)) return "invalid";
   // dense row-major operands, 256-byte aligned (what a fresh allocation gives)
   const void* al = reinterpret_cast<const void*>((uintptr_t)256);
-  return variant_name(choose(make_call(g, w->dtype, y_dtype, T, T, T, al, al, act)));
+  return plan_name(plan_for(make_call(g, w->dtype, y_dtype, T, T, T, al, al, act)));
 }
 
 const char* nm_spmm_variant(const nm_packed* w, int64_t T, int32_t y_dtype) {
@@ -491,7 +592,8 @@ int32_t nm_spmm_ksplit(const nm_packed* w, int64_t T, int32_t y_dtype, int32_t a
   if ((act != NM_ACT_NONE && act != NM_ACT_GELU) || (act != NM_ACT_NONE && y_dtype == NM_I32)) return 0;
   const void* al = reinterpret_cast<const void*>((uintptr_t)256);
   const Call c = make_call(g, w->dtype, y_dtype, T, T, T, al, al, act);
-  return ksplit_for(choose(c), c);
+  const Plan p = plan_for(c);
+  return p.repack ? 1 : ksplit_for(p.v, c);
 }
 
 }  // extern "C"

@@ -106,6 +106,12 @@ hipError_t launch_spmm_expand_decode(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_expand32(const SpmmArgs& a, hipStream_t s);
 bool expand32_supported(int N, int M);   // N:M instantiated by launch_spmm_expand32
 bool expand_supported(int N, int M);   // N:M instantiated by launch_spmm_expand
+// N:M patterns with at most two kept members in every aligned group of four
+// columns (1:4, 1:8, 2:8), and their re-pack into the 2:4 layout of the same
+// matrix (gd: Geometry::make(R, K, 2, 4, eb)), written to dvalues / dmeta.
+bool repack24_supported(const Geometry& g);
+hipError_t launch_repack24(const Geometry& gs, const uint8_t* values, const uint8_t* meta, const Geometry& gd,
+                           uint8_t* dvalues, uint8_t* dmeta, hipStream_t s);
 // Y = epilogue(sum over the a.ksplit slices of the partials at a.ws) with
 // a's own output type, bias and scale (T a multiple of 4).
 hipError_t launch_splitk_reduce(const SpmmArgs& a, hipStream_t s);

@@ -1,0 +1,161 @@
+// Re-pack an N:M weight whose every aligned group of four columns holds at
+// most two kept members (1:4, 1:8, 2:8) into the 2:4 packed layout of the
+// same matrix, so that its product runs on the gfx950 sparse matrix
+// instructions (v_smfmac, which take 2:4 operands) instead of the
+// dense-expand kernels.
+//
+// Such a pattern is a 2:4 pattern ("Realizable N:M Sparse Transformer
+// Inference via Search-Kernel Co-Design", Sec. 2.1: N kept of every M
+// consecutive weights; with N = 1, or N = 2 and M = 8, no group of four
+// consecutive columns can hold more than two kept members), so the re-pack
+// loses nothing: the 2:4 copy describes the same dense matrix, bit for bit.
+// Each group of four gets two slots at two distinct ascending positions:
+//   two kept members (a 2:8 pair in one half): both, at their positions;
+//   one kept member v at q: (v, 0) at (0, 1) when q = 0, else (0, v) at (0, q);
+//   none: (0, 0) at (0, 1), which is also what nm_pack writes into padding.
+// Positions are read as nm_pack writes them (ascending within a group), so
+// two members of a 2:8 group in different halves are the first in the lower
+// half and the second in the upper one.
+//
+// One thread per (row, column block, 32-column chunk): it reads the source's
+// kept values and positions of those 32 columns (one load of 4 to 16 bytes
+// and one or two dwords of positions, all issued before any is used) and
+// writes 16 slots of 2:4 values (16 B for int8, 32 B for fp16 / bf16) and
+// one 32-bit word of 2-bit positions.  Run inside the product call on its stream; the 2:4 copy
+// lives in the caller's workspace.
+#include "nm_common.hpp"
+
+namespace nm {
+
+namespace {
+
+template <int EB, int M, int N>
+__global__ void __launch_bounds__(256) repack24_kernel(Geometry gs, const uint8_t* __restrict__ sv,
+                                                       const uint8_t* __restrict__ sm, Geometry gd,
+                                                       uint8_t* __restrict__ dv, uint8_t* __restrict__ dm) {
+  constexpr int KB = 128 / EB;          // dense columns per block
+  constexpr int NCH = KB / 32;          // 32-column chunks per block row
+  constexpr int SG = 32 / M;            // source groups per chunk
+  constexpr int NS = SG * N;            // source slots per chunk
+  constexpr int W = M == 4 ? 2 : 3;     // position bits
+  constexpr int NVW = NS * EB / 4;      // dwords of source values per chunk (1, 2 or 4)
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = gs.nRB * 16 * gs.nKB * NCH;
+  if (tid >= total) return;
+  const int j = (int)(tid % NCH);
+  const int64_t rk = tid / NCH;
+  const int64_t kb = rk % gs.nKB;
+  const int64_t r = rk / gs.nKB;         // row, padding rows included
+  const int64_t blk = (r >> 4) * gs.nKB + kb;
+  const int rr = (int)(r & 15);
+  const int c0 = j * NS;                 // first source slot of the chunk
+
+  // every load up front (one memory round trip): the chunk's values (NS EB
+  // bytes at slot c0, aligned to their size) and the 64-bit window of the
+  // row's position bitstream that holds its NS W bits; the second dword is
+  // read only where the row has one (the chunk's bits never reach past the
+  // row's own bytes)
+  const uint32_t* vsrc =
+      reinterpret_cast<const uint32_t*>(sv + blk * gs.vblk + (int64_t)rr * gs.C * EB + (int64_t)c0 * EB);
+  uint32_t vw[NVW];
+  if constexpr (NVW == 4) {
+    const v4i t = *reinterpret_cast<const v4i*>(vsrc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vw[i] = (uint32_t)t[i];
+  } else if constexpr (NVW == 2) {
+    typedef int v2i_ __attribute__((ext_vector_type(2)));
+    const v2i_ t = *reinterpret_cast<const v2i_*>(vsrc);
+    vw[0] = (uint32_t)t[0];
+    vw[1] = (uint32_t)t[1];
+  } else {
+    vw[0] = vsrc[0];
+  }
+  const uint32_t* mrow = reinterpret_cast<const uint32_t*>(sm + blk * gs.mblk + (int64_t)rr * gs.MR);
+  const int base = c0 * W, wi = base >> 5;
+  uint64_t win = mrow[wi];
+  if (wi + 1 < gs.MR / 4) win |= (uint64_t)mrow[wi + 1] << 32;
+  win >>= (base & 31);
+
+  uint32_t dval[16];                     // the chunk's 16 destination slots
+  uint32_t dpos = 0;                     // their 2-bit positions
+  // destination group d of the chunk: slots (s0, s1) at positions (q0, q1)
+  auto put = [&](int d, uint32_t s0, uint32_t s1, uint32_t q0, uint32_t q1) {
+    dval[2 * d] = s0;
+    dval[2 * d + 1] = s1;
+    dpos |= (q0 | (q1 << 2)) << (4 * d);
+  };
+  // one kept member v at q of a group of four; one_or_none: the member, or
+  // none when it sits in the other half of its group of eight
+  auto one = [&](int d, uint32_t v, uint32_t q) {
+    put(d, q == 0 ? v : 0u, q == 0 ? 0u : v, 0u, q == 0 ? 1u : q);
+  };
+  auto one_or_none = [&](int d, bool here, uint32_t v, uint32_t q) {
+    one(d, here ? v : 0u, here ? q : 0u);
+  };
+  const uint32_t vmask = EB == 1 ? 0xFFu : 0xFFFFu;
+  auto value = [&](int sl) { return (vw[sl * EB / 4] >> (8 * ((sl * EB) & 3))) & vmask; };
+  auto position = [&](int sl) { return (uint32_t)(win >> (sl * W)) & (uint32_t)(M - 1); };
+#pragma unroll
+  for (int q = 0; q < SG; ++q) {
+    if constexpr (M == 4) {
+      one(q, value(q), position(q));                       // 1:4
+    } else if constexpr (N == 1) {
+      const uint32_t v = value(q), p = position(q);        // 1:8
+      one_or_none(2 * q, p < 4, v, p & 3);
+      one_or_none(2 * q + 1, p >= 4, v, p & 3);
+    } else {
+      const uint32_t v0 = value(2 * q), p0 = position(2 * q);      // 2:8
+      const uint32_t v1 = value(2 * q + 1), p1 = position(2 * q + 1);
+      if ((p0 >> 2) == (p1 >> 2)) {
+        // both in one half: that half holds the pair, the other none
+        const bool lo = p0 < 4;
+        put(2 * q, lo ? v0 : 0u, lo ? v1 : 0u, lo ? (p0 & 3) : 0u, lo ? (p1 & 3) : 1u);
+        put(2 * q + 1, lo ? 0u : v0, lo ? 0u : v1, lo ? 0u : (p0 & 3), lo ? 1u : (p1 & 3));
+      } else {
+        one(2 * q, v0, p0 & 3);
+        one(2 * q + 1, v1, p1 & 3);
+      }
+    }
+  }
+
+  uint8_t* vout = dv + blk * gd.vblk + (int64_t)rr * gd.C * EB + 16 * j * EB;
+  if constexpr (EB == 1) {
+    uint32_t wv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      wv[k] = dval[4 * k] | dval[4 * k + 1] << 8 | dval[4 * k + 2] << 16 | dval[4 * k + 3] << 24;
+    *reinterpret_cast<v4i*>(vout) = v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+  } else {
+    uint32_t wv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) wv[k] = dval[2 * k] | dval[2 * k + 1] << 16;
+    *reinterpret_cast<v4i*>(vout) = v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+    *reinterpret_cast<v4i*>(vout + 16) = v4i{(int)wv[4], (int)wv[5], (int)wv[6], (int)wv[7]};
+  }
+  *reinterpret_cast<uint32_t*>(dm + blk * gd.mblk + (int64_t)rr * gd.MR + 4 * j) = dpos;
+}
+
+}  // namespace
+
+bool repack24_supported(const Geometry& g) {
+  return g.w != 0 && ((g.M == 4 && g.N == 1) || (g.M == 8 && g.N <= 2));
+}
+
+hipError_t launch_repack24(const Geometry& gs, const uint8_t* values, const uint8_t* meta, const Geometry& gd,
+                           uint8_t* dvalues, uint8_t* dmeta, hipStream_t s) {
+  if (!repack24_supported(gs) || gd.N != 2 || gd.M != 4 || gd.eb != gs.eb || gd.nRB != gs.nRB ||
+      gd.nKB != gs.nKB)
+    return hipErrorInvalidValue;
+  const int64_t total = gs.nRB * 16 * gs.nKB * (128 / gs.eb / 32);
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+#define NM_REPACK(E_, M_, N_)                                                                            \
+  if (gs.eb == E_ && gs.M == M_ && gs.N == N_) {                                                         \
+    hipLaunchKernelGGL((repack24_kernel<E_, M_, N_>), grid, block, 0, s, gs, values, meta, gd, dvalues, dmeta); \
+    return hipGetLastError();                                                                            \
+  }
+  NM_REPACK(1, 4, 1) NM_REPACK(1, 8, 1) NM_REPACK(1, 8, 2) NM_REPACK(2, 4, 1) NM_REPACK(2, 8, 1) NM_REPACK(2, 8, 2)
+#undef NM_REPACK
+  return hipErrorInvalidValue;
+}
+
+}  // namespace nm

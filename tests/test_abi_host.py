@@ -223,7 +223,8 @@ def test_activation_validation_and_variant_choice():
     assert va(fc1, 12608, nm.NM_I8, 1) == "smfmac_i8_2of4_persistent"
     assert va(_desc(R=2304, K=768), 12608, nm.NM_I8, 1) == "smfmac_i8_2of4_persistent_w8"
     deep = _desc(R=3072, K=3072, N=1, M=4)
-    assert va(deep, 12608, nm.NM_I8, 1) == "expand_mfma_persistent"
+    assert va(deep, 12608, nm.NM_I8, 1) == "repack24_smfmac_i8_2of4_persistent"
+    assert va(_desc(R=3072, K=3072, N=4, M=8), 12608, nm.NM_I8, 1) == "expand_mfma_persistent"
     assert va(fc1, 12608, nm.NM_I32, 1) == "invalid"
     assert va(fc1, 12608, nm.NM_I8, 7) == "invalid"
     assert L.nm_spmm_variant(ctypes.byref(fc1), 12608, nm.NM_I8).decode() == va(fc1, 12608, nm.NM_I8, 0)
@@ -264,3 +265,39 @@ def test_int8_workgroup_size_choice():
     assert v(2304, 768, 12608) == "smfmac_i8_2of4_persistent_w8"     # QKV: 891
     assert v(768, 3072, 12608) == "smfmac_i8_2of4_persistent_w8"     # FC2: 297
     assert v(768, 768, 12608) == "smfmac_i8_2of4_persistent_w8"      # proj: 297
+
+
+@pytest.mark.parametrize("N,M", [(1, 4), (1, 8), (2, 8)])
+def test_repack24_choice_and_workspace(monkeypatch, N, M):
+    """1:4, 1:8 and 2:8 int8 products large enough (R K T >= 2^31) run
+    re-packed to 2:4 on the sparse-MFMA tile kernels and ask for the 2:4
+    copy's workspace; small products, fp16 weights (unless forced), N:M
+    outside 2:4 and a forced N:M kernel do not."""
+    monkeypatch.delenv("NM_SPMM_VARIANT", raising=False)
+    monkeypatch.delenv("NM_SPMM_KSPLIT", raising=False)
+    L = nm.lib()
+
+    def q(d, T, ydt):
+        n = ctypes.c_size_t()
+        assert L.nm_spmm_workspace_size(ctypes.byref(d), T, ydt, ctypes.byref(n)) == nm.NM_OK
+        return L.nm_spmm_variant(ctypes.byref(d), T, ydt).decode(), n.value, \
+            L.nm_spmm_ksplit(ctypes.byref(d), T, ydt, 0)
+
+    def copy_bytes(R, K, dt):
+        vb, mb = nm.pack_size(R, K, 2, 4, dt)
+        return (vb + 255) // 256 * 256 + mb
+
+    fc1 = _desc(R=3072, K=768, N=N, M=M)
+    assert q(fc1, 12608, nm.NM_I8) == ("repack24_smfmac_i8_2of4_persistent", copy_bytes(3072, 768, nm.NM_I8), 1)
+    fc2 = _desc(R=768, K=3072, N=N, M=M)
+    assert q(fc2, 12608, nm.NM_I8) == ("repack24_smfmac_i8_2of4_persistent_w8", copy_bytes(768, 3072, nm.NM_I8), 1)
+    h = _desc(R=3072, K=768, N=N, M=M, dt=nm.NM_F16)
+    assert q(h, 3136, nm.NM_F16)[:2] == ("expand_mfma_persistent", 0)         # fp16: not by default
+    assert q(fc1, 256, nm.NM_I8)[:2] == ("expand_mfma_persistent", 0)        # R K T < 2^31
+    assert q(fc1, 16, nm.NM_I8)[:2] == ("expand_mfma_decode", 0)
+    monkeypatch.setenv("NM_SPMM_VARIANT", "expand_mfma_persistent")
+    assert q(fc1, 12608, nm.NM_I8)[:2] == ("expand_mfma_persistent", 0)
+    monkeypatch.setenv("NM_SPMM_VARIANT", "repack24_smfmac_i8_2of4_persistent")
+    assert q(fc1, 256, nm.NM_I8)[:2] == ("repack24_smfmac_i8_2of4_persistent", copy_bytes(3072, 768, nm.NM_I8))
+    monkeypatch.setenv("NM_SPMM_VARIANT", "repack24_smfmac_h_2of4_persistent")
+    assert q(h, 3136, nm.NM_F16) == ("repack24_smfmac_h_2of4_persistent", copy_bytes(3072, 768, nm.NM_F16), 1)

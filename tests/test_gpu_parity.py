@@ -283,6 +283,95 @@ def test_expand_variant_more_shapes(force_variant, variant, dt, out, N, M, R, K,
     _expand_case(force_variant, variant, dt, out, N, M, R, K, T, 12)
 
 
+# 1:4, 1:8 and 2:8 weights re-packed to 2:4 in the workspace, then multiplied
+# by the 2:4 sparse-MFMA tile kernels
+REPACK_NMS = [(1, 4), (1, 8), (2, 8)]
+REPACK_CASES = [("smfmac_i8_2of4_persistent", "i8", "i8"), ("smfmac_i8_2of4_persistent", "i8", "i32"),
+                ("smfmac_i8_2of4_persistent_w8", "i8", "i8"), ("smfmac_h_2of4_persistent", "f16", "f16"),
+                ("smfmac_h_2of4_persistent", "bf16", "f32"), ("smfmac_h_2of4_persistent_w8", "bf16", "bf16")]
+
+
+@pytest.mark.parametrize("inner,dt,out", REPACK_CASES)
+@pytest.mark.parametrize("N,M", REPACK_NMS)
+@pytest.mark.parametrize("R,K,T", [(300, 192, 144), (17, 8, 16), (259, 1288, 272), (520, 776, 400)])
+def test_repack24_variants(force_variant, inner, dt, out, N, M, R, K, T):
+    """The re-packed path forced on ragged rows, partial column blocks,
+    several token tiles and padded row strides: the result of the N:M
+    product, element by element."""
+    _expand_case(force_variant, "repack24_" + inner, dt, out, N, M, R, K, T, 13)
+
+
+@pytest.mark.parametrize("dt", ["i8", "f16", "bf16"])
+@pytest.mark.parametrize("N,M", REPACK_NMS)
+@pytest.mark.parametrize("R,K", [(17, 96), (40, 264), (33, 520)])
+def test_repack24_copy_describes_the_same_matrix(force_variant, dt, N, M, R, K):
+    """The 2:4 copy in the workspace, decoded by the oracle, describes bit
+    for bit the dense matrix the N:M packing describes (zeros, -0.0 and
+    magnitude ties included), with two distinct ascending positions per
+    group of four and padding slots as the packed format prescribes."""
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    from tests._parity import TORCH_DT, dev
+    inner = "smfmac_i8_2of4_persistent" if dt == "i8" else "smfmac_h_2of4_persistent"
+    out = {"i8": "i32", "f16": "f16", "bf16": "bf16"}[dt]
+    force_variant("repack24_" + inner)
+    T = 16
+    if dt == "i8":
+        W = nm_inputs.uniform_int8((R, K), 2, "repack", dt, N, M, R, lo=-3, hi=3)
+        W[0, :M] = -128
+    else:
+        W = nm_inputs.normal((R, K), 0.02, dt, 2, "repack", N, M, R)
+        W[1, :M] = 0
+        if dt == "f16":
+            W[2, :M] = np.float16(-0.0)
+    p = nm.pack(dev(W, dt), N, M)
+    assert nm.variant(p, T, TORCH_DT[out]) == "repack24_" + inner
+    need = nm.workspace_size(p, T, TORCH_DT[out])
+    vb, mb = nm.pack_size(R, K, 2, 4, {"i8": nm.NM_I8, "f16": nm.NM_F16, "bf16": nm.NM_BF16}[dt])
+    moff = (vb + 255) // 256 * 256
+    assert need == moff + mb
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
+    X = torch.zeros((K, T), dtype=TORCH_DT[dt], device="cuda")
+    nm.spmm(p, X, out_dtype=TORCH_DT[out], workspace=ws)
+    torch.cuda.synchronize()
+    h = ws.cpu().numpy()
+    v24, m24 = h[:vb], h[moff:moff + mb]
+    vals, idx = oracle.read_packed(v24, m24, R, K, 2, 4, dt)
+    assert np.all(idx[:, :, 0] < idx[:, :, 1])
+    bits = np.uint8 if dt == "i8" else np.uint16
+    cv, ci = oracle.compress(W, N, M, dt)
+    want = oracle.decompress(cv, ci, R, K, N, M, dt)
+    got = oracle.decompress(vals, idx, R, K, 2, 4, dt)
+    assert np.array_equal(got.view(bits), want.view(bits))
+    assert oracle.check_padding(v24, m24, R, K, 2, 4, dt) == 0
+
+
+def test_repack24_small_workspace_runs_the_nm_kernel():
+    """Given less workspace than the 2:4 copy needs, the call runs the N:M
+    kernel instead, with the same result (int8: bit-exact)."""
+    import ctypes
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    R, K, T, N, M = 3072, 768, 1024, 1, 4
+    W, X, b, s = _inputs("i8", "i8", R, K, T, N, M, 14, "repack-small-ws")
+    p = nm.pack(torch.from_numpy(W).cuda(), N, M)
+    assert nm.variant(p, T, torch.int8) == "repack24_smfmac_i8_2of4_persistent_w8"
+    need = nm.workspace_size(p, T, torch.int8)
+    assert need > 0
+    Xd = torch.from_numpy(X).cuda()
+    bd, sd = torch.from_numpy(b).cuda(), torch.from_numpy(s).cuda()
+    ref = reference(W, X, N, M, "i8", "i8", bias=b, scale=s)
+    small = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    for ws, wsb in ((None, 0), (small, need - 1)):
+        Y = torch.full((R, T), 5, dtype=torch.int8, device="cuda")
+        d = p.desc()
+        st = nm.lib().nm_spmm(ctypes.byref(d), Xd.data_ptr(), T, T, Y.data_ptr(), T, nm.NM_I8, bd.data_ptr(),
+                              sd.data_ptr(), None if ws is None else ws.data_ptr(), wsb, None)
+        assert st == nm.NM_OK
+        torch.cuda.synchronize()
+        compare(Y.cpu().numpy(), ref, "i8", "small workspace")
+
+
 def _expand_decode_case(force_variant, dt, out, N, M, R, K, T, seed):
     import semi_structured_sparse_nm_amd as nm
     from tests._parity import TORCH_DT, dev
