@@ -526,6 +526,16 @@ def _gelu_case(force_variant, variant, dt, out, N, M, R, K, T, seed, S=None, for
     assert np.all(Y[:, T:] == want), "writes beyond T"
 
 
+@pytest.mark.parametrize("inner,dt,out", [("smfmac_i8_2of4_persistent", "i8", "i8"),
+                                          ("smfmac_i8_2of4_persistent_w8", "i8", "i8"),
+                                          ("smfmac_h_2of4_persistent", "f16", "f16")])
+@pytest.mark.parametrize("N,M", [(1, 4), (2, 8)])
+@pytest.mark.parametrize("R,K,T", [(300, 192, 144), (259, 1288, 272)])
+def test_gelu_repack24(force_variant, inner, dt, out, N, M, R, K, T):
+    """GELU fused into the re-packed path (the 2:4 kernel's epilogue)."""
+    _gelu_case(force_variant, "repack24_" + inner, dt, out, N, M, R, K, T, 33)
+
+
 GELU_FP = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")]
 GELU_SHAPES = [(300, 192, 144), (259, 1280, 272)]
 
