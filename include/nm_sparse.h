@@ -119,7 +119,7 @@ nm_status nm_pack(const void* W, int64_t ldw, nm_packed* desc, void* stream);
  * second kernel on the same stream adds in slice order before the epilogue.
  * The split is a function of the shape and the device (nm_spmm_ksplit), so
  * the size is too.  For a 1:4, 1:8 or 2:8 int8 weight with a large product
- * (R K T >= 2^31, [K][T] layout) it instead holds a copy of the weight re-packed
+ * (R K T >= 2^31; either operand layout) it instead holds a copy of the weight re-packed
  * into the 2:4 layout (such a pattern is also a 2:4 pattern), which the 2:4
  * sparse-MFMA kernels then multiply: the 2:4 values_bytes rounded up to 256,
  * then the 2:4 meta_bytes.  Given less than that (or a workspace not 256-byte

@@ -303,9 +303,11 @@ size_t workspace_for(Variant v, const Call& c) {
 // 1:4 QKV 33.5 -> 28.1, proj 17.9 -> 17.1, FC1 39.1 -> 35.2, FC2 50.5 ->
 // 37.9; 2:8 QKV 35.4 -> 27.9, proj 18.6 -> 17.2, FC1 43.2 -> 35.1, FC2 55.2
 // -> 38.7.  For fp16 / bf16 it did not pay (Swin-T 1:4: from 4% faster to
-// 24% slower), so it is taken for int8 weights only, in the [K][T] layout,
-// when the product is large enough for the extra launch (R K T >= 2^31) and
-// the 2:4 kernel would run without a K split.
+// 24% slower), so it is taken for int8 weights only, when the product is
+// large enough for the extra launch (R K T >= 2^31) and the 2:4 kernel would
+// run without a K split: in the [K][T] layout in place of the dense-expand
+// kernel, in the [T][K] layout (its int8 2:4 kernel) in place of the generic
+// one.
 // NM_SPMM_VARIANT=repack24_<2:4 tile variant> forces it (fp16 / bf16 too)
 // where the 2:4 kernel's requirements hold.
 constexpr double kRepackMinWork = 2147483648.0;
@@ -321,18 +323,18 @@ size_t repack_meta_off(const Geometry& g24) { return (g24.values_bytes() + 255) 
 size_t repack_bytes(const Geometry& g24) { return repack_meta_off(g24) + g24.meta_bytes(); }
 
 bool repack_inner(Variant v) {
-  return v == V_SMFMAC_I8P || v == V_SMFMAC_I8P8 || v == V_SMFMAC_H || v == V_SMFMAC_H8;
+  return v == V_SMFMAC_I8P || v == V_SMFMAC_I8P8 || v == V_SMFMAC_H || v == V_SMFMAC_H8 || v == V_SMFMAC_I8TK;
 }
 
 Plan plan_for(const Call& c) {
   Plan p;
   p.v = choose(c);
-  if (!nm::repack24_supported(*c.g) || c.layout != NM_LAYOUT_KT) return p;
+  if (!nm::repack24_supported(*c.g)) return p;
   const char* force = getenv("NM_SPMM_VARIANT");
   const bool forced = force && *force;
   const bool forced_rp = forced && strncmp(force, kRepackPrefix, strlen(kRepackPrefix)) == 0;
   if (forced && !forced_rp) return p;
-  if (!forced_rp && (c.wdt != NM_I8 || p.v != V_EXPAND ||
+  if (!forced_rp && (c.wdt != NM_I8 || (p.v != V_EXPAND && p.v != V_GENERIC) ||
                      (double)c.g->R * (double)c.g->K * (double)c.T < kRepackMinWork))
     return p;
   const Geometry g24 = Geometry::make(c.g->R, c.g->K, 2, 4, c.g->eb);
@@ -362,6 +364,7 @@ const char* plan_name(const Plan& p) {
     case V_SMFMAC_I8P8: return "repack24_smfmac_i8_2of4_persistent_w8";
     case V_SMFMAC_H: return "repack24_smfmac_h_2of4_persistent";
     case V_SMFMAC_H8: return "repack24_smfmac_h_2of4_persistent_w8";
+    case V_SMFMAC_I8TK: return "repack24_smfmac_i8_2of4_tk";
     default: return "invalid";
   }
 }
@@ -415,8 +418,10 @@ nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype,
     if (n > need) need = n;
   }
   for (int act = NM_ACT_NONE; act <= NM_ACT_GELU; ++act) {
-    const Plan p = plan_for(make_call(g, w->dtype, y_dtype, T, T, T, al, al, act));
-    if (p.repack && repack_bytes(p.g24) > need) need = repack_bytes(p.g24);
+    const Plan kt = plan_for(make_call(g, w->dtype, y_dtype, T, T, T, al, al, act));
+    const Plan tk = plan_for(make_call(g, w->dtype, y_dtype, T, g.K, g.R, al, al, act, NM_LAYOUT_TK));
+    if (kt.repack && repack_bytes(kt.g24) > need) need = repack_bytes(kt.g24);
+    if (tk.repack && repack_bytes(tk.g24) > need) need = repack_bytes(tk.g24);
   }
   *bytes = need;
   return NM_OK;
@@ -583,7 +588,7 @@ const char* nm_spmm_variant_tk(const nm_packed* w, int64_t T, int32_t y_dtype, i
   if (check_desc(w, &g) != NM_OK || T < 1 || !pair_supported(w->dtype, y_dtype)) return "invalid";
   if ((act != NM_ACT_NONE && act != NM_ACT_GELU) || (act != NM_ACT_NONE && y_dtype == NM_I32)) return "invalid";
   const void* al = reinterpret_cast<const void*>((uintptr_t)256);
-  return variant_name(choose(make_call(g, w->dtype, y_dtype, T, g.K, g.R, al, al, act, NM_LAYOUT_TK)));
+  return plan_name(plan_for(make_call(g, w->dtype, y_dtype, T, g.K, g.R, al, al, act, NM_LAYOUT_TK)));
 }
 
 int32_t nm_spmm_ksplit(const nm_packed* w, int64_t T, int32_t y_dtype, int32_t act) {

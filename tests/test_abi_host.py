@@ -295,6 +295,9 @@ def test_repack24_choice_and_workspace(monkeypatch, N, M):
     assert q(h, 3136, nm.NM_F16)[:2] == ("expand_mfma_persistent", 0)         # fp16: not by default
     assert q(fc1, 256, nm.NM_I8)[:2] == ("expand_mfma_persistent", 0)        # R K T < 2^31
     assert q(fc1, 16, nm.NM_I8)[:2] == ("expand_mfma_decode", 0)
+    tk = lambda d, T: L.nm_spmm_variant_tk(ctypes.byref(d), T, nm.NM_I8, 0).decode()
+    assert tk(fc1, 12608) == "repack24_smfmac_i8_2of4_tk"
+    assert tk(fc1, 256) == "generic_dense_expand"
     monkeypatch.setenv("NM_SPMM_VARIANT", "expand_mfma_persistent")
     assert q(fc1, 12608, nm.NM_I8)[:2] == ("expand_mfma_persistent", 0)
     monkeypatch.setenv("NM_SPMM_VARIANT", "repack24_smfmac_i8_2of4_persistent")

@@ -722,3 +722,18 @@ def test_tk_fast_i8(force_variant, out, R, K, T):
 def test_tk_fast_i8_gelu(force_variant):
     force_variant("smfmac_i8_2of4_tk")
     _tk_case("i8", "i8", 2, 4, 528, 768, 400, 44, act="gelu", xpad=16, variant="smfmac_i8_2of4_tk")
+
+
+@pytest.mark.parametrize("out", ["i8", "i32"])
+@pytest.mark.parametrize("N,M", [(1, 4), (1, 8), (2, 8)])
+@pytest.mark.parametrize("R,K,T", [(256, 192, 144), (528, 1288, 272), (304, 200, 37)])
+def test_tk_repack24(force_variant, out, N, M, R, K, T):
+    """1:4, 1:8 and 2:8 int8 in the [T][K] layout, re-packed to 2:4 in the
+    workspace and multiplied by the layout's int8 2:4 kernel."""
+    force_variant("repack24_smfmac_i8_2of4_tk")
+    _tk_case("i8", out, N, M, R, K, T, 45, xpad=(-K) % 16 + 16, variant="repack24_smfmac_i8_2of4_tk")
+
+
+def test_tk_repack24_gelu(force_variant):
+    force_variant("repack24_smfmac_i8_2of4_tk")
+    _tk_case("i8", "i8", 1, 4, 528, 768, 400, 46, act="gelu", xpad=16, variant="repack24_smfmac_i8_2of4_tk")
