@@ -593,7 +593,7 @@ def main():
         Xi = X0.t().contiguous() if tk else X0.clone()
         Yi = torch.empty((L.T, L.R) if tk else (L.R, L.T), dtype=odt, device=dev)
         sets.append((ps, Xi, Yi))
-    need = nm.workspace_size(p, L.T, odt)
+    need = nm.workspace_size_tk(p, L.T, odt) if args.layout == "tk" else nm.workspace_size(p, L.T, odt)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     variant = nm.variant_tk(p, L.T, odt) if args.layout == "tk" else nm.variant(p, L.T, odt)
 

@@ -124,11 +124,23 @@ nm_status nm_pack(const void* W, int64_t ldw, nm_packed* desc, void* stream);
  * sparse-MFMA kernels then multiply: the 2:4 values_bytes rounded up to 256,
  * then the 2:4 meta_bytes.  Given less than that (or a workspace not 256-byte
  * aligned), nm_spmm runs the N:M kernel instead, with the same result.
+ * (nm_spmm_tk sizes its workspace with nm_spmm_tk_workspace_size.)
  * The caller owns the buffer; nm_spmm only writes it and
  * reads it back within the call's stream order, so calls that share one
  * workspace must be ordered on one stream.
  */
 nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype, size_t* bytes);
+
+/*
+ * The same for nm_spmm_tk (the [T][K] layout).  Besides the needs above (a
+ * 2:4 re-pack for the layout's int8 2:4 kernel), a large call (R K T >=
+ * 2^26) whose operands no [T][K] kernel takes runs through the [K][T]
+ * kernels: its workspace then holds X transposed to [K][T'] (T' = T rounded
+ * up to 16, each part 256-byte aligned), the [K][T'] product before its
+ * transpose into Y, and that product's K-split partials if any.  Given less,
+ * the call runs the generic kernel instead, with the same result.
+ */
+nm_status nm_spmm_tk_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype, size_t* bytes);
 
 /*
  * Y = epilogue(acc), acc[r][t] = sum over kept slots (r, k) of W[r][k] X[k][t].
@@ -197,7 +209,8 @@ const char* nm_status_str(nm_status s);
  * Name of the kernel variant nm_spmm would launch for these arguments
  * (static string; "invalid" when the arguments would be rejected).  A 1:4,
  * 1:8 or 2:8 product re-packed to 2:4 in the workspace is named
- * "repack24_" + the 2:4 kernel's name (assuming the workspace
+ * "repack24_" + the 2:4 kernel's name, a [T][K] call run through the [K][T]
+ * kernels "transpose_" + that kernel's name (assuming the workspace
  * nm_spmm_workspace_size asks for).  For tests and profiling; launches
  * nothing.
  */

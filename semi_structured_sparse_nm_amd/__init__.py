@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
         L.nm_pack_size.argtypes = [I64, I64, I32, I32, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
         L.nm_pack.argtypes = [P, I64, PP, P]
         L.nm_spmm_workspace_size.argtypes = [PP, I64, I32, ctypes.POINTER(SZ)]
+        L.nm_spmm_tk_workspace_size.argtypes = [PP, I64, I32, ctypes.POINTER(SZ)]
         L.nm_spmm.argtypes = [PP, P, I64, I64, P, I64, I32, P, P, P, SZ, P]
         L.nm_status_str.argtypes = [ctypes.c_int]
         L.nm_status_str.restype = ctypes.c_char_p
@@ -162,6 +163,15 @@ def workspace_size(p: Packed, T: int, out_dtype: torch.dtype) -> int:
     return n.value
 
 
+def workspace_size_tk(p: Packed, T: int, out_dtype: torch.dtype) -> int:
+    """nm_spmm_tk_workspace_size: the workspace linear() needs."""
+    n = ctypes.c_size_t()
+    d = p.desc()
+    _check(lib().nm_spmm_tk_workspace_size(ctypes.byref(d), T, _TORCH_TO_NM[out_dtype], ctypes.byref(n)),
+           "nm_spmm_tk_workspace_size")
+    return n.value
+
+
 ACTS = {"none": 0, "gelu": 1}
 
 
@@ -229,7 +239,7 @@ def linear(p: Packed, Xt: torch.Tensor, bias: torch.Tensor | None = None,
         out = torch.empty((T, p.rows), dtype=out_dtype, device=Xt.device)
     if out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (T, p.rows):
         raise ValueError("out must be [T, R] with unit stride along R")
-    need = workspace_size(p, T, out_dtype)
+    need = workspace_size_tk(p, T, out_dtype)
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=Xt.device)
     d = p.desc()

@@ -1,5 +1,6 @@
 // C ABI of the library (include/nm_sparse.h): host-side validation, kernel
 // variant choice per shape, launches.  Stateless and thread-safe.
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -317,6 +318,9 @@ struct Plan {
   Variant v = V_INVALID;
   bool repack = false;
   Geometry g24;              // the 2:4 geometry of the re-packed copy
+  bool transpose = false;    // [T][K] call run as transpose, [K][T] product, transpose
+  int64_t Tp = 0;            // tokens of the [K][T] product (T rounded up to 16)
+  int S = 1;                 // K slices of the [K][T] product
 };
 
 size_t repack_meta_off(const Geometry& g24) { return (g24.values_bytes() + 255) / 256 * 256; }
@@ -326,38 +330,100 @@ bool repack_inner(Variant v) {
   return v == V_SMFMAC_I8P || v == V_SMFMAC_I8P8 || v == V_SMFMAC_H || v == V_SMFMAC_H8 || v == V_SMFMAC_I8TK;
 }
 
+// ---- [T][K] calls without a kernel of their own.  The generic kernel takes
+// every shape in that layout but is slow at scale (about 1 ms on ViT-B
+// shapes), so a large [T][K] call it would get runs as three launches in
+// the caller's workspace instead: X [T][K] transposed into X' [K][T'] (T'
+// = T rounded up to 16, extra tokens zero), the [K][T] product Y' [R][T']
+// with the kernel that layout picks (epilogue included), and Y' transposed
+// into Y [T][R] (nm_transpose.hip).  Taken when R K T >= 2^26.
+// NM_SPMM_VARIANT=transpose_<[K][T] variant> forces it.
+constexpr double kTransposeMinWork = 67108864.0;
+constexpr const char* kTransposePrefix = "transpose_";
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+size_t xkt_bytes(const Geometry& g, int64_t Tp) { return round256((size_t)g.K * Tp * g.eb); }
+size_t ykt_bytes(const Geometry& g, int64_t Tp, int ydt) { return round256((size_t)g.R * Tp * nm::dtype_bytes(ydt)); }
+
+Call transposed_call(const Call& c, int64_t Tp) {
+  const void* al = reinterpret_cast<const void*>((uintptr_t)256);
+  return make_call(*c.g, c.wdt, c.ydt, Tp, Tp, Tp, al, al, c.act, NM_LAYOUT_KT);
+}
+
+size_t plan_workspace(const Plan& p, const Call& c) {
+  if (p.repack) return repack_bytes(p.g24);
+  if (p.transpose)
+    return xkt_bytes(*c.g, p.Tp) + ykt_bytes(*c.g, p.Tp, c.ydt) + (p.S > 1 ? (size_t)p.S * c.g->R * p.Tp * 4 : 0);
+  return workspace_for(p.v, c);
+}
+
 Plan plan_for(const Call& c) {
   Plan p;
   p.v = choose(c);
-  if (!nm::repack24_supported(*c.g)) return p;
   const char* force = getenv("NM_SPMM_VARIANT");
   const bool forced = force && *force;
   const bool forced_rp = forced && strncmp(force, kRepackPrefix, strlen(kRepackPrefix)) == 0;
-  if (forced && !forced_rp) return p;
-  if (!forced_rp && (c.wdt != NM_I8 || (p.v != V_EXPAND && p.v != V_GENERIC) ||
-                     (double)c.g->R * (double)c.g->K * (double)c.T < kRepackMinWork))
-    return p;
-  const Geometry g24 = Geometry::make(c.g->R, c.g->K, 2, 4, c.g->eb);
-  Call c24 = c;
-  c24.g = &g24;
-  Variant inner = V_INVALID;
-  if (forced_rp) {
-    const char* name = force + strlen(kRepackPrefix);
-    for (int v = V_GENERIC; v < V_COUNT; ++v)
-      if (repack_inner((Variant)v) && strcmp(name, variant_name((Variant)v)) == 0 && eligible((Variant)v, c24))
-        inner = (Variant)v;
-  } else {
-    inner = choose_auto(c24);
+  const bool forced_tr = forced && strncmp(force, kTransposePrefix, strlen(kTransposePrefix)) == 0;
+  const double work = (double)c.g->R * (double)c.g->K * (double)c.T;
+
+  // 2:4 re-pack
+  if (nm::repack24_supported(*c.g) && (!forced || forced_rp) &&
+      (forced_rp || (c.wdt == NM_I8 && (p.v == V_EXPAND || p.v == V_GENERIC) && work >= kRepackMinWork))) {
+    const Geometry g24 = Geometry::make(c.g->R, c.g->K, 2, 4, c.g->eb);
+    Call c24 = c;
+    c24.g = &g24;
+    Variant inner = V_INVALID;
+    if (forced_rp) {
+      const char* name = force + strlen(kRepackPrefix);
+      for (int v = V_GENERIC; v < V_COUNT; ++v)
+        if (repack_inner((Variant)v) && strcmp(name, variant_name((Variant)v)) == 0 && eligible((Variant)v, c24))
+          inner = (Variant)v;
+    } else {
+      inner = choose_auto(c24);
+    }
+    // a forced re-pack runs the 2:4 kernel unsplit
+    if (repack_inner(inner) && (forced_rp || ksplit_for(inner, c24) == 1)) {
+      p.v = inner;
+      p.repack = true;
+      p.g24 = g24;
+      return p;
+    }
   }
-  // a forced re-pack runs the 2:4 kernel unsplit
-  if (!repack_inner(inner) || (!forced_rp && ksplit_for(inner, c24) != 1)) return p;
-  p.v = inner;
-  p.repack = true;
-  p.g24 = g24;
+
+  // [T][K] through the [K][T] kernels
+  if (c.layout == NM_LAYOUT_TK && (!forced || forced_tr) &&
+      (forced_tr || (p.v == V_GENERIC && work >= kTransposeMinWork))) {
+    const int64_t Tp = (c.T + 15) / 16 * 16;
+    const Call ckt = transposed_call(c, Tp);
+    Variant inner = V_INVALID;
+    if (forced_tr) {
+      const char* name = force + strlen(kTransposePrefix);
+      for (int v = V_GENERIC + 1; v < V_COUNT; ++v)
+        if (strcmp(name, variant_name((Variant)v)) == 0 && eligible((Variant)v, ckt)) inner = (Variant)v;
+    } else {
+      inner = choose_auto(ckt);
+    }
+    if (inner != V_INVALID && inner != V_GENERIC) {
+      p.v = inner;
+      p.transpose = true;
+      p.Tp = Tp;
+      p.S = ksplit_for(inner, ckt);
+    }
+  }
   return p;
 }
 
 const char* plan_name(const Plan& p) {
+  if (p.transpose) {
+    static char names[V_COUNT][96];
+    static const bool init = [] {
+      for (int v = 0; v < V_COUNT; ++v)
+        snprintf(names[v], sizeof names[v], "%s%s", kTransposePrefix, variant_name((Variant)v));
+      return true;
+    }();
+    (void)init;
+    return names[p.v];
+  }
   if (!p.repack) return variant_name(p.v);
   switch (p.v) {
     case V_SMFMAC_I8P: return "repack24_smfmac_i8_2of4_persistent";
@@ -418,10 +484,27 @@ nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype,
     if (n > need) need = n;
   }
   for (int act = NM_ACT_NONE; act <= NM_ACT_GELU; ++act) {
-    const Plan kt = plan_for(make_call(g, w->dtype, y_dtype, T, T, T, al, al, act));
-    const Plan tk = plan_for(make_call(g, w->dtype, y_dtype, T, g.K, g.R, al, al, act, NM_LAYOUT_TK));
-    if (kt.repack && repack_bytes(kt.g24) > need) need = repack_bytes(kt.g24);
-    if (tk.repack && repack_bytes(tk.g24) > need) need = repack_bytes(tk.g24);
+    const Call lc = make_call(g, w->dtype, y_dtype, T, T, T, al, al, act);
+    const size_t n = plan_workspace(plan_for(lc), lc);
+    if (n > need) need = n;
+  }
+  *bytes = need;
+  return NM_OK;
+}
+
+nm_status nm_spmm_tk_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype, size_t* bytes) {
+  if (!bytes) return NM_EINVAL;
+  Geometry g;
+  nm_status st = check_desc(w, &g);
+  if (st != NM_OK) return st;
+  if (T < 1) return NM_EINVAL;
+  if (!pair_supported(w->dtype, y_dtype)) return NM_EUNSUPPORTED;
+  const void* al = reinterpret_cast<const void*>((uintptr_t)256);
+  size_t need = 0;
+  for (int act = NM_ACT_NONE; act <= NM_ACT_GELU; ++act) {
+    const Call lc = make_call(g, w->dtype, y_dtype, T, g.K, g.R, al, al, act, NM_LAYOUT_TK);
+    const size_t n = plan_workspace(plan_for(lc), lc);
+    if (n > need) need = n;
   }
   *bytes = need;
   return NM_OK;
@@ -430,6 +513,53 @@ nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype,
 }  // extern "C"
 
 namespace {
+
+// One [K][T]-or-[T][K] product with variant v: K split into S slices (raw
+// partial sums at `part`, then the reduction applies a's epilogue) or one
+// launch.
+nm_status run_variant(Variant v, int S, const SpmmArgs& a, void* part, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (S > 1) {
+    // K slices write raw 32-bit partial sums to the workspace; the reduction
+    // adds them and applies this call's epilogue
+    SpmmArgs p = a;
+    p.ydt = a.wdt == NM_I8 ? NM_I32 : NM_F32;
+    p.Y = part;
+    p.ldy = a.T;
+    p.bias = nullptr;
+    p.scale = nullptr;
+    p.act = NM_ACT_NONE;
+    p.ksplit = S;
+    p.kbs = (int)(a.g.nKB / S);
+    p.ys = a.g.R * a.T;
+    e = v == V_SMFMAC_H    ? nm::launch_spmm_smfmac_h(p, s)
+        : v == V_SMFMAC_H8 ? nm::launch_spmm_smfmac_h8(p, s)
+                           : nm::launch_spmm_expand(p, s);
+    if (e != hipSuccess) return NM_EHIP;
+    SpmmArgs r = a;
+    r.ksplit = S;
+    r.ys = p.ys;
+    r.ws = part;
+    e = nm::launch_splitk_reduce(r, s);
+    return e == hipSuccess ? NM_OK : NM_EHIP;
+  }
+  switch (v) {
+    case V_GENERIC: e = nm::launch_spmm_generic(a, s); break;
+    case V_SMFMAC_I8: e = nm::launch_spmm_smfmac_i8(a, 0, s); break;
+    case V_SMFMAC_I8P: e = nm::launch_spmm_smfmac_i8p(a, 0, s); break;
+    case V_SMFMAC_I8P8: e = nm::launch_spmm_smfmac_i8p(a, 1, s); break;
+    case V_SMFMAC_H: e = nm::launch_spmm_smfmac_h(a, s); break;
+    case V_SMFMAC_H8: e = nm::launch_spmm_smfmac_h8(a, s); break;
+    case V_SMFMAC_HD: e = nm::launch_spmm_smfmac_hd(a, s); break;
+    case V_EXPAND: e = nm::launch_spmm_expand(a, s); break;
+    case V_EXPAND32: e = nm::launch_spmm_expand32(a, s); break;
+    case V_EXPAND_DECODE: e = nm::launch_spmm_expand_decode(a, s); break;
+    case V_SMFMAC_I8S: e = nm::launch_spmm_smfmac_i8s(a, s); break;
+    case V_SMFMAC_I8TK: e = nm::launch_spmm_smfmac_i8tk(a, s); break;
+    default: return NM_EINVAL;
+  }
+  return e == hipSuccess ? NM_OK : NM_EHIP;
+}
 
 nm_status spmm_call(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
                     int32_t y_dtype, const void* bias, const float* scale, int32_t act, float out_scale,
@@ -451,15 +581,17 @@ nm_status spmm_call(const nm_packed* w, const void* X, int64_t ldx, int64_t T, v
   if (scale && !aligned(scale, 4)) return NM_EUNSUPPORTED;
   const Call call = make_call(g, w->dtype, y_dtype, T, ldx, ldy, X, Y, act, layout);
   Plan pl = plan_for(call);
-  // a workspace too small (or not 256-byte aligned) for the 2:4 copy: the
-  // N:M kernel the plan would otherwise have used (same result)
-  if (pl.repack && (!workspace || workspace_bytes < repack_bytes(pl.g24) || !aligned(workspace, 256))) {
-    pl.repack = false;
+  // a workspace too small (or not 256-byte aligned) for the re-packed copy
+  // or the transposed operands: the kernel the plain choice gives (same
+  // result)
+  if ((pl.repack || pl.transpose) &&
+      (!workspace || workspace_bytes < plan_workspace(pl, call) || !aligned(workspace, 256))) {
+    pl = Plan();
     pl.v = choose(call);
   }
-  Variant v = pl.v;
-  const int S = pl.repack ? 1 : ksplit_for(v, call);
-  size_t need = pl.repack ? repack_bytes(pl.g24) : workspace_for(v, call);
+  const Variant v = pl.v;
+  const int S = pl.repack ? 1 : pl.transpose ? pl.S : ksplit_for(v, call);
+  const size_t need = plan_workspace(pl, call);
   if (workspace_bytes < need || (need && !workspace)) return NM_EINVAL;
   if (need && !aligned(workspace, 16)) return NM_EUNSUPPORTED;
 
@@ -495,44 +627,27 @@ nm_status spmm_call(const nm_packed* w, const void* X, int64_t ldx, int64_t T, v
     a.values = wv;
     a.meta = wm;
   }
-  if (S > 1) {
-    // K slices write raw 32-bit partial sums to the workspace; the reduction
-    // adds them and applies this call's epilogue
-    SpmmArgs p = a;
-    p.ydt = w->dtype == NM_I8 ? NM_I32 : NM_F32;
-    p.Y = workspace;
-    p.ldy = T;
-    p.bias = nullptr;
-    p.scale = nullptr;
-    p.act = NM_ACT_NONE;
-    p.ksplit = S;
-    p.kbs = (int)(g.nKB / S);
-    p.ys = g.R * T;
-    e = v == V_SMFMAC_H    ? nm::launch_spmm_smfmac_h(p, s)
-        : v == V_SMFMAC_H8 ? nm::launch_spmm_smfmac_h8(p, s)
-                           : nm::launch_spmm_expand(p, s);
+  if (pl.transpose) {
+    // X [T][K] -> X' [K][T'], the [K][T] product into Y' [R][T'], Y' -> Y [T][R]
+    uint8_t* xkt = static_cast<uint8_t*>(workspace);
+    uint8_t* ykt = xkt + xkt_bytes(g, pl.Tp);
+    void* part = ykt + ykt_bytes(g, pl.Tp, y_dtype);
+    e = nm::launch_transpose(X, T, g.K, ldx, xkt, pl.Tp, pl.Tp, g.eb, s);
     if (e != hipSuccess) return NM_EHIP;
-    a.ksplit = S;
-    a.ys = p.ys;
-    e = nm::launch_splitk_reduce(a, s);
+    SpmmArgs k = a;
+    k.X = xkt;
+    k.ldx = pl.Tp;
+    k.T = pl.Tp;
+    k.Y = ykt;
+    k.ldy = pl.Tp;
+    k.layout = NM_LAYOUT_KT;
+    k.ws = part;
+    const nm_status r = run_variant(v, S, k, part, s);
+    if (r != NM_OK) return r;
+    e = nm::launch_transpose(ykt, g.R, T, pl.Tp, Y, ldy, g.R, nm::dtype_bytes(y_dtype), s);
     return e == hipSuccess ? NM_OK : NM_EHIP;
   }
-  switch (v) {
-    case V_GENERIC: e = nm::launch_spmm_generic(a, s); break;
-    case V_SMFMAC_I8: e = nm::launch_spmm_smfmac_i8(a, 0, s); break;
-    case V_SMFMAC_I8P: e = nm::launch_spmm_smfmac_i8p(a, 0, s); break;
-    case V_SMFMAC_I8P8: e = nm::launch_spmm_smfmac_i8p(a, 1, s); break;
-    case V_SMFMAC_H: e = nm::launch_spmm_smfmac_h(a, s); break;
-    case V_SMFMAC_H8: e = nm::launch_spmm_smfmac_h8(a, s); break;
-    case V_SMFMAC_HD: e = nm::launch_spmm_smfmac_hd(a, s); break;
-    case V_EXPAND: e = nm::launch_spmm_expand(a, s); break;
-    case V_EXPAND32: e = nm::launch_spmm_expand32(a, s); break;
-    case V_EXPAND_DECODE: e = nm::launch_spmm_expand_decode(a, s); break;
-    case V_SMFMAC_I8S: e = nm::launch_spmm_smfmac_i8s(a, s); break;
-    case V_SMFMAC_I8TK: e = nm::launch_spmm_smfmac_i8tk(a, s); break;
-    default: return NM_EINVAL;
-  }
-  return e == hipSuccess ? NM_OK : NM_EHIP;
+  return run_variant(v, S, a, workspace, s);
 }
 
 }  // namespace

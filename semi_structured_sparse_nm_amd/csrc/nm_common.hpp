@@ -112,6 +112,10 @@ bool expand_supported(int N, int M);   // N:M instantiated by launch_spmm_expand
 bool repack24_supported(const Geometry& g);
 hipError_t launch_repack24(const Geometry& gs, const uint8_t* values, const uint8_t* meta, const Geometry& gd,
                            uint8_t* dvalues, uint8_t* dmeta, hipStream_t s);
+// dst[j][i] = src[i][j] (i < rows, j < cols), zeros for rows <= i < dst_cols;
+// elements of eb bytes, row pitches lds / ldd in elements.
+hipError_t launch_transpose(const void* src, int64_t rows, int64_t cols, int64_t lds, void* dst, int64_t ldd,
+                            int64_t dst_cols, int eb, hipStream_t s);
 // Y = epilogue(sum over the a.ksplit slices of the partials at a.ws) with
 // a's own output type, bias and scale (T a multiple of 4).
 hipError_t launch_splitk_reduce(const SpmmArgs& a, hipStream_t s);

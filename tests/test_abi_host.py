@@ -297,10 +297,40 @@ def test_repack24_choice_and_workspace(monkeypatch, N, M):
     assert q(fc1, 16, nm.NM_I8)[:2] == ("expand_mfma_decode", 0)
     tk = lambda d, T: L.nm_spmm_variant_tk(ctypes.byref(d), T, nm.NM_I8, 0).decode()
     assert tk(fc1, 12608) == "repack24_smfmac_i8_2of4_tk"
-    assert tk(fc1, 256) == "generic_dense_expand"
+    assert tk(fc1, 256) == "transpose_expand_mfma_persistent"               # below the re-pack size
     monkeypatch.setenv("NM_SPMM_VARIANT", "expand_mfma_persistent")
     assert q(fc1, 12608, nm.NM_I8)[:2] == ("expand_mfma_persistent", 0)
     monkeypatch.setenv("NM_SPMM_VARIANT", "repack24_smfmac_i8_2of4_persistent")
     assert q(fc1, 256, nm.NM_I8)[:2] == ("repack24_smfmac_i8_2of4_persistent", copy_bytes(3072, 768, nm.NM_I8))
     monkeypatch.setenv("NM_SPMM_VARIANT", "repack24_smfmac_h_2of4_persistent")
     assert q(h, 3136, nm.NM_F16) == ("repack24_smfmac_h_2of4_persistent", copy_bytes(3072, 768, nm.NM_F16), 1)
+
+
+def test_tk_transpose_choice_and_workspace(monkeypatch):
+    """Large [T][K] calls without a kernel of their own in that layout run
+    through the [K][T] kernels between two transposes, and ask for X', Y'
+    (and split partials) in the workspace; small ones stay on the generic
+    kernel."""
+    monkeypatch.delenv("NM_SPMM_VARIANT", raising=False)
+    monkeypatch.delenv("NM_SPMM_KSPLIT", raising=False)
+    L = nm.lib()
+    tk = lambda d, T, y: L.nm_spmm_variant_tk(ctypes.byref(d), T, y, 0).decode()
+
+    def ws(d, T, y):
+        n = ctypes.c_size_t()
+        assert L.nm_spmm_tk_workspace_size(ctypes.byref(d), T, y, ctypes.byref(n)) == nm.NM_OK
+        return n.value
+
+    r256 = lambda n: (n + 255) // 256 * 256
+    d48 = _desc(R=3072, K=768, N=4, M=8)
+    assert tk(d48, 12608, nm.NM_I8) == "transpose_expand_mfma_persistent"
+    assert ws(d48, 12608, nm.NM_I8) == r256(768 * 12608) + r256(3072 * 12608)
+    h = _desc(R=3072, K=768, dt=nm.NM_F16)
+    assert tk(h, 3137, nm.NM_F16) == "transpose_smfmac_h_2of4_persistent"
+    assert ws(h, 3137, nm.NM_F16) == r256(768 * 3152 * 2) + r256(3072 * 3152 * 2)
+    assert tk(_desc(R=192, K=192, N=4, M=8), 197, nm.NM_I32) == "generic_dense_expand"
+    assert tk(_desc(R=3072, K=768), 12608, nm.NM_I8) == "smfmac_i8_2of4_tk"
+    assert ws(_desc(R=3072, K=768), 12608, nm.NM_I8) == 0
+    assert _ws(d48, 12608, nm.NM_I8) == 0          # the [K][T] query: no transposes
+    monkeypatch.setenv("NM_SPMM_VARIANT", "generic_dense_expand")
+    assert tk(d48, 12608, nm.NM_I8) == "generic_dense_expand"

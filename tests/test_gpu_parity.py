@@ -734,6 +734,36 @@ def test_tk_repack24(force_variant, out, N, M, R, K, T):
     _tk_case("i8", out, N, M, R, K, T, 45, xpad=(-K) % 16 + 16, variant="repack24_smfmac_i8_2of4_tk")
 
 
+TRANSPOSE_CASES = [("expand_mfma_persistent", "i8", "i8", 4, 8), ("expand_mfma_persistent", "f16", "f16", 1, 4),
+                   ("expand_mfma_persistent", "bf16", "f32", 8, 8), ("smfmac_h_2of4_persistent", "f16", "f16", 2, 4),
+                   ("smfmac_h_2of4_persistent", "bf16", "bf16", 2, 4),
+                   ("smfmac_i8_2of4_persistent", "i8", "i32", 2, 4), ("smfmac_i8_2of4_persistent_w8", "i8", "i8", 2, 4)]
+
+
+@pytest.mark.parametrize("inner,dt,out,N,M", TRANSPOSE_CASES)
+@pytest.mark.parametrize("R,K,T", [(256, 192, 144), (304, 1288, 37), (520, 776, 400)])
+def test_tk_transpose(force_variant, inner, dt, out, N, M, R, K, T):
+    """[T][K] calls run as transpose, [K][T] product, transpose: every dtype
+    pair and several kernels, T not a multiple of 16 (zero tokens pad the
+    product), ragged rows and column blocks, padded strides; nothing written
+    past R."""
+    force_variant("transpose_" + inner)
+    _tk_case(dt, out, N, M, R, K, T, 47, xpad=(-K) % 16 + 16, variant="transpose_" + inner)
+
+
+def test_tk_transpose_decode(force_variant):
+    force_variant("transpose_smfmac_h_2of4_decode")
+    _tk_case("f16", "f16", 2, 4, 300, 1024, 7, 48, xpad=8, variant="transpose_smfmac_h_2of4_decode")
+
+
+def test_tk_transpose_gelu_and_ksplit(force_variant, force_ksplit):
+    import semi_structured_sparse_nm_amd as nm
+    force_variant("transpose_expand_mfma_persistent")
+    _tk_case("i8", "i8", 4, 8, 264, 1024, 144, 49, act="gelu", xpad=16, variant="transpose_expand_mfma_persistent")
+    force_ksplit(4)
+    _tk_case("f16", "f16", 1, 4, 264, 1024, 144, 50, xpad=16, variant="transpose_expand_mfma_persistent")
+
+
 def test_tk_repack24_gelu(force_variant):
     force_variant("repack24_smfmac_i8_2of4_tk")
     _tk_case("i8", "i8", 1, 4, 528, 768, 400, 46, act="gelu", xpad=16, variant="repack24_smfmac_i8_2of4_tk")
