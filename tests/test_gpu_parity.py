@@ -162,6 +162,41 @@ def test_full_size_sampled_rows(L):
     compare(np.asarray(Y)[rows], ref, L.out, L.name)
 
 
+TK_FULL = ["c2_vitb_fc1_1of4", "c2_vitb_fc2_2of8", "c2_vitb_fc1_4of8", "c3_swin_C96_fc1_2of4",
+           "c5_llama_up_2of4_T16_f16"]
+
+
+@pytest.mark.parametrize("name", TK_FULL)
+def test_tk_full_size_sampled_rows(name):
+    """nm_spmm_tk (X [T][K], Y [T][R]) at full workload sizes with the
+    default choice (re-packed 2:4 [T][K] kernel, or transpose, [K][T] kernel,
+    transpose), sampled weight rows against the oracle, and nothing written
+    past R."""
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    from tests._parity import TORCH_DT, dev, host
+    L = {l.name: l for ls in nm_inputs.all_configs().values() for l in ls}[name]
+    W, X, b, s = layer_case(L)
+    p = nm.pack(dev(W, L.dt), L.N, L.M)
+    assert nm.variant_tk(p, L.T, TORCH_DT[L.out]).startswith(("repack24_", "transpose_", "smfmac_i8_2of4_tk"))
+    Xt = dev(np.ascontiguousarray(X.T), L.dt)
+    Yfull = torch.full((L.T, L.R + 16), 5, dtype=TORCH_DT[L.out], device="cuda")
+    kw = {}
+    if b is not None:
+        kw["bias"] = torch.from_numpy(np.asarray(b)).cuda()
+    if s is not None:
+        kw["scale"] = torch.from_numpy(np.asarray(s, np.float32)).cuda()
+    nm.linear(p, Xt, out_dtype=TORCH_DT[L.out], out=Yfull[:, :L.R], **kw)
+    torch.cuda.synchronize()
+    Y = host(Yfull, L.out)
+    rng = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([[0, L.R - 1], rng.integers(0, L.R, 6)]))
+    ref = reference(W, X, L.N, L.M, L.dt, L.out, bias=b, scale=s, rows=rows)
+    compare(np.ascontiguousarray(Y[:, rows].T), ref, L.out, name)
+    want = 5 if L.out != "bf16" else oracle.round_to(np.array([5.0]), "bf16")[0]
+    assert np.all(Y[:, L.R:] == want), "writes beyond R"
+
+
 FAST_I8 = ["smfmac_i8_2of4_256x128", "smfmac_i8_2of4_persistent", "smfmac_i8_2of4_persistent_w8"]
 
 
