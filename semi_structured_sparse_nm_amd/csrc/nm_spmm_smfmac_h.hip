@@ -342,6 +342,11 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         if constexpr (RB > 2)
           *reinterpret_cast<v4i*>(os + wbase + 2048 * w + 16) = v4i{(int)d[4], (int)d[5], (int)d[6], (int)d[7]};
       }
+      // the staging writes complete before the transpose reads are issued
+      // (one wave's LDS operations are ordered; this wait does not rely on
+      // that for the transpose reads, at the cost of one LDS round trip per
+      // quarter)
+      __builtin_amdgcn_s_waitcnt(waitcnt(63, 0));
       const int tok = t0 + 32 * u4 + 8 * lg;
       const bool tok_ok = tok < a.T;
 #pragma unroll
