@@ -334,3 +334,16 @@ def test_tk_transpose_choice_and_workspace(monkeypatch):
     assert _ws(d48, 12608, nm.NM_I8) == 0          # the [K][T] query: no transposes
     monkeypatch.setenv("NM_SPMM_VARIANT", "generic_dense_expand")
     assert tk(d48, 12608, nm.NM_I8) == "generic_dense_expand"
+
+
+def test_tk_workspace_size_validation():
+    """nm_spmm_tk_workspace_size checks its arguments like the [K][T] query."""
+    L = nm.lib()
+    d = _desc(R=3072, K=768, N=4, M=8)
+    n = ctypes.c_size_t()
+    assert L.nm_spmm_tk_workspace_size(ctypes.byref(d), 12608, nm.NM_I8, None) == nm.NM_EINVAL
+    assert L.nm_spmm_tk_workspace_size(ctypes.byref(d), 0, nm.NM_I8, ctypes.byref(n)) == nm.NM_EINVAL
+    assert L.nm_spmm_tk_workspace_size(ctypes.byref(d), 16, nm.NM_F16, ctypes.byref(n)) == nm.NM_EUNSUPPORTED
+    assert L.nm_spmm_tk_workspace_size(None, 16, nm.NM_I8, ctypes.byref(n)) == nm.NM_EINVAL
+    assert L.nm_spmm_tk_workspace_size(ctypes.byref(_desc(R=64, K=64, N=4, M=8)), 16, nm.NM_I8,
+                                       ctypes.byref(n)) == nm.NM_OK and n.value == 0
