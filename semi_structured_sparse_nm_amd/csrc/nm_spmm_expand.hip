@@ -386,6 +386,8 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         // token 16 u + li: f = 2 (u & 1)
         *reinterpret_cast<v2i*>(os + ((512 * u + wb) ^ (16 * (u & 1)))) = v2i{d[0], d[1]};
       }
+      // staging writes complete before the transpose reads
+      __builtin_amdgcn_s_waitcnt(waitcnt(63, 0));
       const int tok = t0 + 64 * h + 16 * lg;
       const bool tok_ok = tok < a.T;
 #pragma unroll

@@ -360,8 +360,10 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         }
         *reinterpret_cast<v4i*>(os + 1024 * u + wb[u & 1]) = v4i{d[0], d[1], d[2], d[3]};
       }
-      // the wave reads back only what it wrote (LDS operations of one wave
-      // complete in order)
+      // the wave reads back only what it wrote, after its staging writes
+      // have completed (no reliance on the order of LDS writes and
+      // transpose reads)
+      __builtin_amdgcn_s_waitcnt(waitcnt(63, 0));
       // every lane stores (fixed operation count for the waits); pieces past
       // T go to an offset past the buffer's end, which the range check drops
       const int tok = t0 + 64 * h + 16 * lg;

@@ -300,6 +300,8 @@ smfmac_i8s_kernel(SpmmArgs a, int mtiles, int ntiles) {
         const int tt = 4 * h + u;
         *reinterpret_cast<v2i*>(os + ((512 * u + wb) ^ (16 * (u & 1)))) = v2i{requant4(0, tt, actc), requant4(1, tt, actc)};
       }
+      // staging writes complete before the transpose reads
+      __builtin_amdgcn_s_waitcnt(waitcnt(63, 0));
       // every lane stores; pieces past T go past the buffer's end (dropped)
       const int tok = tw0 + 64 * h + 16 * lg;
       const bool tok_ok = tok < a.T;
