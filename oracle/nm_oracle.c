@@ -69,7 +69,7 @@ static double elem(const void* p, int dt, int64_t i) {
 }
 
 static int check_nm(int64_t R, int64_t K, int N, int M, int dt) {
-  if (R < 0 || K < 0 || M <= 0 || N < 1 || N > M || K % M) return -1;
+  if (R < 0 || K < 0 || M <= 0 || M > 64 || N < 1 || N > M || K % M) return -1;
   if (dt < ORC_I8 || dt > ORC_BF16) return -1;
   return 0;
 }
@@ -80,30 +80,75 @@ static int check_nm(int64_t R, int64_t K, int N, int M, int dt) {
  * position 0..M-1), j = 0..N-1 in ascending position order.
  *
  * Selection (N:M constraint, paper Sec. 2.1; criterion "largest magnitude"):
- * order the M members of a group by |w| descending, equal magnitudes by
+ * order the M members of a group by magnitude descending, equal magnitudes by
  * position ascending (a stable sort of the position-ordered group), and keep
  * the first N.  Exactly N slots are kept per group, even when some kept
  * values are zero.
+ *
+ * Magnitude of a non-finite fp16 / bf16 weight (the pages only meet finite
+ * weights; this is the reading the library's header documents): every
+ * infinity ranks above every finite value, every NaN above every infinity,
+ * and NaNs rank among themselves by their payload (the fraction field read as
+ * an unsigned integer); the sign never matters.  See sel_key / sel_beats.
  */
+/* Selection key of one weight: a class (0 finite, 1 infinite, 2 NaN) and,
+ * inside the class, |w| (finite) or the NaN payload.  Decoded from the raw
+ * element bits field by field, independently of elem(). */
+typedef struct {
+  int cls;
+  double mag;
+  uint32_t payload;
+} sel_key_t;
+
+static sel_key_t sel_key(const void* p, int dt, int64_t i) {
+  sel_key_t k = {0, 0.0, 0};
+  if (dt == ORC_I8) {
+    k.mag = fabs((double)((const int8_t*)p)[i]);
+    return k;
+  }
+  const uint16_t h = ((const uint16_t*)p)[i];
+  /* binary16: exponent bits 14..10, fraction 9..0; bfloat16: exponent bits
+   * 14..7, fraction 6..0.  An all-ones exponent is an infinity (zero
+   * fraction) or a NaN (nonzero fraction). */
+  const uint32_t emax = dt == ORC_F16 ? 0x1Fu : 0xFFu;
+  const int fbits = dt == ORC_F16 ? 10 : 7;
+  const uint32_t e = (h >> fbits) & emax, f = h & ((1u << fbits) - 1u);
+  if (e == emax) {
+    k.cls = f ? 2 : 1;
+    k.payload = f;
+    return k;
+  }
+  k.mag = fabs(elem(p, dt, i));
+  return k;
+}
+
+/* a ranks strictly above b by magnitude */
+static int sel_beats(sel_key_t a, sel_key_t b) {
+  if (a.cls != b.cls) return a.cls > b.cls;
+  if (a.cls == 0) return a.mag > b.mag;
+  return a.payload > b.payload;
+}
+
 int orc_compress(const void* W, int64_t R, int64_t K, int N, int M, int dt,
                  void* vals, uint8_t* idx) {
   if (check_nm(R, K, N, M, dt)) return -1;
   int b = elt_bytes(dt);
   int64_t G = K / M;
   int order[64];
-  double mag[64];
+  sel_key_t mag[64];
   for (int64_t r = 0; r < R; ++r) {
     for (int64_t g = 0; g < G; ++g) {
       int64_t base = r * K + g * M;
       for (int i = 0; i < M; ++i) {
         order[i] = i;
-        mag[i] = fabs(elem(W, dt, base + i));
+        mag[i] = sel_key(W, dt, base + i);
       }
-      /* stable insertion sort by magnitude, descending */
+      /* stable insertion sort by magnitude, descending: an element moves
+       * ahead only past members it strictly beats */
       for (int i = 1; i < M; ++i) {
         int cur = order[i];
         int j = i - 1;
-        while (j >= 0 && mag[order[j]] < mag[cur]) {
+        while (j >= 0 && sel_beats(mag[cur], mag[order[j]])) {
           order[j + 1] = order[j];
           --j;
         }

@@ -88,12 +88,19 @@ def test_random_fp(dt, M):
 
 
 def _parse_vals(tokens, dt):
+    """Row values of a golden line: decimals, 'inf' / '-inf', or 0x.... raw
+    16-bit patterns (fp16 / bf16)."""
     if dt == "i8":
         return np.array([int(t) for t in tokens], dtype=np.int8)
-    x = np.array([float(t) for t in tokens], dtype=np.float64)
-    if dt == "f16":
-        return x.astype(np.float16)
-    return oracle.f64_to_bf16_bits(x)
+    bits = np.empty(len(tokens), np.uint16)
+    for i, t in enumerate(tokens):
+        if t.lower().startswith("0x"):
+            bits[i] = int(t, 16)
+        elif dt == "f16":
+            bits[i] = np.array([float(t)], np.float16).view(np.uint16)[0]
+        else:
+            bits[i] = oracle.f64_to_bf16_bits(np.array([float(t)]))[0]
+    return bits.view(np.float16) if dt == "f16" else bits
 
 
 def test_golden_hand_examples(golden_dir):

@@ -184,3 +184,57 @@ def test_exhaustive_int_sums_small():
         keep = brute_keep(mags[0], 2, 4)[0]
         want = [w[k] if k in keep else 0 for k in range(4)]
         assert acc[0].tolist() == want
+
+
+def test_reference_fp_bias_and_row_subset_by_hand():
+    """oracle.reference with an fp32 bias, a `rows` subset and each output
+    rounding, against values worked out by hand.
+
+    W (2:4): row 0 = [1, -3, 2, 0.5] keeps positions 1, 2 (|-3|, |2|);
+    row 1 = [0, 4, -1, 1] keeps positions 1, 2 (|4|, then |-1| == |1| goes to
+    the lower position).  X = [[1, 2], [3, 4], [5, 6], [7, 8]]:
+    row 0 -> [-3*3 + 2*5, -3*4 + 2*6] = [1, 0];
+    row 1 -> [4*3 - 5, 4*4 - 6] = [7, 10].
+    bias = [0.5, -0.25] -> [[1.5, 0.5], [6.75, 9.75]]; rows = [1] selects the
+    second row and must take bias[1], not bias[0]."""
+    for dt in ("f16", "bf16"):
+        Wf = np.array([[1, -3, 2, 0.5], [0, 4, -1, 1]], np.float64)
+        Xf = np.array([[1, 2], [3, 4], [5, 6], [7, 8]], np.float64)
+        if dt == "f16":
+            W, X = Wf.astype(np.float16), Xf.astype(np.float16)
+        else:
+            W, X = oracle.f64_to_bf16_bits(Wf), oracle.f64_to_bf16_bits(Xf)
+        bias = np.array([0.5, -0.25], np.float32)
+        full = oracle.reference(W, X, 2, 4, dt, "f64", bias=bias)
+        assert full.tolist() == [[1.5, 0.5], [6.75, 9.75]]
+        sub = oracle.reference(W, X, 2, 4, dt, "f64", bias=bias, rows=[1])
+        assert sub.tolist() == [[6.75, 9.75]]
+        assert oracle.reference(W, X, 2, 4, dt, "f32", bias=bias, rows=[1]).tolist() == [[6.75, 9.75]]
+        nob = oracle.reference(W, X, 2, 4, dt, "f64", rows=[0, 1])
+        assert nob.tolist() == [[1.0, 0.0], [7.0, 10.0]]
+    # bf16 output rounding: 6.75 and 9.75 are exact in bf16 (8 significant
+    # bits); 1/3-ish values are not -- 257 -> 256 (ties to even), 259 -> 260
+    W = oracle.f64_to_bf16_bits(np.array([[1, 0, 0, 0]], np.float64))
+    X = oracle.f64_to_bf16_bits(np.array([[256], [0], [0], [0]], np.float64))
+    y = oracle.reference(W, X, 1, 4, "bf16", "bf16", bias=np.array([1.0], np.float32))
+    assert oracle.to_f64(y, "bf16").tolist() == [[256.0]]
+    y = oracle.reference(W, X, 1, 4, "bf16", "bf16", bias=np.array([3.0], np.float32))
+    assert oracle.to_f64(y, "bf16").tolist() == [[260.0]]
+
+
+def test_reference_int8_row_subset_by_hand():
+    """int8 reference on a `rows` subset indexes bias and scale by the
+    original row numbers.  Row 2 of W = [10, -20, 1, 0] keeps positions 0, 1;
+    X column = [3, 1, 7, 7] -> acc = 30 - 20 = 10; + bias[2] = 5 -> 15;
+    * scale[2] = 0.5 -> 7.5 -> 8 (round half to even); int32 out: 15.
+    Row 0 = [1, 1, 1, 1] keeps positions 0, 1 -> acc 4, + bias[0] 100 -> 104;
+    row 1 with scale 1 and bias 200: 2*3 + 2*1 + 200 = 208 -> saturates to
+    127."""
+    W = np.array([[1, 1, 1, 1], [2, 2, 2, 2], [10, -20, 1, 0]], np.int8)
+    X = np.array([[3], [1], [7], [7]], np.int8)
+    bias = np.array([100, 200, 5], np.int32)
+    scale = np.array([1.0, 1.0, 0.5], np.float32)
+    assert oracle.reference(W, X, 2, 4, "i8", "i32", bias=bias, rows=[2]).tolist() == [[15]]
+    assert oracle.reference(W, X, 2, 4, "i8", "i8", bias=bias, scale=scale, rows=[2]).tolist() == [[8]]
+    assert oracle.reference(W, X, 2, 4, "i8", "i8", bias=bias, scale=scale, rows=[0, 2]).tolist() == [[104], [8]]
+    assert oracle.reference(W, X, 2, 4, "i8", "i8", bias=bias, scale=scale, rows=[1]).tolist() == [[127]]
