@@ -21,7 +21,8 @@
  *
  * Ownership: the caller allocates and owns every buffer (weights, packed
  * values / meta, X, Y, bias, scale, workspace); device buffers are HIP device
- * memory.  The library never allocates, frees or keeps global mutable state;
+ * memory.  The library never allocates or frees, and keeps no mutable state
+ * beyond a per-device cache of the compute-unit count (filled race-free);
  * inputs are not modified; Y is fully overwritten.  `stream` is a hipStream_t
  * (NULL = the default stream); work is enqueued asynchronously on it.
  *
@@ -89,7 +90,9 @@ typedef struct {
 } nm_packed;
 
 /*
- * Sizes of the two packed buffers for an R x K weight of the given N:M and
+ * Sizes of the two packed buffers (the packed window representation of
+ * Sec. 4.2 -- each window's kept values with their in-window positions -- for
+ * the N:M constraint of Sec. 2.1) for an R x K weight of the given N:M and
  * dtype.  NM_EINVAL: null outputs, rows < 1, K < M, K % M != 0, N < 1 or
  * N > M.  NM_EUNSUPPORTED: M not in {4, 8}, dtype not I8 / F16 / BF16.
  * meta_bytes is 0 when N == M.
@@ -102,8 +105,9 @@ nm_status nm_pack_size(int64_t rows, int64_t K, int32_t N, int32_t M, int32_t dt
  * row and every group of M consecutive K-elements, keep the N members of
  * largest magnitude, equal magnitudes going to the lower position (fp16 /
  * bf16 magnitudes are compared as the sign-cleared bit patterns, which orders
- * every finite value by |w| with +0 == -0), and write them with their
- * positions in the layout above.  W is device memory [rows][ldw] of
+ * every finite value by |w| with +0 == -0, every infinity above every finite
+ * value, every NaN above every infinity and NaNs by payload, the sign never
+ * mattering), and write them with their positions in the layout above.  W is device memory [rows][ldw] of
  * desc->dtype; desc->values / desc->meta are caller-allocated device buffers
  * of exactly the sizes nm_pack_size returns (NM_EINVAL otherwise).
  * Requires ldw >= K and W 2-byte aligned for 16-bit dtypes.
@@ -143,6 +147,8 @@ nm_status nm_spmm_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype,
 nm_status nm_spmm_tk_workspace_size(const nm_packed* w, int64_t T, int32_t y_dtype, size_t* bytes);
 
 /*
+ * The N:M sparse product (Sec. 2.1's constrained weight times the
+ * activations; Sec. 4.2: only the kept values of each window enter it):
  * Y = epilogue(acc), acc[r][t] = sum over kept slots (r, k) of W[r][k] X[k][t].
  * Supported (weight dtype -> y_dtype) pairs and epilogues:
  *   I8  -> I32 : y = acc + bias[r]                (int32 accumulate, exact)
@@ -226,9 +232,10 @@ const char* nm_spmm_variant_tk(const nm_packed* w, int64_t T, int32_t y_dtype, i
 /*
  * Number of K slices nm_spmm_act (nm_spmm: act = NM_ACT_NONE) would split
  * this call into across workgroups (1: no split; 0 when the arguments would
- * be rejected), for dense row-major X and Y as nm_spmm_variant assumes.  NM_SPMM_KSPLIT=<S> in the environment
- * forces S slices where S divides the column blocks and the variant takes a
- * split (1 turns the split off).  Launches nothing.
+ * be rejected), for dense row-major X and Y as nm_spmm_variant assumes.
+ * NM_SPMM_VARIANT=<variant>:<S> in the environment (or ":<S>" with the
+ * automatic variant) forces S slices where S divides the column blocks and
+ * the variant takes a split (1 turns the split off).  Launches nothing.
  */
 int32_t nm_spmm_ksplit(const nm_packed* w, int64_t T, int32_t y_dtype, int32_t act);
 

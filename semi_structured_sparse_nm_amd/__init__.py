@@ -140,6 +140,8 @@ def pack(W: torch.Tensor, N: int, M: int) -> Packed:
     dt = _TORCH_TO_NM.get(W.dtype)
     if dt not in (NM_I8, NM_F16, NM_BF16):
         raise TypeError(f"unsupported weight dtype {W.dtype}")
+    if W.device.type != "cuda":
+        raise ValueError(f"W is on {W.device}, not on a GPU")
     R, K = W.shape
     vb, mb = pack_size(R, K, N, M, dt)
     values = torch.empty(vb, dtype=torch.uint8, device=W.device)
@@ -149,6 +151,40 @@ def pack(W: torch.Tensor, N: int, M: int) -> Packed:
     _check(lib().nm_pack(W.data_ptr(), W.stride(0), ctypes.byref(d), _stream(W.device)), "nm_pack")
     p.format_version = d.format_version
     return p
+
+
+def _check_operands(p: Packed, X: torch.Tensor, out: torch.Tensor, out_dtype: torch.dtype,
+                    bias: torch.Tensor | None, scale: torch.Tensor | None,
+                    workspace: torch.Tensor | None) -> None:
+    """Type, length and device checks of one product's operands, before any
+    launch: the kernels size every buffer range from the requested dtypes and
+    R, so a mismatch here would read or write past a tensor's end."""
+    wdt = p.torch_dtype
+    if X.dtype != wdt:
+        raise TypeError(f"activation dtype {X.dtype} does not match the weight dtype {wdt}")
+    if out.dtype != out_dtype:
+        raise TypeError(f"out has dtype {out.dtype}, the call asks for {out_dtype}")
+    if _TORCH_TO_NM.get(out_dtype) is None:
+        raise TypeError(f"unsupported output dtype {out_dtype}")
+    want_bias = torch.int32 if p.dtype == NM_I8 else torch.float32
+    for name, t, dt in (("bias", bias, want_bias), ("scale", scale, torch.float32)):
+        if t is None:
+            continue
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt} for {wdt} weights, got {t.dtype}")
+        if t.dim() != 1 or t.numel() != p.rows or (t.numel() > 1 and t.stride(0) != 1):
+            raise ValueError(f"{name} must be a contiguous vector of length R={p.rows}, got {tuple(t.shape)}")
+    if out_dtype == torch.int8 and scale is None:
+        raise ValueError("int8 output needs a float32 scale of length R")
+    dev = p.values.device
+    if dev.type != "cuda":
+        raise ValueError(f"the packed weight is on {dev}, not on a GPU")
+    for name, t in (("X", X), ("out", out), ("bias", bias), ("scale", scale), ("workspace", workspace),
+                    ("meta", p.meta)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the packed weight on {dev}")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
 
 
 def default_out_dtype(wdt: int) -> torch.dtype:
@@ -209,15 +245,17 @@ def spmm(p: Packed, X: torch.Tensor, bias: torch.Tensor | None = None,
         out = torch.empty((p.rows, T), dtype=out_dtype, device=X.device)
     if out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (p.rows, T):
         raise ValueError("out must be [R, T] with unit stride along T")
+    _check_operands(p, X, out, out_dtype, bias, scale, workspace)
     need = workspace_size(p, T, out_dtype)
-    if need and (workspace is None or workspace.numel() < need):
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     d = p.desc()
     st = lib().nm_spmm_act(ctypes.byref(d), X.data_ptr(), X.stride(0), T, out.data_ptr(), out.stride(0),
                            _TORCH_TO_NM[out_dtype], None if bias is None else bias.data_ptr(),
                            None if scale is None else scale.data_ptr(), ACTS[act], float(out_scale),
                            None if workspace is None else workspace.data_ptr(),
-                           0 if workspace is None else workspace.numel(), _stream(X.device))
+                           0 if workspace is None else workspace.numel() * workspace.element_size(),
+                           _stream(X.device))
     _check(st, "nm_spmm_act" if act != "none" else "nm_spmm")
     return out
 
@@ -239,14 +277,16 @@ def linear(p: Packed, Xt: torch.Tensor, bias: torch.Tensor | None = None,
         out = torch.empty((T, p.rows), dtype=out_dtype, device=Xt.device)
     if out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (T, p.rows):
         raise ValueError("out must be [T, R] with unit stride along R")
+    _check_operands(p, Xt, out, out_dtype, bias, scale, workspace)
     need = workspace_size_tk(p, T, out_dtype)
-    if need and (workspace is None or workspace.numel() < need):
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=Xt.device)
     d = p.desc()
     st = lib().nm_spmm_tk(ctypes.byref(d), Xt.data_ptr(), Xt.stride(0), T, out.data_ptr(), out.stride(0),
                           _TORCH_TO_NM[out_dtype], None if bias is None else bias.data_ptr(),
                           None if scale is None else scale.data_ptr(), ACTS[act], float(out_scale),
                           None if workspace is None else workspace.data_ptr(),
-                          0 if workspace is None else workspace.numel(), _stream(Xt.device))
+                          0 if workspace is None else workspace.numel() * workspace.element_size(),
+                          _stream(Xt.device))
     _check(st, "nm_spmm_tk")
     return out

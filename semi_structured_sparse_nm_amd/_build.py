@@ -9,6 +9,8 @@ import concurrent.futures as cf
 import glob
 import os
 import subprocess
+import sys
+import time
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -26,21 +28,32 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
+def _headers():
+    return glob.glob(os.path.join(CSRC, "*.hpp")) + [os.path.join(ROOT, "include", "nm_sparse.h")]
+
+
+def _compile(src: str, force: bool = True) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if not force and os.path.exists(obj):
+        newest = max(os.path.getmtime(f) for f in [src, *_headers()])
+        if os.path.getmtime(obj) > newest:
+            return obj
+    t0 = time.time()
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    print(f"  {os.path.basename(src)}: {time.time() - t0:.0f} s", flush=True)
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    """Compile every HIP source and link libnmsparse.so; returns its path."""
+def build(jobs: int = 8, force: bool = True) -> str:
+    """Compile the HIP sources (every one, or with force=False only those
+    older than their object) and link libnmsparse.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda f: _compile(f, force), srcs))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,4 +64,4 @@ def build(jobs: int = 8) -> str:
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build(force="--changed" not in sys.argv))

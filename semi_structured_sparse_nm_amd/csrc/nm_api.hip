@@ -9,6 +9,23 @@
 using nm::Geometry;
 using nm::SpmmArgs;
 
+#include <atomic>
+
+namespace nm {
+
+int cu_count(int device) {
+  static std::atomic<int> cache[64];
+  if (device < 0 || device >= 64) return 256;
+  int cus = cache[device].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
+    cus = 256;
+  cache[device].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+}  // namespace nm
+
 namespace {
 
 bool is_weight_dtype(int dt) { return dt == NM_I8 || dt == NM_F16 || dt == NM_BF16; }
@@ -45,52 +62,59 @@ nm_status check_desc(const nm_packed* w, Geometry* out) {
 }
 
 int device_cus() {
-  static int cache[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cache[dev]) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    cache[dev] = cus;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  return nm::cu_count(dev);
+}
+
+// The one debug override: NM_SPMM_VARIANT=<variant>[:<S>] forces a variant
+// where its requirements hold, and with ":<S>" also the number of K slices
+// of the tile kernels that take a K split (tile and split sweeps); an empty
+// variant name (":<S>") keeps the automatic choice and forces only S.
+struct Forced {
+  char name[96];
+  int S;        // 0: not forced
+};
+
+Forced forced() {
+  Forced f{};
+  const char* e = getenv("NM_SPMM_VARIANT");
+  if (!e) return f;
+  const char* colon = strchr(e, ':');
+  const size_t n = colon ? (size_t)(colon - e) : strlen(e);
+  if (n < sizeof f.name) {
+    memcpy(f.name, e, n);
+    f.name[n] = 0;
   }
-  return cache[dev];
+  if (colon) f.S = atoi(colon + 1);
+  return f;
 }
 
 // Variant table (the paper's adaptive parallelism, Sec. 4.1: the kernel and
-// its tiling follow the operator's shape).  NM_SPMM_VARIANT=<name> in the
-// environment forces a variant where its requirements hold (tile sweeps).
+// its tiling follow the operator's shape).
 enum Variant {
   V_INVALID = 0,
   V_GENERIC,
-  V_SMFMAC_I8,      // int8 2:4 sparse MFMA, 256 x 128 tile per workgroup
-  V_SMFMAC_I8P,     // the same tile, persistent workgroups, cross-tile pipeline
+  V_SMFMAC_I8P,     // int8 2:4 sparse MFMA, persistent 256 x 128 tiles, cross-tile pipeline
   V_SMFMAC_I8P8,    // persistent, 8-wave workgroups (512 x 128 tiles, one per CU)
   V_SMFMAC_H,       // fp16 / bf16 2:4 sparse MFMA, persistent 256 x 128 tiles
   V_SMFMAC_HD,      // fp16 / bf16 2:4, decode shapes (T <= 16): K split across 8 waves
   V_EXPAND,         // any other N:M (int8, fp16, bf16): windows expanded in registers, dense MFMA
   V_EXPAND_DECODE,  // any N:M, decode shapes (T <= 16): K split across 8 waves, dense MFMA
-  V_SMFMAC_I8S,     // int8 2:4, K <= 1024: weights held in registers, workgroups walk token strips
-  V_EXPAND32,       // as V_EXPAND with 32 x 32 dense MFMA (forced only: measured slower)
   V_SMFMAC_I8TK,    // int8 2:4 persistent, [T][K] layout (X [T][K], Y [T][R])
-  V_SMFMAC_H8,      // as V_SMFMAC_H with 8-wave workgroups (one per CU)
   V_COUNT
 };
 
 const char* variant_name(Variant v) {
   switch (v) {
     case V_GENERIC: return "generic_dense_expand";
-    case V_SMFMAC_I8: return "smfmac_i8_2of4_256x128";
     case V_SMFMAC_I8P: return "smfmac_i8_2of4_persistent";
     case V_SMFMAC_I8P8: return "smfmac_i8_2of4_persistent_w8";
     case V_SMFMAC_H: return "smfmac_h_2of4_persistent";
     case V_SMFMAC_HD: return "smfmac_h_2of4_decode";
     case V_EXPAND: return "expand_mfma_persistent";
     case V_EXPAND_DECODE: return "expand_mfma_decode";
-    case V_SMFMAC_I8S: return "smfmac_i8_2of4_stationary";
-    case V_EXPAND32: return "expand_mfma32_persistent";
     case V_SMFMAC_I8TK: return "smfmac_i8_2of4_tk";
-    case V_SMFMAC_H8: return "smfmac_h_2of4_persistent_w8";
     default: return "invalid";
   }
 }
@@ -106,14 +130,10 @@ struct Call {
 };
 
 bool eligible(Variant v, const Call& c) {
-  // the 256 x 128 int8 kernel and the 32 x 32-fragment dense-expand kernel
-  // (tested alternatives, forced only) carry no fused activation
-  if (c.act != NM_ACT_NONE && (v == V_SMFMAC_I8 || v == V_EXPAND32)) return false;
   // the [T][K] layout has kernels of its own (and the generic one)
   if ((c.layout == NM_LAYOUT_TK) != (v == V_SMFMAC_I8TK) && v != V_GENERIC) return false;
   switch (v) {
     case V_GENERIC: return true;
-    case V_SMFMAC_I8:
     case V_SMFMAC_I8P:
     case V_SMFMAC_I8P8:
       // 2:4 int8; X rows in whole 16-byte chunks; 32-bit buffer offsets,
@@ -123,15 +143,7 @@ bool eligible(Variant v, const Call& c) {
              aligned(c.X, 16) && (c.g->K + 128) * c.ldx < (1ll << 31) &&
              c.g->values_bytes() < (1ull << 31) && (c.g->R + 512) * c.ldy * 4 < (1ll << 31) &&
              (c.ydt == NM_I32 || (c.ydt == NM_I8 && c.ldy % 16 == 0 && aligned(c.Y, 16)));
-    case V_SMFMAC_I8S:
-      // as the persistent int8 2:4 kernel, with 2 to 8 column blocks (the
-      // weights of a wave's rows over all of K fit its registers)
-      return c.wdt == NM_I8 && c.g->N == 2 && c.g->M == 4 && nm::smfmac_i8s_supported(c.g->nKB) &&
-             c.T % 16 == 0 && c.ldx % 16 == 0 && aligned(c.X, 16) && (c.g->K + 128) * c.ldx < (1ll << 31) &&
-             c.g->values_bytes() + 8192 < (1ull << 31) && (c.g->R + 256) * c.ldy * 4 < (1ll << 31) &&
-             (c.ydt == NM_I32 || (c.ydt == NM_I8 && c.ldy % 16 == 0 && aligned(c.Y, 16)));
     case V_SMFMAC_H:
-    case V_SMFMAC_H8:
       // fp16 / bf16 2:4; X rows in whole 16-byte pieces; 32-bit buffer
       // offsets that do not wrap for the rows a tile reaches past K and R;
       // 16-bit output stored as 16-byte row pieces
@@ -155,14 +167,6 @@ bool eligible(Variant v, const Call& c) {
              c.T % 16 == 0 &&
              c.ldx % (16 / c.g->eb) == 0 && aligned(c.X, 16) && (c.g->K + 128) * c.ldx * c.g->eb < (1ll << 31) &&
              c.g->values_bytes() + 1024 < (1ull << 31) && c.g->meta_bytes() + 1024 < (1ull << 31) &&
-             (c.g->R + 256) * c.ldy * 4 < (1ll << 31) &&
-             (c.ydt == NM_I32 || c.ydt == NM_F32 || (c.ldy % (16 / nm::dtype_bytes(c.ydt)) == 0 && aligned(c.Y, 16)));
-    case V_EXPAND32:
-      // as the 16 x 16 dense-expand kernel; a lane's 32 rows span two packed
-      // row blocks, so offsets reach one block column past a row block
-      return nm::expand32_supported(c.g->N, c.g->M) && c.T % 16 == 0 && c.ldx % (16 / c.g->eb) == 0 &&
-             aligned(c.X, 16) && (c.g->K + 128) * c.ldx * c.g->eb < (1ll << 31) &&
-             2 * c.g->values_bytes() + 65536 < (1ull << 31) && 2 * c.g->meta_bytes() + 65536 < (1ull << 31) &&
              (c.g->R + 256) * c.ldy * 4 < (1ll << 31) &&
              (c.ydt == NM_I32 || c.ydt == NM_F32 || (c.ldy % (16 / nm::dtype_bytes(c.ydt)) == 0 && aligned(c.Y, 16)));
     case V_EXPAND_DECODE:
@@ -189,10 +193,10 @@ bool eligible(Variant v, const Call& c) {
 Variant choose_auto(const Call& c);
 
 Variant choose(const Call& c) {
-  const char* force = getenv("NM_SPMM_VARIANT");
-  if (force && *force) {
+  const Forced f = forced();
+  if (f.name[0]) {
     for (int v = V_GENERIC; v < V_COUNT; ++v)
-      if (strcmp(force, variant_name((Variant)v)) == 0 && eligible((Variant)v, c)) return (Variant)v;
+      if (strcmp(f.name, variant_name((Variant)v)) == 0 && eligible((Variant)v, c)) return (Variant)v;
   }
   return choose_auto(c);
 }
@@ -214,16 +218,7 @@ Variant choose_auto(const Call& c) {
     if (tiles4 < 4 * (int64_t)device_cus() && eligible(V_SMFMAC_I8P8, c)) return V_SMFMAC_I8P8;
     return V_SMFMAC_I8P;
   }
-  // fp16 / bf16 2:4: 4-wave workgroups.  The 8-wave instance (two row
-  // blocks per wave, same 256 x 128 tiles) is forced only: each of its waves
-  // reads every B fragment for half the matrix work, and measured on MI355X
-  // it was slower on most few-tile shapes (LLaMA-7B down 154.7 -> 163.7 us,
-  // Swin-T stage 3/4 projections 2-12%), faster only on LLaMA qkvo (61.6 ->
-  // 58.4 us)
   if (eligible(V_SMFMAC_H, c)) return V_SMFMAC_H;
-  // the 32 x 32-fragment dense-expand kernel is correct but measured 2-10%
-  // slower than the 16 x 16 one on every ViT-B, Swin and LLaMA shape (the
-  // block loop is not bound by the matrix cores): forced only
   if (eligible(V_EXPAND, c)) return V_EXPAND;
   return V_GENERIC;
 }
@@ -250,25 +245,22 @@ Call make_call(const Geometry& g, int wdt, int ydt, int64_t T, int64_t ldx, int6
 // are fitted on MI355X (Swin-T and LLaMA-7B shapes, forced S = 1 .. 16): the
 // model ranks the measured times and picks S = 4 for the Swin stage-4 MLP
 // out-projection (37.7 -> 22.8 us) and no split where the partials' traffic
-// outweighs the gain.  NM_SPMM_KSPLIT=<S> forces S where it divides the
-// column blocks (1 turns the split off).
+// outweighs the gain.  NM_SPMM_VARIANT=<variant>:<S> forces S where it
+// divides the column blocks (1 turns the split off).
 constexpr int kMinBlocks = 4;
 constexpr double kStepUs = 0.8;          // one column-block step of a work item
 constexpr double kPartialGBs = 5000.0;   // partial sums' effective write + read rate
 constexpr double kReduceUs = 2.0;        // reduction launch and tail
 
 int ksplit_for(Variant v, const Call& c) {
-  if (v != V_SMFMAC_H && v != V_SMFMAC_H8 && v != V_EXPAND) return 1;
+  if (v != V_SMFMAC_H && v != V_EXPAND) return 1;
   const Geometry& g = *c.g;
   const int nKB = (int)g.nKB;
   if (c.T % 4 != 0) return 1;
   // the partials' 32-bit element offsets within one slice
   if ((g.R + 256) * c.T * 4 >= (1ll << 31)) return 1;
-  const char* force = getenv("NM_SPMM_KSPLIT");
-  if (force && *force) {
-    const int S = atoi(force);
-    return (S >= 1 && S <= nKB && nKB % S == 0) ? S : 1;
-  }
+  const int fS = forced().S;
+  if (fS) return (fS >= 1 && fS <= nKB && nKB % fS == 0) ? fS : 1;
   const int64_t tiles = ((g.R + 255) / 256) * ((c.T + 127) / 128);
   const int64_t slots = device_cus();
   auto cost = [&](int S) {
@@ -327,7 +319,7 @@ size_t repack_meta_off(const Geometry& g24) { return (g24.values_bytes() + 255) 
 size_t repack_bytes(const Geometry& g24) { return repack_meta_off(g24) + g24.meta_bytes(); }
 
 bool repack_inner(Variant v) {
-  return v == V_SMFMAC_I8P || v == V_SMFMAC_I8P8 || v == V_SMFMAC_H || v == V_SMFMAC_H8 || v == V_SMFMAC_I8TK;
+  return v == V_SMFMAC_I8P || v == V_SMFMAC_I8P8 || v == V_SMFMAC_H || v == V_SMFMAC_I8TK;
 }
 
 // ---- [T][K] calls without a kernel of their own.  The generic kernel takes
@@ -360,8 +352,9 @@ size_t plan_workspace(const Plan& p, const Call& c) {
 Plan plan_for(const Call& c) {
   Plan p;
   p.v = choose(c);
-  const char* force = getenv("NM_SPMM_VARIANT");
-  const bool forced = force && *force;
+  const Forced fv = forced();
+  const char* force = fv.name;
+  const bool forced = force[0] != 0;
   const bool forced_rp = forced && strncmp(force, kRepackPrefix, strlen(kRepackPrefix)) == 0;
   const bool forced_tr = forced && strncmp(force, kTransposePrefix, strlen(kTransposePrefix)) == 0;
   const double work = (double)c.g->R * (double)c.g->K * (double)c.T;
@@ -429,7 +422,6 @@ const char* plan_name(const Plan& p) {
     case V_SMFMAC_I8P: return "repack24_smfmac_i8_2of4_persistent";
     case V_SMFMAC_I8P8: return "repack24_smfmac_i8_2of4_persistent_w8";
     case V_SMFMAC_H: return "repack24_smfmac_h_2of4_persistent";
-    case V_SMFMAC_H8: return "repack24_smfmac_h_2of4_persistent_w8";
     case V_SMFMAC_I8TK: return "repack24_smfmac_i8_2of4_tk";
     default: return "invalid";
   }
@@ -532,9 +524,7 @@ nm_status run_variant(Variant v, int S, const SpmmArgs& a, void* part, hipStream
     p.ksplit = S;
     p.kbs = (int)(a.g.nKB / S);
     p.ys = a.g.R * a.T;
-    e = v == V_SMFMAC_H    ? nm::launch_spmm_smfmac_h(p, s)
-        : v == V_SMFMAC_H8 ? nm::launch_spmm_smfmac_h8(p, s)
-                           : nm::launch_spmm_expand(p, s);
+    e = v == V_SMFMAC_H ? nm::launch_spmm_smfmac_h(p, s) : nm::launch_spmm_expand(p, s);
     if (e != hipSuccess) return NM_EHIP;
     SpmmArgs r = a;
     r.ksplit = S;
@@ -545,16 +535,12 @@ nm_status run_variant(Variant v, int S, const SpmmArgs& a, void* part, hipStream
   }
   switch (v) {
     case V_GENERIC: e = nm::launch_spmm_generic(a, s); break;
-    case V_SMFMAC_I8: e = nm::launch_spmm_smfmac_i8(a, 0, s); break;
     case V_SMFMAC_I8P: e = nm::launch_spmm_smfmac_i8p(a, 0, s); break;
     case V_SMFMAC_I8P8: e = nm::launch_spmm_smfmac_i8p(a, 1, s); break;
     case V_SMFMAC_H: e = nm::launch_spmm_smfmac_h(a, s); break;
-    case V_SMFMAC_H8: e = nm::launch_spmm_smfmac_h8(a, s); break;
     case V_SMFMAC_HD: e = nm::launch_spmm_smfmac_hd(a, s); break;
     case V_EXPAND: e = nm::launch_spmm_expand(a, s); break;
-    case V_EXPAND32: e = nm::launch_spmm_expand32(a, s); break;
     case V_EXPAND_DECODE: e = nm::launch_spmm_expand_decode(a, s); break;
-    case V_SMFMAC_I8S: e = nm::launch_spmm_smfmac_i8s(a, s); break;
     case V_SMFMAC_I8TK: e = nm::launch_spmm_smfmac_i8tk(a, s); break;
     default: return NM_EINVAL;
   }

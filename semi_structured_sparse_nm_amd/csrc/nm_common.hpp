@@ -93,18 +93,12 @@ struct SpmmArgs {
 hipError_t launch_pack(const void* W, int64_t ldw, const Geometry& g, int wdt, uint8_t* values,
                        uint8_t* meta, hipStream_t s);
 hipError_t launch_spmm_generic(const SpmmArgs& a, hipStream_t s);
-hipError_t launch_spmm_smfmac_i8(const SpmmArgs& a, int cfg, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8p(const SpmmArgs& a, int cfg, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8tk(const SpmmArgs& a, hipStream_t s);   // [T][K] layout
 hipError_t launch_spmm_smfmac_h(const SpmmArgs& a, hipStream_t s);
-hipError_t launch_spmm_smfmac_h8(const SpmmArgs& a, hipStream_t s);   // 8-wave workgroups
 hipError_t launch_spmm_smfmac_hd(const SpmmArgs& a, hipStream_t s);
-hipError_t launch_spmm_smfmac_i8s(const SpmmArgs& a, hipStream_t s);
-bool smfmac_i8s_supported(int64_t nKB);   // column-block counts launch_spmm_smfmac_i8s instantiates
 hipError_t launch_spmm_expand(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_expand_decode(const SpmmArgs& a, hipStream_t s);
-hipError_t launch_spmm_expand32(const SpmmArgs& a, hipStream_t s);
-bool expand32_supported(int N, int M);   // N:M instantiated by launch_spmm_expand32
 bool expand_supported(int N, int M);   // N:M instantiated by launch_spmm_expand
 // N:M patterns with at most two kept members in every aligned group of four
 // columns (1:4, 1:8, 2:8), and their re-pack into the 2:4 layout of the same
@@ -120,6 +114,10 @@ hipError_t launch_transpose(const void* src, int64_t rows, int64_t cols, int64_t
 // a's own output type, bias and scale (T a multiple of 4).
 hipError_t launch_splitk_reduce(const SpmmArgs& a, hipStream_t s);
 
+// Compute units of a device (cached per device; safe to call from several
+// threads at once: a racing first call only repeats the query).
+int cu_count(int device);
+
 // ---------------------------------------------------------------- device
 // Cache policy of the output stores (gfx950 buffer-store cache bits: sc0 |
 // nt).  The output is written once and never read back by the kernel;
@@ -128,9 +126,83 @@ hipError_t launch_splitk_reduce(const SpmmArgs& a, hipStream_t s);
 constexpr int kStreamStore = 3;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// compile-time integer as a type (unrolled stage / part indices)
+template <int N> struct ic { static constexpr int value = N; };
+
+// Barrier without a memory fence (the waits that make data visible are
+// explicit); the memory clobber keeps memory accesses from moving across it.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt bits 3:0 and 15:14, expcnt 6:4
+// (no wait), lgkmcnt 11:8.
+constexpr int waitcnt(int vm, int lgkm) {
+  return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
+}
+
+// Raw buffer resource over [p, p + num_records) bytes: offsets past the end
+// read as zero and drop stores.
+__device__ __forceinline__ v4i make_rsrc(const void* p, int num_records) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  return v4i{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), num_records, 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// A page of zeros in device memory (one per code object).  Every load whose
+// lanes would all fall outside its operand -- row blocks past R, activation
+// rows past K, a null bias or scale, the load groups a pipelined kernel issues
+// past its last block -- reads from here instead.  A buffer load with every
+// lane out of its resource's range returns zeros at once, ahead of older
+// loads still in flight, so counting it in an explicit vmcnt wait would let
+// the wait pass with those older loads (another wave's part of a staged tile)
+// still outstanding.  Loads from this page are ordinary in-range loads and
+// complete in issue order like the rest.
+static __device__ __attribute__((aligned(256))) uint8_t nm_zero_page[4096];
+// a wave-uniform condition, made visibly uniform (scalar), so that a buffer
+// resource chosen by it stays in scalar registers
+__device__ __forceinline__ bool uniform(bool c) { return __builtin_amdgcn_readfirstlane((int)c) != 0; }
+__device__ __forceinline__ v4i zero_rsrc() { return make_rsrc(nm_zero_page, (int)sizeof nm_zero_page); }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t zero_brsrc() {
+  return __builtin_amdgcn_make_buffer_rsrc(nm_zero_page, 0, (int)sizeof nm_zero_page, 0x00020000);
+}
+
+// Direct-to-LDS buffer loads: lane l's bytes land at M0 + size * l; offsets
+// past the resource's range read as zero.  The compiler does not see these
+// loads in its wait bookkeeping: completion is waited for explicitly (vmcnt,
+// then a barrier where other waves read the data).  M0 is written here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(v4i rsrc, uint32_t lds, int voff, int soff) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(v4i rsrc, uint32_t lds, int voff, int soff) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Transposing LDS reads (ds_read_b64_tr_b8 / _b16): each lane receives 8
+// bytes gathered across the lanes of its 16-lane group.
+__device__ __forceinline__ v2i lds_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(p));
+}
+__device__ __forceinline__ v2i lds_tr16(const uint8_t* p) {
+  typedef short v4s_ __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(
+      v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_*)(p)));
+}
 
 // binary32 -> binary16 / bfloat16 bits, round to nearest even (finite inputs;
 // bfloat16 NaN kept quiet).

@@ -25,6 +25,7 @@
 // counts and one barrier per block, as in the 2:4 kernels.  Epilogues: int8
 // bias + requant, int32, fp16 / bf16 (LDS transpose and 16-byte row pieces),
 // fp32 (direct).
+#pragma once
 #include "nm_common.hpp"
 #include "nm_expand.hpp"
 
@@ -32,48 +33,10 @@ namespace nm {
 
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef int v2i __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-
-template <int N> struct ic { static constexpr int value = N; };
-
-__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
-constexpr int waitcnt(int vm, int lgkm) {
-  return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
-}
-__device__ __forceinline__ v4i make_rsrc(const void* p, int num_records) {
-  const uint64_t a = (uint64_t)(uintptr_t)p;
-  return v4i{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), num_records, 0x00020000};
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(v4i rsrc, uint32_t lds, int voff, int soff) {
-  lds = __builtin_amdgcn_readfirstlane(lds);
-  soff = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(v4i rsrc, uint32_t lds, int voff, int soff) {
-  lds = __builtin_amdgcn_readfirstlane(lds);
-  soff = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-__device__ __forceinline__ v2i lds_tr8(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(p));
-}
-__device__ __forceinline__ v2i lds_tr16(const uint8_t* p) {
-  return __builtin_bit_cast(
-      v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p)));
-}
 
 constexpr int RB = 2;              // row blocks (16 rows) per wave
 constexpr int TN = 8;              // token tiles (16 tokens) per wave
@@ -100,7 +63,6 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   constexpr int EB = RG::EB, VB = RG::VB, VD = RG::VD, W = RG::W, C_B = RG::C_B, MRB = RG::MRB;
   constexpr int NVL = (VB + 15) / 16;             // value loads per row block
   constexpr int LA = NVL + (W ? 1 : 0);           // A loads per row block (values, positions)
-  constexpr int NL = RB * LA + DPW;               // loads per group (+2 on a tile's first block)
   constexpr bool OUT16 = OUT == NM_F16 || OUT == NM_BF16;
   typedef typename std::conditional<I8, v4i, v4f>::type Acc;
 
@@ -140,9 +102,9 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   };
 
   const v4i rx = make_rsrc(a.X, (int)(g.K * a.ldx * EB));
-  const __amdgpu_buffer_rsrc_t rv =
+  const __amdgpu_buffer_rsrc_t rvv =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values), 0, (int)g.values_bytes(), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+  const __amdgpu_buffer_rsrc_t rmm = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(a.meta), 0, W ? (int)g.meta_bytes() : 0, 0x00020000);
   const v4i rbias = make_rsrc(a.bias, a.bias ? (int)(g.R * 4) : 0);
   const v4i rscale = make_rsrc(a.scale, a.scale ? (int)(g.R * 4) : 0);
@@ -199,21 +161,26 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   int g_live = 0, g_rb0 = 0, g_soff = 0;
   // group parts: 0, 1: A of row block 0, 1; 2, 3: X halves; 4: bias / scale
   // on a tile's first block and the cursor
+  // No load has all its lanes outside its operand: row blocks past R, X rows
+  // past K, absent bias / scale and the groups issued past the end read the
+  // zero page instead (see nm_zero_page); partly outside rows and tokens are
+  // in the vector offset, which the range check covers.
+  const __amdgpu_buffer_rsrc_t rzb = zero_brsrc();
+  const v4i rz = zero_rsrc();
   auto load_part = [&](auto st, auto part) {
     constexpr int S = decltype(st)::value;
     constexpr int P = decltype(part)::value;
-    // Every offset that can leave its buffer (blocks past the matrix, rows
-    // past K, tokens past a row's end, groups past the end) is in the
-    // vector offset, which the range check covers; the scalar offset is 0.
     if constexpr (P == 0) {
       g_live = __builtin_amdgcn_readfirstlane(ln < total ? 1 : 0);
       g_rb0 = (lr0 >> 4) + RB * wave;
-      g_soff = __builtin_amdgcn_readfirstlane(g_live ? ((lks + lkb) * (128 / EB) * ldx + lt0) * EB
-                                                     : (int)(g.K * a.ldx * EB));
+      g_soff = __builtin_amdgcn_readfirstlane(((lks + lkb) * (128 / EB) * ldx + lt0) * EB);
     }
     if constexpr (P < RB) {
-      const int rbc = __builtin_amdgcn_readfirstlane(min(g_rb0 + P, nRB));
-      const int blk = (g_live ? rbc : nRB) * nKB + (rbc < nRB ? lks + lkb : 0);
+      const int rbr = g_rb0 + P;
+      const bool real = uniform(g_live && rbr < nRB);
+      const auto rv = real ? rvv : rzb;
+      const auto rm = real ? rmm : rzb;
+      const int blk = real ? rbr * nKB + lks + lkb : 0;
       const int vo = voff_v + blk * C_B * 16;
 #pragma unroll
       for (int c = 0; c < NVL; ++c) {
@@ -244,14 +211,18 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
 #pragma unroll
       for (int j = J0; j < J0 + H; ++j) {
         const int d = wave * DPW + j;
-        lds_dma16(rx, lds_addr(sp + d * 1024), xoff(j) + g_soff, 0);
+        // load d fills rows (8 or 4) d .. of the stage: all past K -> zeros
+        const bool real = uniform(g_live && (lks + lkb) * (128 / EB) + (I8 ? 8 : 4) * d < (int)g.K);
+        lds_dma16(real ? rx : rz, lds_addr(sp + d * 1024), real ? xoff(j) + g_soff : 16 * lane, 0);
       }
     } else {
       if (g_live && lkb == 0) {
         uint8_t* bs = bsw + 512 * (lk & 3);
+        const bool rows_ok = uniform(lr0 + 32 * wave < (int)g.R);
+        const bool hb = uniform(rows_ok && a.bias), hs = uniform(rows_ok && a.scale);
         const int boff = 4 * (lr0 + 32 * wave + lane);
-        lds_dma4(rbias, lds_addr(bs), boff, 0);
-        lds_dma4(rscale, lds_addr(bs + 256), boff, 0);
+        lds_dma4(hb ? rbias : rz, lds_addr(bs), hb ? boff : 4 * lane, 0);
+        lds_dma4(hs ? rscale : rz, lds_addr(bs + 256), hs ? boff : 4 * lane, 0);
       }
       ++ln;
       if (g_live && ++lkb == kbs) {
@@ -467,14 +438,18 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
 
   int n = 0, ck = 0, ckb = 0, cr0, ct0, cks;
   tile_of(0, cr0, ct0, cks);
-  // Wait until the oldest outstanding group has landed: every group holds
-  // at least NL loads and loads complete in order, so at most NL
-  // outstanding means everything before the newest group is in.  One
-  // unconditional count (not NL plus the next group's extra loads) keeps the
-  // wait a single instruction on every path through the unrolled steps.
+  // Wait until the stage of the oldest outstanding group (and a tile's bias
+  // rows) has landed.  Only direct-to-LDS loads are counted: they complete
+  // in issue order among themselves, but the register loads of a later
+  // group (A fragments hitting in L2) may complete before them, so a count
+  // that included those could pass with the stage still in flight.  Every
+  // group holds at least DPW of them, so at most DPW outstanding means every
+  // direct-to-LDS load before the newest group is in; the compiler's own
+  // waits cover the A registers.  One unconditional count keeps the wait a
+  // single instruction on every path through the unrolled steps.
   auto wait_for_group = [&](int extra_after) {
     (void)extra_after;
-    __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
+    __builtin_amdgcn_s_waitcnt(waitcnt(DPW, 15));
   };
 
   load_group(ic<0>());
@@ -526,18 +501,6 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
 #endif
 }
 
-int cu_count(int device) {
-  static int cache[64];
-  if (device < 0 || device >= 64) return 256;
-  if (!cache[device]) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
-      cus = 256;
-    cache[device] = cus;
-  }
-  return cache[device];
-}
-
 template <int WT, int NN, int MM, int OUT>
 hipError_t launch_one(const SpmmArgs& a, hipStream_t s) {
   const int mtiles = (int)((a.g.R + BM - 1) / BM);
@@ -582,14 +545,10 @@ hipError_t launch_wt(const SpmmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool expand_supported(int N, int M) {
-  return (M == 4) || (M == 8 && (N == 1 || N == 2 || N == 4 || N == 8));
-}
-
-hipError_t launch_spmm_expand(const SpmmArgs& a, hipStream_t s) {
-  if (a.wdt == NM_I8) return launch_wt<NM_I8>(a, s);
-  if (a.wdt == NM_F16) return launch_wt<NM_F16>(a, s);
-  return launch_wt<NM_BF16>(a, s);
-}
+// one instantiation per weight dtype, each in its own translation unit
+// (nm_spmm_expand_{i8,f16,bf16}.hip) so that they compile in parallel
+hipError_t launch_spmm_expand_i8(const SpmmArgs& a, hipStream_t s);
+hipError_t launch_spmm_expand_f16(const SpmmArgs& a, hipStream_t s);
+hipError_t launch_spmm_expand_bf16(const SpmmArgs& a, hipStream_t s);
 
 }  // namespace nm

@@ -27,41 +27,7 @@ namespace nm {
 
 namespace {
 
-typedef int v2i __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
-
-constexpr int waitcnt(int vm, int lgkm) {
-  return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
-}
-__device__ __forceinline__ v4i make_rsrc(const void* p, int num_records) {
-  const uint64_t a = (uint64_t)(uintptr_t)p;
-  return v4i{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), num_records, 0x00020000};
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(v4i rsrc, uint32_t lds, int voff, int soff) {
-  lds = __builtin_amdgcn_readfirstlane(lds);
-  soff = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(v4i rsrc, uint32_t lds, int voff, int soff) {
-  lds = __builtin_amdgcn_readfirstlane(lds);
-  soff = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-__device__ __forceinline__ v2i lds_tr8(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(p));
-}
-__device__ __forceinline__ v2i lds_tr16(const uint8_t* p) {
-  return __builtin_bit_cast(
-      v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p)));
-}
 
 constexpr int NWD = 8;             // waves per workgroup (K split)
 
@@ -133,24 +99,33 @@ __global__ void __launch_bounds__(NWD * 64) expand_decode_kernel(SpmmArgs a) {
     }
   }
 
-  // group m (0 <= m < nblk: block kb0 + m; otherwise zeros) into slot m % D
+  // group m (0 <= m < nblk: block kb0 + m; otherwise zeros) into slot m % D.
+  // No load has all its lanes outside its operand: groups past the wave's
+  // last block, and X rows past K, read the zero page (see nm_zero_page), so
+  // every group is the same NLG in-order loads.
+  const v4i rz = zero_rsrc();
   auto issue = [&](int m, int s) {
-    const bool live = m < nblk;
+    const bool live = uniform(m < nblk);
     const int kb = kb0 + m;
     uint8_t* sp = ws + s * SL::BYTES;
-    const int xs = __builtin_amdgcn_readfirstlane(live ? kb * (128 / EB) * ldx * EB : (int)(g.K * a.ldx * EB));
-    lds_dma16(rx, lds_addr(sp), xoff[0], xs);
-    lds_dma16(rx, lds_addr(sp + 1024), xoff[1], xs);
-    const int blk = live ? rb * nKB + kb : (int)(g.nRB * g.nKB);
+    const int xs = __builtin_amdgcn_readfirstlane(live ? kb * (128 / EB) * ldx * EB : 0);
+    constexpr int XROWS = I8 ? 64 : 32;   // k rows one X load covers
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool xr = uniform(live && kb * (128 / EB) + XROWS * j < (int)g.K);
+      lds_dma16(xr ? rx : rz, lds_addr(sp + 1024 * j), xr ? xoff[j] : 16 * lane, xr ? xs : 0);
+    }
+    const v4i ra = live ? rv : rz, rmm = live ? rm : rz;
+    const int blk = live ? rb * nKB + kb : 0;
     const int vb = __builtin_amdgcn_readfirstlane(blk * SL::AB);
 #pragma unroll
-    for (int c = 0; c < SL::NAV16; ++c) lds_dma16(rv, lds_addr(sp + SL::A_OFF + 1024 * c), 16 * lane, vb + 1024 * c);
+    for (int c = 0; c < SL::NAV16; ++c) lds_dma16(ra, lds_addr(sp + SL::A_OFF + 1024 * c), 16 * lane, vb + 1024 * c);
 #pragma unroll
     for (int c = 0; c < SL::NAV4; ++c)
-      lds_dma4(rv, lds_addr(sp + SL::A_OFF + 1024 * SL::NAV16 + 256 * c), 4 * lane, vb + 1024 * SL::NAV16 + 256 * c);
+      lds_dma4(ra, lds_addr(sp + SL::A_OFF + 1024 * SL::NAV16 + 256 * c), 4 * lane, vb + 1024 * SL::NAV16 + 256 * c);
     const int mbase = __builtin_amdgcn_readfirstlane(blk * 16 * RG::MRB);
 #pragma unroll
-    for (int c = 0; c < SL::NM4; ++c) lds_dma4(rm, lds_addr(sp + SL::M_OFF + 256 * c), 4 * lane, mbase + 256 * c);
+    for (int c = 0; c < SL::NM4; ++c) lds_dma4(rmm, lds_addr(sp + SL::M_OFF + 256 * c), 4 * lane, mbase + 256 * c);
   };
 
   // A: lane (i, g) reads its run at row i, offset g VB; its meta window

@@ -37,51 +37,9 @@ namespace nm {
 
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef int v2i __attribute__((ext_vector_type(2)));
 typedef _Float16 v16h __attribute__((ext_vector_type(16)));
 typedef __bf16 v16bf __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
-
-template <int N> struct ic { static constexpr int value = N; };
-
-__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
-
-// s_waitcnt immediate (gfx9): vmcnt bits 3:0 and 15:14, expcnt 6:4 (no
-// wait), lgkmcnt 11:8.
-constexpr int waitcnt(int vm, int lgkm) {
-  return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
-}
-
-__device__ __forceinline__ v4i make_rsrc(const void* p, int num_records) {
-  const uint64_t a = (uint64_t)(uintptr_t)p;
-  return v4i{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), num_records, 0x00020000};
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-// Direct-to-LDS buffer loads: lane l's bytes land at M0 + size * l; offsets
-// past num_records read as zero.  Completion is waited for explicitly.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(v4i rsrc, uint32_t lds, int voff, int soff) {
-  lds = __builtin_amdgcn_readfirstlane(lds);
-  soff = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(v4i rsrc, uint32_t lds, int voff, int soff) {
-  lds = __builtin_amdgcn_readfirstlane(lds);
-  soff = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ __forceinline__ v2i lds_tr16(const uint8_t* p) {
-  return __builtin_bit_cast(
-      v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p)));
-}
 
 constexpr int TN = 8;              // token tiles (16 tokens) per wave
 constexpr int BN = TN * 16;        // 128 tokens per tile
@@ -123,7 +81,6 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   constexpr int RB = 16 / NW;
   constexpr int BM = NW * RB * 16;
   constexpr int DPW = STAGE / 1024 / NW;     // 1 KB direct-to-LDS loads per wave per block
-  constexpr int NL = 2 * RB + DPW;           // loads per group (+1 bias on a tile's first block)
 
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs1[STAGE];
@@ -203,31 +160,40 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   tile_of(0, lr0, lt0, lks);
   lks *= kbs;                                // first column block of the slice
   int g_live = 0, g_rb0 = 0, g_soff = 0;
+  // No load has all its lanes outside its operand: row blocks past R, X
+  // rows past K, an absent bias and the groups issued past the end read the
+  // zero page instead (see nm_zero_page).
+  const __amdgpu_buffer_rsrc_t rzb = zero_brsrc();
+  const v4i rz = zero_rsrc();
   auto load_part = [&](auto st, auto part) {
     constexpr int S = decltype(st)::value;
     constexpr int P = decltype(part)::value;
     if constexpr (P == 0) {
       g_live = __builtin_amdgcn_readfirstlane(ln < total ? 1 : 0);
       g_rb0 = (lr0 >> 4) + RB * wave;
-      g_soff = __builtin_amdgcn_readfirstlane(g_live ? ((lks + lkb) * 64 * ldx + lt0) * 2 : (int)(g.K * a.ldx * 2));
+      g_soff = __builtin_amdgcn_readfirstlane(((lks + lkb) * 64 * ldx + lt0) * 2);
     }
     if constexpr (P < RB) {
-      const int rbc = __builtin_amdgcn_readfirstlane(min(g_rb0 + P, nRB));
-      const int blk = (g_live ? rbc : nRB) * nKB + (rbc < nRB ? lks + lkb : 0);
-      av[S][P] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, blk * 1024, 0));
-      ai[S][P] = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, voff_m, blk * 128, 0);
+      const int rb = g_rb0 + P;
+      const bool real = uniform(g_live && rb < nRB);
+      const int blk = __builtin_amdgcn_readfirstlane(real ? rb * nKB + lks + lkb : 0);
+      av[S][P] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(real ? rv : rzb, voff_v, blk * 1024, 0));
+      ai[S][P] = (int)__builtin_amdgcn_raw_buffer_load_b32(real ? rm : rzb, voff_m, blk * 128, 0);
     } else if constexpr (P == RB || P == RB + 1) {
       uint8_t* sp = xstage(st);
       constexpr int H = DPW / 2, J0 = (P - RB) * H;
 #pragma unroll
       for (int j = J0; j < J0 + H; ++j) {
         const int d = wave * DPW + j;
-        lds_dma16(rx, lds_addr(sp + d * 1024), xoff(j), g_soff);
+        // load d fills rows 4 d .. 4 d + 3 of the stage: all past K -> zeros
+        const bool real = uniform(g_live && (lks + lkb) * 64 + 4 * d < (int)g.K);
+        lds_dma16(real ? rx : rz, lds_addr(sp + d * 1024), real ? xoff(j) : 16 * lane, real ? g_soff : 0);
       }
     } else {
       if (g_live && lkb == 0) {
-        const int boff = __builtin_amdgcn_readfirstlane(4 * (lr0 + 16 * RB * wave));
-        lds_dma4(rbias, lds_addr(bsw + 256 * (lk & 3)), 4 * lane, boff);
+        const bool hb = uniform(a.bias && lr0 + 16 * RB * wave < (int)g.R);
+        const int boff = __builtin_amdgcn_readfirstlane(hb ? 4 * (lr0 + 16 * RB * wave) : 0);
+        lds_dma4(hb ? rbias : rz, lds_addr(bsw + 256 * (lk & 3)), 4 * lane, boff);
       }
       ++ln;
       if (g_live && ++lkb == kbs) {
@@ -390,14 +356,18 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   int n = 0, ck = 0, ckb = 0, cr0, ct0, cks;
   tile_of(0, cr0, ct0, cks);
 
-  // Wait until the oldest outstanding group has landed: every group holds
-  // at least NL loads and loads complete in order, so at most NL
-  // outstanding means everything before the newest group is in.  One
-  // unconditional count (not NL plus the next group's extra loads) keeps the
-  // wait a single instruction on every path through the unrolled steps.
+  // Wait until the stage of the oldest outstanding group (and a tile's bias
+  // rows) has landed.  Only direct-to-LDS loads are counted: they complete
+  // in issue order among themselves, but the register loads of a later
+  // group (A fragments hitting in L2) may complete before them, so a count
+  // that included those could pass with the stage still in flight.  Every
+  // group holds at least DPW of them, so at most DPW outstanding means every
+  // direct-to-LDS load before the newest group is in; the compiler's own
+  // waits cover the A registers.  One unconditional count keeps the wait a
+  // single instruction on every path through the unrolled steps.
   auto wait_for_group = [&](int extra_after) {
     (void)extra_after;
-    __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
+    __builtin_amdgcn_s_waitcnt(waitcnt(DPW, 15));
   };
 
   load_group(ic<0>());
@@ -421,13 +391,9 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     ++ck;
     if (ck < nmine) {
       tile_of(ck, cr0, ct0, cks);
-      // Drain every outstanding load and the epilogue's stores before the
-      // next tile starts.  The load-only count above is sufficient in
-      // principle, but on MI355X the first B reads of a workgroup's second
-      // tile (LLaMA-7B up-projection shape) were seen, rarely, to return
-      // stale stage data (two runs out of many); the full drain costs one
-      // memory round trip per tile.
-      __builtin_amdgcn_s_waitcnt(waitcnt(0, 15));
+      // the next tile's bias rows arrive with its first group, L(n); only
+      // the group after it (and the epilogue's stores) may still be in flight
+      wait_for_group(group_size_extra(n + 1));
       init_acc(ck);
     }
   };
@@ -441,18 +407,6 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   if (rest > 1) step(ic<1>());
   __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
 #endif
-}
-
-int cu_count(int device) {
-  static int cache[64];
-  if (device < 0 || device >= 64) return 256;
-  if (!cache[device]) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
-      cus = 256;
-    cache[device] = cus;
-  }
-  return cache[device];
 }
 
 template <int NW, int WT>
@@ -493,11 +447,6 @@ hipError_t launch_nw(const SpmmArgs& a, hipStream_t s) {
 // fp16 / bf16 2:4, 4-wave workgroups (256 x 128 tiles, two per CU)
 hipError_t launch_spmm_smfmac_h(const SpmmArgs& a, hipStream_t s) {
   return a.wdt == NM_F16 ? launch_nw<4, NM_F16>(a, s) : launch_nw<4, NM_BF16>(a, s);
-}
-
-// the same tiles with 8-wave workgroups (one per CU, two waves per SIMD)
-hipError_t launch_spmm_smfmac_h8(const SpmmArgs& a, hipStream_t s) {
-  return a.wdt == NM_F16 ? launch_nw<8, NM_F16>(a, s) : launch_nw<8, NM_BF16>(a, s);
 }
 
 }  // namespace nm

@@ -23,41 +23,9 @@ namespace nm {
 
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef int v2i __attribute__((ext_vector_type(2)));
 typedef _Float16 v16h __attribute__((ext_vector_type(16)));
 typedef __bf16 v16bf __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
-
-constexpr int waitcnt(int vm, int lgkm) {
-  return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
-}
-__device__ __forceinline__ v4i make_rsrc(const void* p, int num_records) {
-  const uint64_t a = (uint64_t)(uintptr_t)p;
-  return v4i{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), num_records, 0x00020000};
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(v4i rsrc, uint32_t lds, int voff, int soff) {
-  lds = __builtin_amdgcn_readfirstlane(lds);
-  soff = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(v4i rsrc, uint32_t lds, int voff, int soff) {
-  lds = __builtin_amdgcn_readfirstlane(lds);
-  soff = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-__device__ __forceinline__ v2i lds_tr16(const uint8_t* p) {
-  return __builtin_bit_cast(
-      v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p)));
-}
 
 template <int WT>
 __device__ __forceinline__ v4f smfmac(v4i a, v8i b, v4f c, int idx) {
@@ -112,17 +80,24 @@ __global__ void __launch_bounds__(NWD * 64) smfmac_hd_kernel(SpmmArgs a) {
   // index words: 128 bytes per block; lanes 32..63 repeat lanes 0..31
   const int moff = 4 * (lane & 31);
 
-  // group m (0 <= m < nblk: block kb0 + m; otherwise zeros) into slot m % D
+  // group m (0 <= m < nblk: block kb0 + m; otherwise zeros) into slot m % D.
+  // No load has all its lanes outside its operand: groups past the wave's
+  // last block, and X rows past K, read the zero page (see nm_zero_page), so
+  // every group is the same NLG in-order loads.
+  const v4i rz = zero_rsrc();
   auto issue = [&](int m, int s) {
-    const bool live = m < nblk;
+    const bool live = uniform(m < nblk);
     const int kb = kb0 + m;
     uint8_t* sp = ws + s * SLOT;
-    const int xs = __builtin_amdgcn_readfirstlane(live ? kb * 64 * ldx * 2 : (int)(g.K * a.ldx * 2));
-    lds_dma16(rx, lds_addr(sp), xoff[0], xs);
-    lds_dma16(rx, lds_addr(sp + 1024), xoff[1], xs);
-    const int blk = live ? rb * nKB + kb : (int)(g.nRB * g.nKB);
-    lds_dma16(rv, lds_addr(sp + 2048), 16 * lane, __builtin_amdgcn_readfirstlane(blk * 1024));
-    lds_dma4(rm, lds_addr(sp + 3072), moff, __builtin_amdgcn_readfirstlane(blk * 128));
+    const int xs = __builtin_amdgcn_readfirstlane(live ? kb * 64 * ldx * 2 : 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool xr = uniform(live && kb * 64 + 32 * j < (int)g.K);
+      lds_dma16(xr ? rx : rz, lds_addr(sp + 1024 * j), xr ? xoff[j] : 16 * lane, xr ? xs : 0);
+    }
+    const int blk = __builtin_amdgcn_readfirstlane(live ? rb * nKB + kb : 0);
+    lds_dma16(live ? rv : rz, lds_addr(sp + 2048), 16 * lane, blk * 1024);
+    lds_dma4(live ? rm : rz, lds_addr(sp + 3072), moff, blk * 128);
   };
 
   // B transpose reads: source lane 4 e + q reads row 8 g + e (+4, +32, +36),

@@ -52,52 +52,6 @@ namespace nm {
 
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef int v2i __attribute__((ext_vector_type(2)));
-
-template <int N> struct ic { static constexpr int value = N; };
-
-// Barrier without a memory fence (the waits that make data visible are
-// explicit); the memory clobber keeps memory accesses from moving across it.
-__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
-
-// s_waitcnt immediate (gfx9): vmcnt bits 3:0 and 15:14, expcnt 6:4 (no
-// wait), lgkmcnt 11:8.
-constexpr int waitcnt(int vm, int lgkm) {
-  return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
-}
-
-// Direct-to-LDS buffer loads: lane l's bytes land at M0 + size * l; offsets
-// past num_records read as zero.  Completion is waited for explicitly
-// (vmcnt, then a barrier).  M0 is written here; nothing else in these
-// kernels uses it.
-__device__ __forceinline__ v4i make_rsrc(const void* p, int num_records) {
-  const uint64_t a = (uint64_t)(uintptr_t)p;
-  return v4i{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), num_records, 0x00020000};
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(v4i rsrc, uint32_t lds, int voff, int soff) {
-  lds = __builtin_amdgcn_readfirstlane(lds);
-  soff = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(v4i rsrc, uint32_t lds, int voff, int soff) {
-  lds = __builtin_amdgcn_readfirstlane(lds);
-  soff = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ __forceinline__ v2i lds_tr8(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(p));
-}
-
 constexpr int RB = 4;              // row blocks (16 rows) per wave
 constexpr int TN = 8;              // token tiles (16 tokens) per wave
 constexpr int BN = TN * 16;        // 128 tokens per tile
@@ -114,7 +68,6 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   constexpr int DPW = STAGE / 1024 / NW;     // 1 KB direct-to-LDS loads per wave per block
   // one group of loads per block and wave: A values + meta, X (+ bias and
   // scale on a tile's first block)
-  constexpr int NL = 2 * RB + DPW;
 
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs1[STAGE];
@@ -186,6 +139,8 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   // 4, so a slot is rewritten only after its tile's epilogue; rows past R
   // and absent vectors read as zero.
   uint8_t* const bsw = bsbuf + wave * 2048;
+  // the same slot area as an LDS address (integer offsets from the array)
+  const uint32_t bs_lds = lds_addr(bsbuf) + wave * 2048;
   auto bias_vec = [&](int k, int rb) {
     return *reinterpret_cast<const v4i*>(bsw + 512 * (k & 3) + 4 * (16 * rb + 4 * lg));
   };
@@ -197,42 +152,52 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   // issued.  A group is issued in parts between the token tiles of a block:
   // part rb < RB the A fragment of row block rb, then the X loads in two
   // halves, then (first block of a tile) bias and scale.  Groups past the
-  // end (at most two) still issue their A and X loads, reading nothing but
-  // zeros into a stage and register set nobody reads again, so every group
-  // but a tile's first has the same size.
+  // end (at most two) still issue their A and X loads, from the zero page
+  // into a stage and register set nobody reads again, so every group but a
+  // tile's first has the same size.  No load has all its lanes outside its
+  // operand: row blocks past R, X rows past K, absent bias / scale and
+  // groups past the end read the zero page (see nm_zero_page).
   int ln = 0, lk = 0, lkb = 0, lr0 = 0, lt0 = 0;
   tile_of(0, lr0, lt0);
   int g_live = 0, g_rb0 = 0, g_soff = 0;
+  const __amdgpu_buffer_rsrc_t rzb = zero_brsrc();
+  const v4i rz = zero_rsrc();
   auto load_part = [&](auto st, auto part) {
     constexpr int S = decltype(st)::value;
     constexpr int P = decltype(part)::value;
     if constexpr (P == 0) {
       g_live = __builtin_amdgcn_readfirstlane(ln < total ? 1 : 0);
       g_rb0 = (lr0 >> 4) + RB * wave;
-      g_soff = __builtin_amdgcn_readfirstlane(g_live ? lkb * 128 * ldx + lt0 : (int)(g.K * a.ldx));
+      g_soff = __builtin_amdgcn_readfirstlane(lkb * 128 * ldx + lt0);
     }
     if constexpr (P < RB) {
       // A first: the compiler's waits for these registers may then hold
       // back at most later A loads, never an X stage.  Row blocks past the
-      // matrix read past the end (zeros).
-      const int rbc = __builtin_amdgcn_readfirstlane(min(g_rb0 + P, nRB));
-      const int blk = (g_live ? rbc : nRB) * nKB + (rbc < nRB ? lkb : 0);
-      av[S][P] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, blk * 1024, 0));
-      ai[S][P] = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, voff_m, blk * 256, 0);
+      // matrix read the zero page.
+      const int rb = g_rb0 + P;
+      const bool real = uniform(g_live && rb < nRB);
+      const int blk = __builtin_amdgcn_readfirstlane(real ? rb * nKB + lkb : 0);
+      av[S][P] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(real ? rv : rzb, voff_v, blk * 1024, 0));
+      ai[S][P] = (int)__builtin_amdgcn_raw_buffer_load_b32(real ? rm : rzb, voff_m, blk * 256, 0);
     } else if constexpr (P == RB || P == RB + 1) {
       uint8_t* sp = xstage(st);
       constexpr int H = DPW / 2, J0 = (P - RB) * H;
 #pragma unroll
       for (int j = J0; j < J0 + H; ++j) {
         const int d = wave * DPW + j;
-        lds_dma16(rx, lds_addr(sp + d * 1024), xoff(j), g_soff);
+        // load d fills rows 8 d .. 8 d + 7 of the stage: past K entirely ->
+        // zeros from the zero page (16 bytes per lane)
+        const bool real = uniform(g_live && lkb * 128 + 8 * d < (int)g.K);
+        lds_dma16(real ? rx : rz, lds_addr(sp + d * 1024), real ? xoff(j) : 16 * lane, real ? g_soff : 0);
       }
     } else {
       if (g_live && lkb == 0) {
-        uint8_t* bs = bsw + 512 * (lk & 3);
-        const int boff = __builtin_amdgcn_readfirstlane(4 * (lr0 + 64 * wave));
-        lds_dma4(rbias, lds_addr(bs), 4 * lane, boff);
-        lds_dma4(rscale, lds_addr(bs + 256), 4 * lane, boff);
+        const uint32_t bs = bs_lds + 512 * (lk & 3);
+        const bool rows_ok = uniform(lr0 + 64 * wave < (int)g.R);
+        const int boff = __builtin_amdgcn_readfirstlane(rows_ok ? 4 * (lr0 + 64 * wave) : 0);
+        const bool hb = uniform(rows_ok && a.bias), hs = uniform(rows_ok && a.scale);
+        lds_dma4(hb ? rbias : rz, bs, 4 * lane, hb ? boff : 0);
+        lds_dma4(hs ? rscale : rz, bs + 256, 4 * lane, hs ? boff : 0);
       }
       ++ln;
       if (g_live && ++lkb == nKB) {
@@ -247,7 +212,7 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     load_part(st, ic<4>()); load_part(st, ic<5>()); load_part(st, ic<6>());
   };
   static_assert(RB == 4 && NPART == 7, "load parts are spelled out for four row blocks");
-  // groups issued so far have sizes NL (plus 2 on a live tile's first block)
+  // direct-to-LDS loads per group: DPW (plus 2 on a live tile's first block)
   auto group_size_extra = [&](int m) { return (m < total && m % nKB == 0) ? 2 : 0; };
 
   v4i acc[RB][TN];
@@ -400,14 +365,18 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   int n = 0, ck = 0, ckb = 0, cr0, ct0;
   tile_of(0, cr0, ct0);
 
-  // wait until L(m) has landed, given the group issued after it (its
-  // size: NL, plus 2 when it starts a live tile); loads complete in order,
-  // and an epilogue's stores issued since only make the wait longer
+  // wait until the stage of L(m) (and a tile's bias / scale rows) has
+  // landed, given the group issued after it.  Only direct-to-LDS loads are
+  // counted: they complete in issue order among themselves, but register
+  // loads of a later group (A fragments hitting in L2) may complete before
+  // them, so a count that included those could pass with the stage still in
+  // flight.  The group after holds DPW of them, plus 2 when it starts a
+  // live tile; the compiler's own waits cover the A registers.
   auto wait_for_group = [&](int extra_after) {
     if (extra_after)
-      __builtin_amdgcn_s_waitcnt(waitcnt(NL + 2, 15));
+      __builtin_amdgcn_s_waitcnt(waitcnt(DPW + 2, 15));
     else
-      __builtin_amdgcn_s_waitcnt(waitcnt(NL, 15));
+      __builtin_amdgcn_s_waitcnt(waitcnt(DPW, 15));
   };
 
   load_group(ic<0>());
@@ -456,18 +425,6 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   if (rest > 1) step(ic<1>());
   __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
 #endif
-}
-
-int cu_count(int device) {
-  static int cache[64];
-  if (device < 0 || device >= 64) return 256;
-  if (!cache[device]) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
-      cus = 256;
-    cache[device] = cus;
-  }
-  return cache[device];
 }
 
 template <int NW>

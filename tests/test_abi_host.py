@@ -161,9 +161,8 @@ def _ws(d, T, ydt):
 def test_ksplit_choice_and_workspace(monkeypatch):
     """K split across workgroups: chosen for deep-K shapes with few output
     tiles, never for shapes that fill the GPU; the workspace query reports
-    the slices' partial sums; NM_SPMM_KSPLIT forces a divisor of the column
+    the slices' partial sums; NM_SPMM_VARIANT=":<S>" forces a divisor of the column
     blocks or turns the split off."""
-    monkeypatch.delenv("NM_SPMM_KSPLIT", raising=False)
     # Swin-T stage-4 MLP out-projection, fp16 2:4: 39 tiles, 48 column blocks
     deep = _desc(R=768, K=3072, dt=nm.NM_F16)
     S = _ksplit(deep, 1568, nm.NM_F16)
@@ -178,17 +177,17 @@ def test_ksplit_choice_and_workspace(monkeypatch):
     # decode shapes split K inside a workgroup instead
     assert _ksplit(deep, 16, nm.NM_F16) == 1
     assert _ksplit(deep, 0, nm.NM_F16) == 0
-    monkeypatch.setenv("NM_SPMM_KSPLIT", "3")
+    monkeypatch.setenv("NM_SPMM_VARIANT", ":3")
     assert _ksplit(deep, 1568, nm.NM_F16) == 3
     assert _ws(deep, 1568, nm.NM_F16) == 3 * 768 * 1568 * 4
-    monkeypatch.setenv("NM_SPMM_KSPLIT", "5")     # does not divide 48 blocks
+    monkeypatch.setenv("NM_SPMM_VARIANT", ":5")     # does not divide 48 blocks
     assert _ksplit(deep, 1568, nm.NM_F16) == 1
-    monkeypatch.setenv("NM_SPMM_KSPLIT", "1")
+    monkeypatch.setenv("NM_SPMM_VARIANT", ":1")
     assert _ksplit(deep, 1568, nm.NM_F16) == 1 and _ws(deep, 1568, nm.NM_F16) == 0
 
 
 def test_split_call_validates_its_workspace(monkeypatch):
-    monkeypatch.setenv("NM_SPMM_KSPLIT", "4")
+    monkeypatch.setenv("NM_SPMM_VARIANT", ":4")
     d = _desc(R=768, K=3072, dt=nm.NM_F16)
     need = _ws(d, 1568, nm.NM_F16)
     assert need == 4 * 768 * 1568 * 4
@@ -274,7 +273,6 @@ def test_repack24_choice_and_workspace(monkeypatch, N, M):
     copy's workspace; small products, fp16 weights (unless forced), N:M
     outside 2:4 and a forced N:M kernel do not."""
     monkeypatch.delenv("NM_SPMM_VARIANT", raising=False)
-    monkeypatch.delenv("NM_SPMM_KSPLIT", raising=False)
     L = nm.lib()
 
     def q(d, T, ydt):
@@ -312,7 +310,6 @@ def test_tk_transpose_choice_and_workspace(monkeypatch):
     (and split partials) in the workspace; small ones stay on the generic
     kernel."""
     monkeypatch.delenv("NM_SPMM_VARIANT", raising=False)
-    monkeypatch.delenv("NM_SPMM_KSPLIT", raising=False)
     L = nm.lib()
     tk = lambda d, T, y: L.nm_spmm_variant_tk(ctypes.byref(d), T, y, 0).decode()
 
@@ -347,3 +344,51 @@ def test_tk_workspace_size_validation():
     assert L.nm_spmm_tk_workspace_size(None, 16, nm.NM_I8, ctypes.byref(n)) == nm.NM_EINVAL
     assert L.nm_spmm_tk_workspace_size(ctypes.byref(_desc(R=64, K=64, N=4, M=8)), 16, nm.NM_I8,
                                        ctypes.byref(n)) == nm.NM_OK and n.value == 0
+
+
+def test_binding_rejects_mismatched_operands_before_any_call(monkeypatch):
+    """spmm() / linear() check dtypes, lengths and devices before touching the
+    library: a mismatch raises TypeError / ValueError and nothing is launched
+    (the library handle is poisoned here, so any call would fail loudly)."""
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+
+    def no_call():
+        raise AssertionError("the library was called")
+
+    monkeypatch.setattr(nm, "lib", no_call)
+    R, K, T = 16, 64, 8
+    vb, mb = 16 * 64 // 2 * 2, 16 * 16 // 1
+    p16 = nm.Packed(R, K, 2, 4, nm.NM_F16, torch.empty(vb, dtype=torch.uint8),
+                    torch.empty(mb, dtype=torch.uint8), nm.FORMAT_VERSION)
+    p8 = nm.Packed(R, K, 2, 4, nm.NM_I8, torch.empty(vb // 2, dtype=torch.uint8),
+                   torch.empty(mb, dtype=torch.uint8), nm.FORMAT_VERSION)
+    X16 = torch.zeros((K, T), dtype=torch.float16)
+    X8 = torch.zeros((K, T), dtype=torch.int8)
+    with pytest.raises(TypeError):
+        nm.spmm(p16, X8)                                             # activation dtype
+    with pytest.raises(TypeError):
+        nm.spmm(p16, torch.zeros((K, T), dtype=torch.float32))
+    with pytest.raises(TypeError):
+        nm.spmm(p8, X8, out=torch.empty((R, T), dtype=torch.int8), out_dtype=torch.int32,
+                scale=torch.ones(R))                                 # out tensor vs out dtype
+    with pytest.raises(TypeError):
+        nm.spmm(p16, X16, bias=torch.zeros(R, dtype=torch.float16))  # fp bias must be float32
+    with pytest.raises(TypeError):
+        nm.spmm(p8, X8, bias=torch.zeros(R, dtype=torch.float32))    # int8 bias must be int32
+    with pytest.raises(ValueError):
+        nm.spmm(p16, X16, bias=torch.zeros(R - 1, dtype=torch.float32))
+    with pytest.raises(TypeError):
+        nm.spmm(p8, X8, out_dtype=torch.int8, scale=torch.ones(R, dtype=torch.float64))
+    with pytest.raises(ValueError):
+        nm.spmm(p8, X8, out_dtype=torch.int8, scale=torch.ones(R + 3))
+    with pytest.raises(ValueError):
+        nm.spmm(p8, X8, out_dtype=torch.int8)                        # int8 output needs a scale
+    with pytest.raises(ValueError):
+        nm.spmm(p16, X16)                                            # weights not on a GPU
+    with pytest.raises(TypeError):
+        nm.linear(p16, torch.zeros((T, K), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        nm.linear(p16, torch.zeros((T, K), dtype=torch.float16), bias=torch.zeros(2 * R))
+    with pytest.raises(ValueError):
+        nm.pack(torch.zeros((R, K), dtype=torch.float16), 2, 4)      # W not on a GPU

@@ -61,6 +61,30 @@ def test_pack_matches_oracle(dt, N, M):
         assert oracle.check_padding(v, m, R, K, N, M, dt) == 0, (R, K)
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("N,M", [(1, 4), (2, 4), (3, 8), (4, 8)])
+def test_pack_nonfinite_matches_oracle(dt, N, M):
+    """Weights holding +-Inf and NaNs of several payloads and signs: the packed
+    selection equals the oracle's (NaN above Inf above finite, NaNs by
+    payload, sign ignored, ties to the lower position)."""
+    R, K = 24, 64
+    W = nm_inputs.normal((R, K), 0.02, dt, 9, "pack-nonfinite", N, M)
+    bits = W.view(np.uint16)
+    if dt == "f16":
+        specials = np.array([0x7C00, 0xFC00, 0x7E00, 0xFE00, 0x7C01, 0x7FFF, 0xFE01, 0x7BFF], np.uint16)
+    else:
+        specials = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x7F81, 0x7FFF, 0xFFC1, 0x7F7F], np.uint16)
+    rng = np.random.default_rng(11)
+    pos = rng.random((R, K)) < 0.3
+    bits[pos] = specials[rng.integers(0, len(specials), int(pos.sum()))]
+    _, p = run(W, np.zeros((K, 1), W.dtype), N, M, dt, dt)
+    v, m = packed_host(p)
+    vals, idx = oracle.read_packed(v, m, R, K, N, M, dt)
+    cv, ci = oracle.compress(W, N, M, dt)
+    assert np.array_equal(ci, idx)
+    assert np.array_equal(cv.view(np.uint8), vals.view(np.uint8))
+
+
 def test_pack_row_stride():
     import torch
     import semi_structured_sparse_nm_amd as nm
@@ -152,14 +176,60 @@ def _full_layers():
     return out
 
 
-@pytest.mark.parametrize("L", _full_layers(), ids=lambda L: L.name)
-def test_full_size_sampled_rows(L):
+# Multiply-adds (R K T N / M) up to which a full-size case is compared on
+# every output; the oracle's direct loop runs at tens of G multiply-adds per
+# second on the host's cores.
+FULL_COMPARE_MACS = 16e9
+
+
+def _full_size_rows(L):
+    """Output rows a full-size case compares: every row when the oracle's
+    cost allows, else a fixed set -- the first and last row of every 64-row
+    band (one wave's rows), and every row of each 256- or 512-row tile that is
+    some workgroup's second (or later) tile under the persistent kernels'
+    tile order (row tile fastest, XCD x owning a contiguous range of tiles,
+    one workgroup per 4-wave / 8-wave slot of 256 CUs)."""
+    if L.R * L.K * L.T * L.N / L.M <= FULL_COMPARE_MACS:
+        return np.arange(L.R)
+    rows = set()
+    for b0 in range(0, L.R, 64):
+        rows.update((b0, min(b0 + 63, L.R - 1)))
+    ntok = (L.T + 127) // 128
+    for BM, nwg in ((256, 64), (512, 32)):
+        mt = (L.R + BM - 1) // BM
+        ntot = mt * ntok
+        per_xcd = (ntot + 7) // 8
+        for x in range(8):
+            for L2 in range(x * per_xcd + nwg, min((x + 1) * per_xcd, ntot)):
+                r0 = (L2 % mt) * BM
+                rows.update(range(r0, min(r0 + BM, L.R)))
+    return np.array(sorted(rows))
+
+
+def _full_size_case(L, out=None):
+    out = out or L.out
     W, X, b, s = layer_case(L)
-    Y, _ = run(W, X, L.N, L.M, L.dt, L.out, bias=b, scale=s)
-    rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([[0, L.R - 1], rng.integers(0, L.R, 6)]))
-    ref = reference(W, X, L.N, L.M, L.dt, L.out, bias=b, scale=s, rows=rows)
-    compare(np.asarray(Y)[rows], ref, L.out, L.name)
+    Y, _ = run(W, X, L.N, L.M, L.dt, out, bias=b, scale=s)
+    rows = _full_size_rows(L)
+    whole = len(rows) == L.R
+    ref = reference(W, X, L.N, L.M, L.dt, out, bias=b, scale=s, rows=None if whole else rows)
+    compare(np.asarray(Y) if whole else np.asarray(Y)[rows], ref, out, f"{L.name} -> {out}")
+
+
+@pytest.mark.parametrize("L", _full_layers(), ids=lambda L: L.name)
+def test_full_size(L):
+    """Every workload shape at full size with the kernel nm_spmm picks for it
+    (the launch the benchmark times), on every output or on the rows of
+    _full_size_rows."""
+    _full_size_case(L)
+
+
+@pytest.mark.parametrize("L", [L for L in nm_inputs.config5() if L.dt == "bf16"], ids=lambda L: L.name)
+def test_full_size_bf16_in_f32_out(L):
+    """LLaMA-7B shapes with bf16 operands and fp32 output at the 2e-3
+    max-abs-normalised bar (one bf16 ulp of the output alone would exceed
+    it, so the bar is checked where the output is fp32)."""
+    _full_size_case(L, out="f32")
 
 
 TK_FULL = ["c2_vitb_fc1_1of4", "c2_vitb_fc2_2of8", "c2_vitb_fc1_4of8", "c3_swin_C96_fc1_2of4",
@@ -197,14 +267,27 @@ def test_tk_full_size_sampled_rows(name):
     assert np.all(Y[:, L.R:] == want), "writes beyond R"
 
 
-FAST_I8 = ["smfmac_i8_2of4_256x128", "smfmac_i8_2of4_persistent", "smfmac_i8_2of4_persistent_w8"]
+FAST_I8 = ["smfmac_i8_2of4_persistent", "smfmac_i8_2of4_persistent_w8"]
+
+
+def _set_forced(name=None, S=None):
+    """NM_SPMM_VARIANT=<variant>[:<S>], the library's one debug override:
+    set the variant part or the K-slice part, keeping the other."""
+    import os
+    cur = os.environ.get("NM_SPMM_VARIANT", "")
+    v, _, k = cur.partition(":")
+    if name is not None:
+        v = name
+    if S is not None:
+        k = str(S)
+    os.environ["NM_SPMM_VARIANT"] = v + (":" + k if k else "")
 
 
 @pytest.fixture
 def force_variant():
     import os
     old = os.environ.get("NM_SPMM_VARIANT")
-    yield lambda name: os.environ.__setitem__("NM_SPMM_VARIANT", name)
+    yield lambda name: _set_forced(name=name)
     if old is None:
         os.environ.pop("NM_SPMM_VARIANT", None)
     else:
@@ -228,7 +311,7 @@ def test_fast_i8_variants(force_variant, variant, out, R, K, T):
     assert np.all(Y[:, T:] == 5), "writes beyond T"
 
 
-FAST_H = ["smfmac_h_2of4_persistent", "smfmac_h_2of4_persistent_w8"]
+FAST_H = ["smfmac_h_2of4_persistent"]
 
 
 @pytest.mark.parametrize("variant", FAST_H)
@@ -278,7 +361,7 @@ EXPAND_NMS = [(1, 4), (3, 4), (4, 4), (1, 8), (2, 8), (4, 8), (8, 8)]
 EXPAND_SHAPES = [(300, 192, 144), (17, 8, 16), (259, 1288, 272)]
 
 
-EXPAND_VARIANTS = ["expand_mfma_persistent", "expand_mfma32_persistent"]
+EXPAND_VARIANTS = ["expand_mfma_persistent"]
 
 
 def _expand_case(force_variant, variant, dt, out, N, M, R, K, T, seed):
@@ -323,7 +406,7 @@ def test_expand_variant_more_shapes(force_variant, variant, dt, out, N, M, R, K,
 REPACK_NMS = [(1, 4), (1, 8), (2, 8)]
 REPACK_CASES = [("smfmac_i8_2of4_persistent", "i8", "i8"), ("smfmac_i8_2of4_persistent", "i8", "i32"),
                 ("smfmac_i8_2of4_persistent_w8", "i8", "i8"), ("smfmac_h_2of4_persistent", "f16", "f16"),
-                ("smfmac_h_2of4_persistent", "bf16", "f32"), ("smfmac_h_2of4_persistent_w8", "bf16", "bf16")]
+                ("smfmac_h_2of4_persistent", "bf16", "f32"), ("smfmac_h_2of4_persistent", "bf16", "bf16")]
 
 
 @pytest.mark.parametrize("inner,dt,out", REPACK_CASES)
@@ -441,41 +524,15 @@ def test_expand_decode_variant_more_shapes(force_variant, dt, out, N, M, R, K, T
     _expand_decode_case(force_variant, dt, out, N, M, R, K, T, 14)
 
 
-@pytest.mark.parametrize("out", ["i8", "i32"])
-@pytest.mark.parametrize("R,K,T", [(300, 192, 144), (520, 384, 400), (259, 512, 272), (64, 640, 32),
-                                   (1100, 768, 2000), (2000, 896, 4096), (700, 1000, 1008),
-                                   (3072, 768, 12608)])
-def test_stationary_i8_variant(force_variant, out, R, K, T):
-    """Weight-stationary int8 2:4 kernel forced: every column-block count it
-    takes (2..8, a partial last block), ragged rows, workgroup runs that
-    cross row blocks (weights reloaded mid-run), padded row strides."""
-    import torch
-    import semi_structured_sparse_nm_amd as nm
-    variant = "smfmac_i8_2of4_stationary"
-    force_variant(variant)
-    W, X, b, s = _inputs("i8", out, R, K, T, 2, 4, 15, f"stat-{out}-{R}-{K}-{T}")
-    p = nm.pack(torch.from_numpy(W).cuda(), 2, 4)
-    assert nm.variant(p, T, torch.int8 if out == "i8" else torch.int32) == variant
-    Y, _ = run(W, X, 2, 4, "i8", out, bias=b, scale=s, ldx_pad=32, ldy_pad=16 if out == "i8" else 3,
-               sentinel=5)
-    if R * T > 4_000_000:
-        rows = np.unique(np.concatenate([[0, R - 1], np.random.default_rng(3).integers(0, R, 40)]))
-        ref = reference(W, X, 2, 4, "i8", out, bias=b, scale=s, rows=rows)
-        compare(np.asarray(Y)[rows, :T], ref, out, variant)
-    else:
-        compare(Y[:, :T], reference(W, X, 2, 4, "i8", out, bias=b, scale=s), out, variant)
-    assert np.all(Y[:, T:] == 5), "writes beyond T"
-
-
 @pytest.fixture
 def force_ksplit():
     import os
-    old = os.environ.get("NM_SPMM_KSPLIT")
-    yield lambda S: os.environ.__setitem__("NM_SPMM_KSPLIT", str(S))
+    old = os.environ.get("NM_SPMM_VARIANT")
+    yield lambda S: _set_forced(S=S)
     if old is None:
-        os.environ.pop("NM_SPMM_KSPLIT", None)
+        os.environ.pop("NM_SPMM_VARIANT", None)
     else:
-        os.environ["NM_SPMM_KSPLIT"] = old
+        os.environ["NM_SPMM_VARIANT"] = old
 
 
 def _ksplit_case(force_variant, force_ksplit, variant, dt, out, N, M, R, K, T, S, ldy_pad, seed):
@@ -573,13 +630,6 @@ def test_gelu_repack24(force_variant, inner, dt, out, N, M, R, K, T):
 
 GELU_FP = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")]
 GELU_SHAPES = [(300, 192, 144), (259, 1280, 272)]
-
-
-@pytest.mark.parametrize("R,K,T", [(300, 192, 144), (259, 1024, 272), (520, 768, 400)])
-def test_gelu_i8_stationary(force_variant, R, K, T):
-    """int8 2:4 weight-stationary kernel (K <= 1024) with GELU fused between
-    the dequantising and the requantising scale."""
-    _gelu_case(force_variant, "smfmac_i8_2of4_stationary", "i8", "i8", 2, 4, R, K, T, 31)
 
 
 @pytest.mark.parametrize("dt,out", [("i8", "i8")] + GELU_FP)
