@@ -208,6 +208,29 @@ nm_status nm_spmm_tk(const nm_packed* w, const void* Xt, int64_t ldx, int64_t T,
                      int32_t y_dtype, const void* bias, const float* scale, int32_t act, float out_scale,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * nm_spmm_act without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  It allocates nothing: the workspace nm_spmm_act
+ * would take (K-split partial sums, a 2:4 re-pack of a 1:4 / 1:8 / 2:8 int8
+ * weight) is a scratch array of nm_spmm_noalloc_max_bytes() = 32 MiB that the
+ * library holds on each device it runs on until the process ends.  Same
+ * arguments, arithmetic and results as nm_spmm_act ([K][T] layout).  A call
+ * whose K split needs more partial-sum bytes than the scratch holds returns
+ * NM_EINVAL before launching anything; a re-pack copy that does not fit makes
+ * the call run the N:M kernel instead (same result).  No kernel relies on
+ * what an earlier call left in the scratch.  Every call on one device shares
+ * its scratch: calls that overlap on one device (different streams, threads
+ * without ordering) race and must be ordered by the caller.  NM_EHIP: the
+ * scratch's device address could not be obtained.
+ */
+nm_status nm_spmm_noalloc(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
+                          int32_t y_dtype, const void* bias, const float* scale, int32_t act, float out_scale,
+                          void* stream);
+
+/* Bytes of the scratch nm_spmm_noalloc uses (its maximum workspace). */
+size_t nm_spmm_noalloc_max_bytes(void);
+
 /* Static description of a status code (never NULL). */
 const char* nm_status_str(nm_status s);
 

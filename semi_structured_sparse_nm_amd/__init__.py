@@ -79,6 +79,10 @@ def lib() -> ctypes.CDLL:
         L.nm_spmm_tk.restype = ctypes.c_int
         L.nm_spmm_variant_tk.argtypes = [PP, I64, I32, I32]
         L.nm_spmm_variant_tk.restype = ctypes.c_char_p
+        L.nm_spmm_noalloc.argtypes = [PP, P, I64, I64, P, I64, I32, P, P, I32, ctypes.c_float, P]
+        L.nm_spmm_noalloc.restype = ctypes.c_int
+        L.nm_spmm_noalloc_max_bytes.argtypes = []
+        L.nm_spmm_noalloc_max_bytes.restype = SZ
         for f in ("nm_pack_size", "nm_pack", "nm_spmm_workspace_size", "nm_spmm"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -258,6 +262,30 @@ def spmm(p: Packed, X: torch.Tensor, bias: torch.Tensor | None = None,
                            _stream(X.device))
     _check(st, "nm_spmm_act" if act != "none" else "nm_spmm")
     return out
+
+
+def spmm_noalloc(p: Packed, X: torch.Tensor, out: torch.Tensor, bias: torch.Tensor | None = None,
+                 scale: torch.Tensor | None = None, act: str = "none", out_scale: float = 1.0) -> torch.Tensor:
+    """nm_spmm_noalloc: spmm() into a caller-given `out` with no allocation
+    at all (the library's per-device scratch replaces the workspace), for
+    code that cannot allocate, such as HIP graph capture."""
+    if X.dim() != 2 or X.stride(1) != 1 or X.shape[0] != p.K:
+        raise ValueError("X must be [K, T] with unit stride along T")
+    T = X.shape[1]
+    if out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (p.rows, T):
+        raise ValueError("out must be [R, T] with unit stride along T")
+    _check_operands(p, X, out, out.dtype, bias, scale, None)
+    d = p.desc()
+    st = lib().nm_spmm_noalloc(ctypes.byref(d), X.data_ptr(), X.stride(0), T, out.data_ptr(), out.stride(0),
+                               _TORCH_TO_NM[out.dtype], None if bias is None else bias.data_ptr(),
+                               None if scale is None else scale.data_ptr(), ACTS[act], float(out_scale),
+                               _stream(X.device))
+    _check(st, "nm_spmm_noalloc")
+    return out
+
+
+def noalloc_max_bytes() -> int:
+    return int(lib().nm_spmm_noalloc_max_bytes())
 
 
 def linear(p: Packed, Xt: torch.Tensor, bias: torch.Tensor | None = None,

@@ -10,6 +10,7 @@ using nm::Geometry;
 using nm::SpmmArgs;
 
 #include <atomic>
+#include <mutex>
 
 namespace nm {
 
@@ -638,7 +639,50 @@ nm_status spmm_call(const nm_packed* w, const void* X, int64_t ldx, int64_t T, v
 
 }  // namespace
 
+// ---- scratch for callers that cannot allocate (nm_spmm_noalloc).  One
+// copy of this array per device, held until the process ends.  In host code
+// its name is a host-side stand-in: every host use goes through the device
+// address hipGetSymbolAddress returns, cached per device.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::atomic<void*> g_scratch[64];
+std::mutex g_scratch_mu;
+
+// the calling thread's current device's copy of `scratch` (nullptr on error)
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
 extern "C" {
+
+nm_status nm_spmm_noalloc(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
+                          int32_t y_dtype, const void* bias, const float* scale, int32_t act, float out_scale,
+                          void* stream) {
+  void* ws = scratch_ptr();
+  if (!ws) return NM_EHIP;
+  // the plan of nm_spmm_act given kScratchBytes of workspace: a K split whose
+  // partial sums exceed it is rejected (NM_EINVAL); a re-pack or transpose
+  // copy that does not fit runs the plain kernel, as with any small workspace
+  return spmm_call(w, X, ldx, T, Y, ldy, y_dtype, bias, scale, act, out_scale, NM_LAYOUT_KT, ws, kScratchBytes,
+                   stream);
+}
+
+size_t nm_spmm_noalloc_max_bytes(void) { return kScratchBytes; }
 
 nm_status nm_spmm_act(const nm_packed* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
                       int32_t y_dtype, const void* bias, const float* scale, int32_t act, float out_scale,
