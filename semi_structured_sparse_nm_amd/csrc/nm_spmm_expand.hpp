@@ -161,26 +161,27 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   int g_live = 0, g_rb0 = 0, g_soff = 0;
   // group parts: 0, 1: A of row block 0, 1; 2, 3: X halves; 4: bias / scale
   // on a tile's first block and the cursor
-  // No load has all its lanes outside its operand: row blocks past R, X rows
-  // past K, absent bias / scale and the groups issued past the end read the
-  // zero page instead (see nm_zero_page); partly outside rows and tokens are
-  // in the vector offset, which the range check covers.
-  const __amdgpu_buffer_rsrc_t rzb = zero_brsrc();
+  // No load has all its lanes outside its operand (such a load returns at
+  // once, ahead of older loads; see nm_zero_page): row blocks past R and
+  // groups past the end read valid blocks (data nobody uses), X rows
+  // entirely past K and absent bias / scale rows read the zero page; rows
+  // and tokens partly outside are in the vector offset, which the range
+  // check covers.
   const v4i rz = zero_rsrc();
+  int g_krem = 0;
   auto load_part = [&](auto st, auto part) {
     constexpr int S = decltype(st)::value;
     constexpr int P = decltype(part)::value;
     if constexpr (P == 0) {
       g_live = __builtin_amdgcn_readfirstlane(ln < total ? 1 : 0);
-      g_rb0 = (lr0 >> 4) + RB * wave;
+      g_rb0 = __builtin_amdgcn_readfirstlane((lr0 >> 4) + RB * wave);
       g_soff = __builtin_amdgcn_readfirstlane(((lks + lkb) * (128 / EB) * ldx + lt0) * EB);
+      g_krem = __builtin_amdgcn_readfirstlane((int)g.K - (lks + lkb) * (128 / EB));
     }
     if constexpr (P < RB) {
-      const int rbr = g_rb0 + P;
-      const bool real = uniform(g_live && rbr < nRB);
-      const auto rv = real ? rvv : rzb;
-      const auto rm = real ? rmm : rzb;
-      const int blk = real ? rbr * nKB + lks + lkb : 0;
+      const auto rv = rvv;
+      const auto rm = rmm;
+      const int blk = __builtin_amdgcn_readfirstlane(min(g_rb0 + P, nRB - 1) * nKB + lks + lkb);
       const int vo = voff_v + blk * C_B * 16;
 #pragma unroll
       for (int c = 0; c < NVL; ++c) {
@@ -211,18 +212,25 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
 #pragma unroll
       for (int j = J0; j < J0 + H; ++j) {
         const int d = wave * DPW + j;
-        // load d fills rows (8 or 4) d .. of the stage: all past K -> zeros
-        const bool real = uniform(g_live && (lks + lkb) * (128 / EB) + (I8 ? 8 : 4) * d < (int)g.K);
-        lds_dma16(real ? rx : rz, lds_addr(sp + d * 1024), real ? xoff(j) + g_soff : 16 * lane, 0);
+        // load d fills rows (8 or 4) d .. of the stage
+        if ((I8 ? 8 : 4) * d < g_krem)
+          lds_dma16(rx, lds_addr(sp + d * 1024), xoff(j) + g_soff, 0);
+        else
+          lds_dma16(rz, lds_addr(sp + d * 1024), 16 * lane, 0);
       }
     } else {
       if (g_live && lkb == 0) {
         uint8_t* bs = bsw + 512 * (lk & 3);
-        const bool rows_ok = uniform(lr0 + 32 * wave < (int)g.R);
-        const bool hb = uniform(rows_ok && a.bias), hs = uniform(rows_ok && a.scale);
-        const int boff = 4 * (lr0 + 32 * wave + lane);
-        lds_dma4(hb ? rbias : rz, lds_addr(bs), hb ? boff : 4 * lane, 0);
-        lds_dma4(hs ? rscale : rz, lds_addr(bs + 256), hs ? boff : 4 * lane, 0);
+        const int row0 = __builtin_amdgcn_readfirstlane(lr0 + 32 * wave);
+        const int boff = 4 * (row0 + lane);
+        if (a.bias && row0 < (int)g.R)
+          lds_dma4(rbias, lds_addr(bs), boff, 0);
+        else
+          lds_dma4(rz, lds_addr(bs), 4 * lane, 0);
+        if (a.scale && row0 < (int)g.R)
+          lds_dma4(rscale, lds_addr(bs + 256), boff, 0);
+        else
+          lds_dma4(rz, lds_addr(bs + 256), 4 * lane, 0);
       }
       ++ln;
       if (g_live && ++lkb == kbs) {

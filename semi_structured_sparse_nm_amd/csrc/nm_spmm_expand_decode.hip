@@ -99,33 +99,36 @@ __global__ void __launch_bounds__(NWD * 64) expand_decode_kernel(SpmmArgs a) {
     }
   }
 
-  // group m (0 <= m < nblk: block kb0 + m; otherwise zeros) into slot m % D.
-  // No load has all its lanes outside its operand: groups past the wave's
-  // last block, and X rows past K, read the zero page (see nm_zero_page), so
-  // every group is the same NLG in-order loads.
+  // group m (0 <= m < nblk: block kb0 + m) into slot m % D.  No load has all
+  // its lanes outside its operand (such a load returns at once, ahead of
+  // older loads; see nm_zero_page): groups past the wave's last block re-read
+  // a valid block into a slot nobody reads, X rows entirely past K read the
+  // zero page, so every group is the same NLG in-order loads.
   const v4i rz = zero_rsrc();
+  const int kb_last = min(max(kb1 - 1, kb0), nKB - 1);
+  constexpr int XROWS = I8 ? 64 : 32;   // k rows one X load covers
   auto issue = [&](int m, int s) {
-    const bool live = uniform(m < nblk);
-    const int kb = kb0 + m;
+    const int kb = __builtin_amdgcn_readfirstlane(m < nblk ? kb0 + m : kb_last);
+    const int krem = __builtin_amdgcn_readfirstlane((int)g.K - kb * (128 / EB));
     uint8_t* sp = ws + s * SL::BYTES;
-    const int xs = __builtin_amdgcn_readfirstlane(live ? kb * (128 / EB) * ldx * EB : 0);
-    constexpr int XROWS = I8 ? 64 : 32;   // k rows one X load covers
+    const int xs = __builtin_amdgcn_readfirstlane(kb * (128 / EB) * ldx * EB);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const bool xr = uniform(live && kb * (128 / EB) + XROWS * j < (int)g.K);
-      lds_dma16(xr ? rx : rz, lds_addr(sp + 1024 * j), xr ? xoff[j] : 16 * lane, xr ? xs : 0);
+      if (XROWS * j < krem)
+        lds_dma16(rx, lds_addr(sp + 1024 * j), xoff[j], xs);
+      else
+        lds_dma16(rz, lds_addr(sp + 1024 * j), 16 * lane, 0);
     }
-    const v4i ra = live ? rv : rz, rmm = live ? rm : rz;
-    const int blk = live ? rb * nKB + kb : 0;
+    const int blk = rb * nKB + kb;
     const int vb = __builtin_amdgcn_readfirstlane(blk * SL::AB);
 #pragma unroll
-    for (int c = 0; c < SL::NAV16; ++c) lds_dma16(ra, lds_addr(sp + SL::A_OFF + 1024 * c), 16 * lane, vb + 1024 * c);
+    for (int c = 0; c < SL::NAV16; ++c) lds_dma16(rv, lds_addr(sp + SL::A_OFF + 1024 * c), 16 * lane, vb + 1024 * c);
 #pragma unroll
     for (int c = 0; c < SL::NAV4; ++c)
-      lds_dma4(ra, lds_addr(sp + SL::A_OFF + 1024 * SL::NAV16 + 256 * c), 4 * lane, vb + 1024 * SL::NAV16 + 256 * c);
+      lds_dma4(rv, lds_addr(sp + SL::A_OFF + 1024 * SL::NAV16 + 256 * c), 4 * lane, vb + 1024 * SL::NAV16 + 256 * c);
     const int mbase = __builtin_amdgcn_readfirstlane(blk * 16 * RG::MRB);
 #pragma unroll
-    for (int c = 0; c < SL::NM4; ++c) lds_dma4(rmm, lds_addr(sp + SL::M_OFF + 256 * c), 4 * lane, mbase + 256 * c);
+    for (int c = 0; c < SL::NM4; ++c) lds_dma4(rm, lds_addr(sp + SL::M_OFF + 256 * c), 4 * lane, mbase + 256 * c);
   };
 
   // A: lane (i, g) reads its run at row i, offset g VB; its meta window

@@ -160,40 +160,44 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   tile_of(0, lr0, lt0, lks);
   lks *= kbs;                                // first column block of the slice
   int g_live = 0, g_rb0 = 0, g_soff = 0;
-  // No load has all its lanes outside its operand: row blocks past R, X
-  // rows past K, an absent bias and the groups issued past the end read the
-  // zero page instead (see nm_zero_page).
-  const __amdgpu_buffer_rsrc_t rzb = zero_brsrc();
+  // No load has all its lanes outside its operand (such a load returns at
+  // once, ahead of older loads; see nm_zero_page): row blocks past R and
+  // groups past the end read valid blocks (data nobody uses), X rows
+  // entirely past K and absent bias rows read the zero page.
   const v4i rz = zero_rsrc();
+  int g_krem = 0;
   auto load_part = [&](auto st, auto part) {
     constexpr int S = decltype(st)::value;
     constexpr int P = decltype(part)::value;
     if constexpr (P == 0) {
       g_live = __builtin_amdgcn_readfirstlane(ln < total ? 1 : 0);
-      g_rb0 = (lr0 >> 4) + RB * wave;
+      g_rb0 = __builtin_amdgcn_readfirstlane((lr0 >> 4) + RB * wave);
       g_soff = __builtin_amdgcn_readfirstlane(((lks + lkb) * 64 * ldx + lt0) * 2);
+      g_krem = __builtin_amdgcn_readfirstlane((int)g.K - (lks + lkb) * 64);   // rows of this block inside K
     }
     if constexpr (P < RB) {
-      const int rb = g_rb0 + P;
-      const bool real = uniform(g_live && rb < nRB);
-      const int blk = __builtin_amdgcn_readfirstlane(real ? rb * nKB + lks + lkb : 0);
-      av[S][P] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(real ? rv : rzb, voff_v, blk * 1024, 0));
-      ai[S][P] = (int)__builtin_amdgcn_raw_buffer_load_b32(real ? rm : rzb, voff_m, blk * 128, 0);
+      const int blk = __builtin_amdgcn_readfirstlane(min(g_rb0 + P, nRB - 1) * nKB + lks + lkb);
+      av[S][P] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, blk * 1024, 0));
+      ai[S][P] = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, voff_m, blk * 128, 0);
     } else if constexpr (P == RB || P == RB + 1) {
       uint8_t* sp = xstage(st);
       constexpr int H = DPW / 2, J0 = (P - RB) * H;
 #pragma unroll
       for (int j = J0; j < J0 + H; ++j) {
         const int d = wave * DPW + j;
-        // load d fills rows 4 d .. 4 d + 3 of the stage: all past K -> zeros
-        const bool real = uniform(g_live && (lks + lkb) * 64 + 4 * d < (int)g.K);
-        lds_dma16(real ? rx : rz, lds_addr(sp + d * 1024), real ? xoff(j) : 16 * lane, real ? g_soff : 0);
+        // load d fills rows 4 d .. 4 d + 3 of the stage
+        if (4 * d < g_krem)
+          lds_dma16(rx, lds_addr(sp + d * 1024), xoff(j), g_soff);
+        else
+          lds_dma16(rz, lds_addr(sp + d * 1024), 16 * lane, 0);
       }
     } else {
       if (g_live && lkb == 0) {
-        const bool hb = uniform(a.bias && lr0 + 16 * RB * wave < (int)g.R);
-        const int boff = __builtin_amdgcn_readfirstlane(hb ? 4 * (lr0 + 16 * RB * wave) : 0);
-        lds_dma4(hb ? rbias : rz, lds_addr(bsw + 256 * (lk & 3)), 4 * lane, boff);
+        const int row0 = __builtin_amdgcn_readfirstlane(lr0 + 16 * RB * wave);
+        if (a.bias && row0 < (int)g.R)
+          lds_dma4(rbias, lds_addr(bsw + 256 * (lk & 3)), 4 * lane, 4 * row0);
+        else
+          lds_dma4(rz, lds_addr(bsw + 256 * (lk & 3)), 4 * lane, 0);
       }
       ++ln;
       if (g_live && ++lkb == kbs) {

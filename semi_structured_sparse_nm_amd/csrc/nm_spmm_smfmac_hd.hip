@@ -80,24 +80,28 @@ __global__ void __launch_bounds__(NWD * 64) smfmac_hd_kernel(SpmmArgs a) {
   // index words: 128 bytes per block; lanes 32..63 repeat lanes 0..31
   const int moff = 4 * (lane & 31);
 
-  // group m (0 <= m < nblk: block kb0 + m; otherwise zeros) into slot m % D.
-  // No load has all its lanes outside its operand: groups past the wave's
-  // last block, and X rows past K, read the zero page (see nm_zero_page), so
-  // every group is the same NLG in-order loads.
+  // group m (0 <= m < nblk: block kb0 + m) into slot m % D.  No load has all
+  // its lanes outside its operand (such a load returns at once, ahead of
+  // older loads; see nm_zero_page): groups past the wave's last block re-read
+  // a valid block into a slot nobody reads, X rows entirely past K read the
+  // zero page, so every group is the same NLG in-order loads.
   const v4i rz = zero_rsrc();
+  const int kb_last = min(max(kb1 - 1, kb0), nKB - 1);
   auto issue = [&](int m, int s) {
-    const bool live = uniform(m < nblk);
-    const int kb = kb0 + m;
+    const int kb = __builtin_amdgcn_readfirstlane(m < nblk ? kb0 + m : kb_last);
+    const int krem = __builtin_amdgcn_readfirstlane((int)g.K - kb * 64);
     uint8_t* sp = ws + s * SLOT;
-    const int xs = __builtin_amdgcn_readfirstlane(live ? kb * 64 * ldx * 2 : 0);
+    const int xs = __builtin_amdgcn_readfirstlane(kb * 64 * ldx * 2);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const bool xr = uniform(live && kb * 64 + 32 * j < (int)g.K);
-      lds_dma16(xr ? rx : rz, lds_addr(sp + 1024 * j), xr ? xoff[j] : 16 * lane, xr ? xs : 0);
+      if (32 * j < krem)
+        lds_dma16(rx, lds_addr(sp + 1024 * j), xoff[j], xs);
+      else
+        lds_dma16(rz, lds_addr(sp + 1024 * j), 16 * lane, 0);
     }
-    const int blk = __builtin_amdgcn_readfirstlane(live ? rb * nKB + kb : 0);
-    lds_dma16(live ? rv : rz, lds_addr(sp + 2048), 16 * lane, blk * 1024);
-    lds_dma4(live ? rm : rz, lds_addr(sp + 3072), moff, blk * 128);
+    const int blk = rb * nKB + kb;
+    lds_dma16(rv, lds_addr(sp + 2048), 16 * lane, blk * 1024);
+    lds_dma4(rm, lds_addr(sp + 3072), moff, blk * 128);
   };
 
   // B transpose reads: source lane 4 e + q reads row 8 g + e (+4, +32, +36),

@@ -152,52 +152,57 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   // issued.  A group is issued in parts between the token tiles of a block:
   // part rb < RB the A fragment of row block rb, then the X loads in two
   // halves, then (first block of a tile) bias and scale.  Groups past the
-  // end (at most two) still issue their A and X loads, from the zero page
-  // into a stage and register set nobody reads again, so every group but a
-  // tile's first has the same size.  No load has all its lanes outside its
-  // operand: row blocks past R, X rows past K, absent bias / scale and
-  // groups past the end read the zero page (see nm_zero_page).
+  // end (at most two) still issue their A and X loads, at the last block's
+  // addresses, into a stage and register set nobody reads again, so every
+  // group but a tile's first has the same number of direct-to-LDS loads.
+  // No load has all its lanes outside its operand (such a load returns at
+  // once, ahead of older loads; see nm_zero_page): row blocks past R read
+  // the last row block, X rows entirely past K read the zero page, absent
+  // bias / scale rows too.
   int ln = 0, lk = 0, lkb = 0, lr0 = 0, lt0 = 0;
   tile_of(0, lr0, lt0);
-  int g_live = 0, g_rb0 = 0, g_soff = 0;
-  const __amdgpu_buffer_rsrc_t rzb = zero_brsrc();
+  int g_live = 0, g_rb0 = 0, g_soff = 0, g_krem = 0;
   const v4i rz = zero_rsrc();
   auto load_part = [&](auto st, auto part) {
     constexpr int S = decltype(st)::value;
     constexpr int P = decltype(part)::value;
     if constexpr (P == 0) {
       g_live = __builtin_amdgcn_readfirstlane(ln < total ? 1 : 0);
-      g_rb0 = (lr0 >> 4) + RB * wave;
+      g_rb0 = __builtin_amdgcn_readfirstlane((lr0 >> 4) + RB * wave);
       g_soff = __builtin_amdgcn_readfirstlane(lkb * 128 * ldx + lt0);
+      g_krem = __builtin_amdgcn_readfirstlane((int)g.K - lkb * 128);   // rows of this block inside K
     }
     if constexpr (P < RB) {
       // A first: the compiler's waits for these registers may then hold
-      // back at most later A loads, never an X stage.  Row blocks past the
-      // matrix read the zero page.
-      const int rb = g_rb0 + P;
-      const bool real = uniform(g_live && rb < nRB);
-      const int blk = __builtin_amdgcn_readfirstlane(real ? rb * nKB + lkb : 0);
-      av[S][P] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(real ? rv : rzb, voff_v, blk * 1024, 0));
-      ai[S][P] = (int)__builtin_amdgcn_raw_buffer_load_b32(real ? rm : rzb, voff_m, blk * 256, 0);
+      // back at most later A loads, never an X stage.
+      const int blk = __builtin_amdgcn_readfirstlane(min(g_rb0 + P, nRB - 1) * nKB + lkb);
+      av[S][P] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, blk * 1024, 0));
+      ai[S][P] = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, voff_m, blk * 256, 0);
     } else if constexpr (P == RB || P == RB + 1) {
       uint8_t* sp = xstage(st);
       constexpr int H = DPW / 2, J0 = (P - RB) * H;
 #pragma unroll
       for (int j = J0; j < J0 + H; ++j) {
         const int d = wave * DPW + j;
-        // load d fills rows 8 d .. 8 d + 7 of the stage: past K entirely ->
-        // zeros from the zero page (16 bytes per lane)
-        const bool real = uniform(g_live && lkb * 128 + 8 * d < (int)g.K);
-        lds_dma16(real ? rx : rz, lds_addr(sp + d * 1024), real ? xoff(j) : 16 * lane, real ? g_soff : 0);
+        // load d fills rows 8 d .. 8 d + 7 of the stage
+        if (8 * d < g_krem)
+          lds_dma16(rx, lds_addr(sp + d * 1024), xoff(j), g_soff);
+        else
+          lds_dma16(rz, lds_addr(sp + d * 1024), 16 * lane, 0);
       }
     } else {
       if (g_live && lkb == 0) {
         const uint32_t bs = bs_lds + 512 * (lk & 3);
-        const bool rows_ok = uniform(lr0 + 64 * wave < (int)g.R);
-        const int boff = __builtin_amdgcn_readfirstlane(rows_ok ? 4 * (lr0 + 64 * wave) : 0);
-        const bool hb = uniform(rows_ok && a.bias), hs = uniform(rows_ok && a.scale);
-        lds_dma4(hb ? rbias : rz, bs, 4 * lane, hb ? boff : 0);
-        lds_dma4(hs ? rscale : rz, bs + 256, 4 * lane, hs ? boff : 0);
+        const int row0 = __builtin_amdgcn_readfirstlane(lr0 + 64 * wave);
+        const int boff = 4 * row0;
+        if (a.bias && row0 < (int)g.R)
+          lds_dma4(rbias, bs, 4 * lane, boff);
+        else
+          lds_dma4(rz, bs, 4 * lane, 0);
+        if (a.scale && row0 < (int)g.R)
+          lds_dma4(rscale, bs + 256, 4 * lane, boff);
+        else
+          lds_dma4(rz, bs + 256, 4 * lane, 0);
       }
       ++ln;
       if (g_live && ++lkb == nKB) {
