@@ -64,6 +64,8 @@ def _load():
         L.orc_check_padding.argtypes = [P, P, I64, I64, I, I, I]
         L.orc_check_padding.restype = ctypes.c_int64
         L.orc_max_threads.argtypes = []
+        L.orc_hy_encode.argtypes = [P, I64, I64, I64, I, P, P, P, P, P, I64, P]
+        L.orc_hy_read.argtypes = [P, P, P, P, P, I64, I64, I, P]
         _lib = L
     return _lib
 
@@ -199,6 +201,54 @@ def check_padding(values, meta, R: int, K: int, N: int, M: int, dt: str) -> int:
     if n < 0:
         raise ValueError("oracle check_padding rejected its arguments")
     return int(n)
+
+
+def hy_geometry(R: int, K: int):
+    """(nRB, nKB, nSeg) of the three-layer format."""
+    nRB, nKB = (R + 15) // 16, (K + 63) // 64
+    return nRB, nKB, (nKB + 7) // 8
+
+
+def hy_encode(W, dt: str):
+    """Three-layer image (Sparse-TC 2:4, slot filling with PDD codes, CSR
+    residual) of raw fp16 / bf16 weights: dict of uint8 / int32 / uint32
+    arrays 'values', 'meta', 'codes', 'res_ptr', 'res_ent'."""
+    if dt not in ("f16", "bf16"):
+        raise ValueError(dt)
+    Wb = np.ascontiguousarray(W).view(np.uint16)
+    R, K = Wb.shape
+    nRB, nKB, nSeg = hy_geometry(R, K)
+    img = {"values": np.empty(nRB * nKB * 1024, np.uint8),
+           "meta": np.empty(nRB * nKB * 128, np.uint8),
+           "codes": np.empty(nRB * nSeg * 512, np.uint8),
+           "res_ptr": np.empty(nRB * nSeg * 16 + 1, np.int32)}
+    n = ctypes.c_int64(0)
+    args = lambda ent, cap: (_ptr(Wb), K, R, K, _DT[dt], _ptr(img["values"]), _ptr(img["meta"]),
+                             _ptr(img["codes"]), _ptr(img["res_ptr"]), _ptr(ent), cap,
+                             ctypes.byref(n))
+    rc = _load().orc_hy_encode(*args(None, 0))
+    if rc < 0:
+        raise ValueError("oracle hy_encode rejected its arguments")
+    ent = np.empty(max(n.value, 1), np.uint32)
+    _ok(_load().orc_hy_encode(*args(ent, n.value)), "hy_encode")
+    img["res_ent"] = ent[:n.value]
+    return img
+
+
+def hy_read(img, R: int, K: int, dt: str):
+    """Dense raw bits (uint16, R x K) rebuilt from a three-layer image."""
+    W = np.empty((R, K), np.uint16)
+    ent = img["res_ent"] if len(img["res_ent"]) else np.zeros(1, np.uint32)
+    rc = _load().orc_hy_read(_ptr(np.ascontiguousarray(img["values"]).view(np.uint8)),
+                             _ptr(np.ascontiguousarray(img["meta"]).view(np.uint8)),
+                             _ptr(np.ascontiguousarray(img["codes"]).view(np.uint8)),
+                             _ptr(np.ascontiguousarray(img["res_ptr"], dtype=np.int32)),
+                             _ptr(np.ascontiguousarray(ent, dtype=np.uint32)), R, K, _DT[dt],
+                             _ptr(W))
+    if rc == -2:
+        raise ValueError("inconsistent three-layer image")
+    _ok(rc, "hy_read")
+    return W
 
 
 def max_threads() -> int:

@@ -444,3 +444,273 @@ int orc_max_threads(void) {
   return 1;
 #endif
 }
+
+/* ====================================================================
+ * Three-layer format for moderately unstructured fp16 / bf16 weights
+ * (page "Accelerating GPU Inference of Large Language Models with
+ * Moderately Unstructured Sparse Weight Matrices", Methodology 1: a
+ * Sparse-TC 2:4 layer with 2-bit positions, a Slot-Filling layer whose
+ * elements sit in the empty 2:4 slots with 4-bit relative distances (PDD)
+ * and dummy points for long gaps, and a CSR residual layer).
+ *
+ * Written from this prose description of the byte image, independently of
+ * the library's packer:
+ *   nRB = ceil(R/16), nKB = ceil(K/64), nSeg = ceil(nKB/8).  Column block kb
+ *   = columns 64kb..64kb+63; segment s = blocks 8s .. min(8s+8, nKB)-1.
+ *   Rows >= R and columns >= K are zero.  A group is 4 columns 4g..4g+3.
+ *   Fill unit (r, s, q), q = 0..3: in every block kb of segment s the 16
+ *   columns 64kb+16q .. +15.  Its local column u = 16 (kb - 8s) + (c mod 16);
+ *   its slots sigma = 8 (kb - 8s) + 2 t + j for group t = 0..3 of the quad and
+ *   slot j = 0, 1.
+ *   Layer 1 (values, meta) in the 2:4 packed layout: block rb*nKB+kb at
+ *   1024 B (values) / 128 B (meta); row rr at 64 B / 8 B; group gb (0..15) of
+ *   the block has slots 2gb, 2gb+1, value at 2 bytes each, 2-bit position at
+ *   bits 2c..2c+1 of the row's 64-bit little-endian meta word.
+ *     nz >= 2 nonzeros (bits & 0x7FFF != 0): the two ranked highest by the
+ *       selection order (sel_key / sel_beats; ties to the lower column), in
+ *       ascending column order, positions i0 < i1.
+ *     nz == 1 at p: slot 0 = w_p at p; slot 1 empty, position p.
+ *     nz == 0: both empty, positions 1 (slot 0) and 0 (slot 1).
+ *   Surplus = nonzeros of groups with nz >= 3 that layer 1 does not hold.
+ *   Layer 2 (codes): 8 bytes per fill unit at ((rb*nSeg + s)*64 + 16q + rr)*8,
+ *   sixteen 4-bit codes, code i in bits 4(i%2) of byte i/2.  Greedy over the
+ *   unit's surplus in ascending u, prev = -1, used = 0, f = 0, E = number of
+ *   empty slots: d = u - prev, n0 = (d-1)/15; if f < E and used+n0+1 <= 16:
+ *   n0 codes 0 (dummy point: advance 15, no value), then code d - 15 n0, the
+ *   value goes to the f-th empty slot in ascending sigma, f++, prev = u;
+ *   otherwise the element goes to layer 3.  Unused codes are 0.  Empty slots
+ *   not filled hold +0.
+ *   Layer 3 (res_ptr, res_ent): CSR over segment rows z = (rb*nSeg + s)*16 +
+ *   rr; res_ptr[0] = 0, res_ptr[z+1] - res_ptr[z] entries of row z in
+ *   ascending column, each (column - 512 s) << 16 | value bits.
+ * ==================================================================== */
+
+static int hy_nonzero(const uint16_t* W, int64_t ldw, int64_t R, int64_t K, int64_t r, int64_t c) {
+  if (r >= R || c >= K) return 0;
+  return (W[r * ldw + c] & 0x7FFF) != 0;
+}
+
+static uint16_t hy_at(const uint16_t* W, int64_t ldw, int64_t R, int64_t K, int64_t r, int64_t c) {
+  return (r < R && c < K) ? W[r * ldw + c] : 0;
+}
+
+/* which layer holds each element: 0 zero, 1 Sparse-TC, 2 slot-filled,
+ * 3 residual (layer[r*K + c]); also per fill unit the codes, and per empty
+ * slot the filled value.  Shared by the byte-image writer below. */
+typedef struct {
+  int64_t R, K, nRB, nKB, nSeg;
+} hy_geo_t;
+
+static hy_geo_t hy_geo(int64_t R, int64_t K) {
+  hy_geo_t g;
+  g.R = R; g.K = K;
+  g.nRB = (R + 15) / 16;
+  g.nKB = (K + 63) / 64;
+  g.nSeg = (g.nKB + 7) / 8;
+  return g;
+}
+
+/*
+ * orc_hy_encode: write the byte image of W (raw fp16 / bf16 bits, row stride
+ * ldw).  values / meta / codes must hold nRB*nKB*1024, nRB*nKB*128 and
+ * nRB*nSeg*512 bytes, res_ptr nRB*nSeg*16 + 1 int32.  res_ent receives at
+ * most cap entries; *n_res is set to the number needed either way (call with
+ * cap 0 to size it).  Returns 0, -1 on bad arguments, 1 if cap was short.
+ */
+int orc_hy_encode(const uint16_t* W, int64_t ldw, int64_t R, int64_t K, int dt, uint8_t* values,
+                  uint8_t* meta, uint8_t* codes, int32_t* res_ptr, uint32_t* res_ent, int64_t cap,
+                  int64_t* n_res) {
+  if (R < 1 || K < 4 || K % 4 || ldw < K || (dt != ORC_F16 && dt != ORC_BF16)) return -1;
+  hy_geo_t g = hy_geo(R, K);
+  memset(values, 0, (size_t)(g.nRB * g.nKB * 1024));
+  memset(meta, 0, (size_t)(g.nRB * g.nKB * 128));
+  memset(codes, 0, (size_t)(g.nRB * g.nSeg * 512));
+  /* residual elements per segment row, collected column-sorted afterwards */
+  const int64_t nz_rows = g.nRB * g.nSeg * 16;
+  int64_t total = 0;
+  res_ptr[0] = 0;
+  for (int64_t rb = 0; rb < g.nRB; ++rb)
+    for (int64_t s = 0; s < g.nSeg; ++s)
+      for (int64_t rr = 0; rr < 16; ++rr) {
+        const int64_t r = rb * 16 + rr;
+        const int64_t kb0 = 8 * s, kb1 = (8 * s + 8 < g.nKB) ? 8 * s + 8 : g.nKB;
+        /* residual columns of this segment row, one flag per column */
+        uint8_t resflag[512];
+        uint16_t resval[512];
+        memset(resflag, 0, sizeof resflag);
+        for (int q = 0; q < 4; ++q) {
+          /* pass 1: layer 1 of every group of the unit, empty slots, surplus */
+          int64_t slot_col[64];     /* dense column of each slot's element, -1 if empty */
+          int empty_sigma[64], E = 0;
+          int sur_u[64], S = 0;
+          uint16_t sur_v[64];
+          const int nb = (int)(kb1 - kb0);
+          for (int sg = 0; sg < 64; ++sg) slot_col[sg] = -1;
+          for (int bi = 0; bi < nb; ++bi)
+            for (int t = 0; t < 4; ++t) {
+              const int64_t kb = kb0 + bi;
+              const int gb = 4 * q + t;                 /* group within the block */
+              const int64_t c0 = 64 * kb + 4 * gb;      /* first column of the group */
+              int nzc = 0;
+              for (int p = 0; p < 4; ++p) nzc += hy_nonzero(W, ldw, R, K, r, c0 + p);
+              int sel[2] = {-1, -1}, pos[2];
+              if (nzc >= 2) {
+                /* rank = number of group members that beat p (ties: lower
+                 * column first); the two with rank 0 and 1 are selected */
+                for (int p = 0; p < 4; ++p) {
+                  if (!hy_nonzero(W, ldw, R, K, r, c0 + p)) continue;
+                  sel_key_t kp = sel_key(W, dt, r * ldw + c0 + p);
+                  int rank = 0;
+                  for (int o = 0; o < 4; ++o) {
+                    if (o == p || !hy_nonzero(W, ldw, R, K, r, c0 + o)) continue;
+                    sel_key_t ko = sel_key(W, dt, r * ldw + c0 + o);
+                    if (sel_beats(ko, kp) || (!sel_beats(kp, ko) && o < p)) ++rank;
+                  }
+                  if (rank < 2) {
+                    if (sel[0] < 0) sel[0] = p; else sel[1] = p;   /* p ascending */
+                  }
+                }
+                pos[0] = sel[0]; pos[1] = sel[1];
+              } else if (nzc == 1) {
+                for (int p = 0; p < 4; ++p)
+                  if (hy_nonzero(W, ldw, R, K, r, c0 + p)) sel[0] = p;
+                pos[0] = sel[0]; pos[1] = sel[0];
+              } else {
+                pos[0] = 1; pos[1] = 0;
+              }
+              const int64_t blk = rb * g.nKB + kb;
+              for (int j = 0; j < 2; ++j) {
+                const int c = 2 * gb + j;
+                uint8_t* mrow = meta + blk * 128 + rr * 8;
+                mrow[(2 * c) / 8] |= (uint8_t)(pos[j] << ((2 * c) % 8));
+                const int sigma = 8 * bi + 2 * t + j;
+                if (sel[j] >= 0) {
+                  const uint16_t v = hy_at(W, ldw, R, K, r, c0 + sel[j]);
+                  memcpy(values + blk * 1024 + rr * 64 + 2 * c, &v, 2);
+                  slot_col[sigma] = c0 + sel[j];
+                } else {
+                  empty_sigma[E++] = sigma;
+                }
+              }
+              /* surplus: the group's other nonzeros, ascending column */
+              if (nzc >= 3)
+                for (int p = 0; p < 4; ++p)
+                  if (hy_nonzero(W, ldw, R, K, r, c0 + p) && p != sel[0] && p != sel[1]) {
+                    sur_u[S] = 16 * bi + 4 * t + p;
+                    sur_v[S] = hy_at(W, ldw, R, K, r, c0 + p);
+                    ++S;
+                  }
+            }
+          (void)slot_col;
+          /* pass 2: greedy slot filling with PDD codes */
+          int prev = -1, used = 0, f = 0;
+          uint8_t* cu = codes + ((rb * g.nSeg + s) * 64 + 16 * q + rr) * 8;
+          for (int i = 0; i < S; ++i) {
+            const int d = sur_u[i] - prev, n0 = (d - 1) / 15;
+            if (f < E && used + n0 + 1 <= 16) {
+              for (int z = 0; z < n0; ++z) ++used;              /* code 0: dummy point */
+              const int code = d - 15 * n0;
+              cu[used / 2] |= (uint8_t)(code << (4 * (used % 2)));
+              ++used;
+              const int sigma = empty_sigma[f++];
+              const int64_t kb = kb0 + sigma / 8;
+              const int c = 2 * (4 * q + (sigma % 8) / 2) + sigma % 2;
+              memcpy(values + (rb * g.nKB + kb) * 1024 + rr * 64 + 2 * c, &sur_v[i], 2);
+              prev = sur_u[i];
+            } else {
+              const int u = sur_u[i];
+              const int64_t col_in_seg = 64 * (u / 16) + 16 * q + u % 16;
+              resflag[col_in_seg] = 1;
+              resval[col_in_seg] = sur_v[i];
+            }
+          }
+        }
+        for (int c = 0; c < 512; ++c)
+          if (resflag[c]) {
+            if (total < cap) res_ent[total] = ((uint32_t)c << 16) | resval[c];
+            ++total;
+          }
+        const int64_t z = (rb * g.nSeg + s) * 16 + rr;
+        if (total > INT32_MAX) return -1;
+        res_ptr[z + 1] = (int32_t)total;
+      }
+  (void)nz_rows;
+  *n_res = total;
+  return total > cap ? 1 : 0;
+}
+
+/*
+ * orc_hy_read: rebuild dense W (raw bits, R x K, zero-filled) from a byte
+ * image, layer by layer.  Returns 0, -1 on bad arguments, -2 when the image
+ * is inconsistent (more points than empty slots, a point outside its unit, an
+ * element written twice, a residual column outside the matrix, a stored
+ * element whose value is zero).
+ */
+int orc_hy_read(const uint8_t* values, const uint8_t* meta, const uint8_t* codes,
+                const int32_t* res_ptr, const uint32_t* res_ent, int64_t R, int64_t K, int dt,
+                uint16_t* W) {
+  if (R < 1 || K < 4 || K % 4 || (dt != ORC_F16 && dt != ORC_BF16)) return -1;
+  hy_geo_t g = hy_geo(R, K);
+  memset(W, 0, (size_t)(R * K * 2));
+  uint8_t* seen = (uint8_t*)calloc((size_t)(R * K), 1);
+  if (!seen) return -1;
+  int rc = 0;
+#define HY_PUT(rw, cl, val)                                                   \
+  do {                                                                        \
+    int64_t r_ = (rw), c_ = (cl);                                             \
+    uint16_t v_ = (val);                                                      \
+    if (r_ >= R || c_ >= K || c_ < 0) { if (v_ & 0x7FFF) rc = -2; break; }    \
+    if (!(v_ & 0x7FFF) || seen[r_ * K + c_]) { rc = -2; break; }              \
+    seen[r_ * K + c_] = 1;                                                    \
+    W[r_ * K + c_] = v_;                                                      \
+  } while (0)
+  for (int64_t rb = 0; rb < g.nRB; ++rb)
+    for (int64_t s = 0; s < g.nSeg; ++s)
+      for (int64_t rr = 0; rr < 16; ++rr) {
+        const int64_t r = rb * 16 + rr;
+        const int64_t kb0 = 8 * s, kb1 = (8 * s + 8 < g.nKB) ? 8 * s + 8 : g.nKB;
+        const int nb = (int)(kb1 - kb0);
+        for (int q = 0; q < 4; ++q) {
+          uint16_t empty_val[64];
+          int E = 0;
+          for (int bi = 0; bi < nb; ++bi)
+            for (int t = 0; t < 4; ++t) {
+              const int64_t kb = kb0 + bi, blk = rb * g.nKB + kb;
+              const int gb = 4 * q + t;
+              int pos[2];
+              uint16_t val[2];
+              for (int j = 0; j < 2; ++j) {
+                const int c = 2 * gb + j;
+                pos[j] = (meta[blk * 128 + rr * 8 + (2 * c) / 8] >> ((2 * c) % 8)) & 3;
+                memcpy(&val[j], values + blk * 1024 + rr * 64 + 2 * c, 2);
+              }
+              const int e0 = pos[0] > pos[1], e1 = pos[0] >= pos[1];
+              if (!e0) HY_PUT(r, 64 * kb + 4 * gb + pos[0], val[0]);
+              else empty_val[E++] = val[0];
+              if (!e1) HY_PUT(r, 64 * kb + 4 * gb + pos[1], val[1]);
+              else empty_val[E++] = val[1];
+            }
+          const uint8_t* cu = codes + ((rb * g.nSeg + s) * 64 + 16 * q + rr) * 8;
+          int p = -1, k = 0;
+          for (int i = 0; i < 16; ++i) {
+            const int code = (cu[i / 2] >> (4 * (i % 2))) & 15;
+            if (code == 0) { p += 15; continue; }
+            p += code;
+            if (k >= E || p >= 16 * nb) { rc = -2; break; }
+            HY_PUT(r, 64 * (kb0 + p / 16) + 16 * q + p % 16, empty_val[k]);
+            ++k;
+          }
+          for (; k < E; ++k)
+            if (empty_val[k] & 0x7FFF) rc = -2;     /* unfilled empty slot must hold +-0 */
+        }
+        const int64_t z = (rb * g.nSeg + s) * 16 + rr;
+        for (int32_t e = res_ptr[z]; e < res_ptr[z + 1]; ++e) {
+          const int64_t col = 512 * s + (res_ent[e] >> 16);
+          if (col >= 64 * kb1) { rc = -2; break; }
+          HY_PUT(r, col, (uint16_t)(res_ent[e] & 0xFFFF));
+        }
+      }
+#undef HY_PUT
+  free(seen);
+  return rc;
+}
