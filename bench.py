@@ -488,6 +488,123 @@ def run_search(args):
         json.dump(out, open(args.details, "w"), indent=1)
 
 
+def run_hybrid(args):
+    """Three-layer format product (nm_hybrid_spmm) on the ~50% unstructured
+    LLaMA-7B projections and the 4:8 ViT-B FC1, one JSON line per workload,
+    each timed as a HIP graph of back-to-back calls over rotating buffer sets,
+    with comparison paths timed the same way: the same weight dense through
+    torch.matmul (hipBLASLt), and for the 4:8 weight the library's own 4:8
+    path (nm_spmm)."""
+    import numpy as np
+    import torch
+
+    import nm_inputs
+    import semi_structured_sparse_nm_amd as nm
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    names = [L.name for L in nm_inputs.hybrid_workloads()]
+    want = names if args.hybrid == "all" else args.hybrid.split(",")
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+    def to_dev(a, dt):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if dt == "bf16":
+            t = t.view(torch.bfloat16)
+        return t.to(dev)
+
+    def graph_us(fn, nsets, reps):
+        for i in range(3):
+            fn(i % nsets)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for i in range(reps):
+                    fn(i % nsets)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    for L in nm_inputs.hybrid_workloads():
+        if L.name not in want:
+            continue
+        inp = nm_inputs.hybrid_inputs(L)
+        W, X = inp["W"], inp["X"]
+        Wd = to_dev(W, L.dt)
+        t0 = time.perf_counter()
+        h = nm.pack_hybrid(Wd, device=dev)
+        pack_s = time.perf_counter() - t0
+        nnz = int(((W.view(np.uint16) & 0x7FFF) != 0).sum())
+        Xd = to_dev(X, L.dt)
+        odt = tdt[L.out]
+        yb = torch.empty(0, dtype=odt).element_size()
+        fmt_bytes = h.nbytes()
+        nbytes = fmt_bytes + L.K * L.T * 2 + L.R * L.T * yb
+        nsets = max(2, math.ceil(args.rotate_gib * 2**30 / nbytes))
+        sets = []
+        for _ in range(nsets):
+            hs = nm.Hybrid(h.rows, h.K, h.dtype, *(None if getattr(h, n) is None else getattr(h, n).clone()
+                                                   for n in nm.HYBRID_BUFFERS), h.n_fill, h.n_res,
+                           h.format_version)
+            sets.append((hs, Xd.clone(), torch.empty((L.R, L.T), dtype=odt, device=dev)))
+
+        def hy(i):
+            hs, Xi, Yi = sets[i]
+            nm.spmm_hybrid(hs, Xi, out_dtype=odt, out=Yi)
+        us = graph_us(hy, nsets, args.steps)
+        # dense reference path: the same weight, all K columns, through torch.matmul
+        dsets = [(Wd.clone(), Xd.clone(), torch.empty((L.R, L.T), dtype=tdt[L.dt], device=dev))
+                 for _ in range(max(2, math.ceil(args.rotate_gib * 2**30 / (L.R * L.K * 2))))]
+
+        def dense(i):
+            Wi, Xi, Yi = dsets[i]
+            torch.matmul(Wi, Xi, out=Yi)
+        dense_us = graph_us(dense, len(dsets), args.steps)
+        del dsets
+        nm48_us = None
+        if L.pattern == "4of8":
+            p = nm.pack(Wd, 4, 8)
+            psets = [(nm.Packed(p.rows, p.K, 4, 8, p.dtype, p.values.clone(), p.meta.clone(), p.format_version),
+                      Xd.clone(), torch.empty((L.R, L.T), dtype=odt, device=dev)) for _ in range(nsets)]
+            ws = torch.empty(max(1, nm.workspace_size(p, L.T, odt)), dtype=torch.uint8, device=dev)
+
+            def nm48(i):
+                ps, Xi, Yi = psets[i]
+                nm.spmm(ps, Xi, out_dtype=odt, out=Yi, workspace=ws)
+            nm48_us = round(graph_us(nm48, nsets, args.steps), 3)
+            del psets
+        t_s = us * 1e-6
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+        line = {
+            "metric": "three-layer format SpMM: effective GB/s of the format's bytes + % of MI355X HBM roofline",
+            "value": round(nbytes / t_s / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": 3, "ms_per_step": round(us * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": L.dt, "data": "synthetic",
+            "config": {"workload": L.name, "R": L.R, "K": L.K, "T": L.T, "pattern": L.pattern, "out": L.out,
+                       "nonzeros": nnz, "slot_filled": h.n_fill, "residual": h.n_res},
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / t_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(t_hbm / t_s, 4), "traffic": None,
+                         "t_roof_us": round(t_hbm * 1e6, 3)},
+            "format_bytes": fmt_bytes, "dense_weight_bytes": L.R * L.K * 2,
+            "dense_equiv_TOPS": round(2 * L.R * L.K * L.T / t_s / 1e12, 3),
+            "us_hybrid": round(us, 3), "us_dense_torch_matmul": round(dense_us, 3),
+            "speedup_vs_dense": round(dense_us / us, 3), "us_library_4of8": nm48_us,
+            "rotation_sets": nsets, "launch": "hip-graph", "pack_host_s": round(pack_s, 3),
+        }
+        print(json.dumps(line), flush=True)
+        del sets
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -513,6 +630,8 @@ def main():
                          "X [T][K], Y [T][R] (tk)")
     ap.add_argument("--chain", action="store_true",
                     help="time the int8 ViT-B MLP: FC1 with GELU fused, chained into FC2 on the device")
+    ap.add_argument("--hybrid", default="",
+                    help="time the three-layer format product: 'all' or comma-separated workload names")
     ap.add_argument("--sweep", default="",
                     help="comma-separated workload sets to time layer by layer (1, 2, 3, 5)")
     args = ap.parse_args()
@@ -526,6 +645,9 @@ def main():
         return
     if args.sweep:
         run_sweep(args)
+        return
+    if args.hybrid:
+        run_hybrid(args)
         return
     if args.lut:
         run_lut(args)

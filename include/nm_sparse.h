@@ -262,6 +262,92 @@ const char* nm_spmm_variant_tk(const nm_packed* w, int64_t T, int32_t y_dtype, i
  */
 int32_t nm_spmm_ksplit(const nm_packed* w, int64_t T, int32_t y_dtype, int32_t act);
 
+/* ------------------------------------------------------------------------
+ * Three-layer format for moderately unstructured fp16 / bf16 weights (page
+ * "Accelerating GPU Inference of Large Language Models with Moderately
+ * Unstructured Sparse Weight Matrices", Methodology 1 and 2): any sparse
+ * weight is stored exactly as
+ *   1. a Sparse-TC layer: the 2:4 packed layout above (N = 2, M = 4) holding
+ *      the two largest nonzeros of every group of four (the nm_pack order),
+ *      2-bit positions;
+ *   2. a Slot-Filling layer: the other nonzeros of groups with three or four
+ *      ("surplus") moved into the Sparse-TC layer's empty slots, their
+ *      columns given by 4-bit relative distances (PDD), with dummy points
+ *      breaking gaps longer than 15;
+ *   3. a Residual layer in CSR: surplus that found no slot or code.
+ * Geometry: nRB = ceil(rows / 16), nKB = ceil(K / 64), nSeg = ceil(nKB / 8);
+ * segment s = column blocks 8s .. 8s+7 (512 columns).  Slot filling works
+ * inside a fill unit (row r, segment s, quad q = 0..3): in every block of
+ * the segment the 16 columns 64 kb + 16 q .. + 15, which is what one lane
+ * holds of the sparse matrix instruction's A operand.  Unit column
+ * u = 16 (kb - 8 s) + column % 16, unit slot sigma = 8 (kb - 8 s) + 2 t + j
+ * (group t = 0..3 of the quad, slot j).
+ *   values / meta: the 2:4 layout; a group with one nonzero at p stores it in
+ *     slot 0 at position p and marks slot 1 empty with position p; a group
+ *     with none marks both slots empty with positions 1 and 0 (position
+ *     pairs never produced by a group with two nonzeros, which are
+ *     ascending).  Empty slots hold a slot-filled value or +0.
+ *   codes: 8 bytes per unit at ((rb * nSeg + s) * 64 + 16 q + rr) * 8, sixteen
+ *     4-bit codes (code i in bits 4 (i % 2) of byte i / 2).  Read in order
+ *     from position -1: code 0 is a dummy point (advance 15, no value), code
+ *     d in 1..15 advances d to the next surplus element, whose value is in
+ *     the unit's next empty slot (ascending sigma).  The packer takes the
+ *     unit's surplus in ascending column, greedily, while slots and codes last.
+ *   res_ptr / res_ent: CSR over segment rows z = (rb * nSeg + s) * 16 + rr:
+ *     nRB * nSeg * 16 + 1 int32 pointers, entries (column - 512 s) << 16 |
+ *     value bits (uint32), ascending column within a segment row.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t rows, K;          /* R, K (K % 4 == 0) */
+  int32_t dtype;            /* NM_F16 or NM_BF16 */
+  uint32_t format_version;  /* NM_FORMAT_VERSION, written by nm_hybrid_pack */
+  void* values;  size_t values_bytes;   /* Sparse-TC values */
+  void* meta;    size_t meta_bytes;     /* Sparse-TC positions */
+  void* codes;   size_t codes_bytes;    /* Slot-Filling PDD codes */
+  void* res_ptr; size_t res_ptr_bytes;  /* Residual CSR row pointers (int32) */
+  void* res_ent; size_t res_ent_bytes;  /* Residual CSR entries (uint32; may be NULL when n_res == 0) */
+  int64_t n_fill;           /* slot-filled elements */
+  int64_t n_res;            /* residual elements */
+} nm_hybrid;
+
+/*
+ * Fill desc's rows, K, dtype, the five byte sizes, n_fill and n_res for the
+ * weight W (host memory, [rows][ldw] of dtype).  The pointers are left
+ * alone.  NM_EINVAL: null W / desc, rows < 1, K < 4, K % 4 != 0, ldw < K, or
+ * more than 2^31 - 1 residual entries.  NM_EUNSUPPORTED: dtype not F16 / BF16.
+ */
+nm_status nm_hybrid_pack_size(const void* W, int64_t ldw, int64_t rows, int64_t K, int32_t dtype,
+                              nm_hybrid* desc);
+
+/*
+ * Write the three-layer image of W (host memory, as above) into the five
+ * HOST buffers desc points to, which the caller allocates with the sizes
+ * nm_hybrid_pack_size wrote (res_ent may be NULL when n_res is 0); copying
+ * them to device memory is the caller's.  Offline, once per weight; runs on
+ * the calling thread plus worker threads it joins before returning.
+ * NM_EINVAL as for nm_hybrid_pack_size, for a null buffer, or when desc's
+ * sizes or shape do not match W.
+ */
+nm_status nm_hybrid_pack(const void* W, int64_t ldw, nm_hybrid* desc);
+
+/*
+ * Y = epilogue(W X) for a weight in the three-layer format (Methodology 2 of
+ * the page: the Slot-Filling codes are decoded by the vector units, the
+ * Sparse-TC layer and the decoded slot-filled elements run on the sparse
+ * matrix instruction, the residual is accumulated by the vector units in a
+ * separate buffer added at the end; loads of the next unit overlap the
+ * decode of the current one).  desc's five buffers are device memory.  X is
+ * [K][ldx] of the weight's dtype, Y [rows][ldy] of y_dtype (the weight's
+ * dtype or NM_F32); bias NULL or float[rows]; act NM_ACT_NONE or
+ * NM_ACT_GELU.  Asynchronous on `stream`; allocates nothing.  NM_EINVAL: null
+ * pointers, T < 1, ldx < T, ldy < T, a descriptor whose sizes do not match
+ * its shape; NM_EUNSUPPORTED: other dtypes, X / Y / buffers not 16-byte
+ * aligned, T > 16 tokens per call with K > 4096 (tiles of 16 tokens repeat
+ * the decode), version mismatch; NM_EHIP: launch failure.
+ */
+nm_status nm_hybrid_spmm(const nm_hybrid* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
+                         int32_t y_dtype, const void* bias, int32_t act, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -249,3 +249,73 @@ def ops_and_bytes(L: Layer):
     epi = L.R * 8 if L.out == "i8" else 0
     nbytes = kept * b + meta + L.K * L.T * b + L.R * L.T * by + epi
     return 2 * L.R * L.K * L.T * L.N / L.M, nbytes, 2 * L.R * L.K * L.T
+
+
+def unstructured(R: int, K: int, density: float, dt: str, seed: int, *names) -> np.ndarray:
+    """N(0, 0.02^2) weights pruned without structure to `density`: in every
+    row the round(density K) entries of largest |w| stay (equal |w|: the lower
+    column), the rest become +0 -- the moderately unstructured weights
+    (about 50% kept) of LLM pruning by magnitude per output row.  Raw bits for
+    bf16, as normal() returns them."""
+    W = normal((R, K), 0.02, dt, seed, *names)
+    mag = (W.view(np.uint16) & 0x7FFF) if dt in ("f16", "bf16") else np.abs(W)
+    keep = int(round(density * K))
+    order = np.argsort(-mag.astype(np.int64), axis=1, kind="stable")
+    mask = np.zeros((R, K), bool)
+    np.put_along_axis(mask, order[:, :keep], True, axis=1)
+    out = W.copy()
+    out[~mask] = 0
+    return out
+
+
+@dataclass
+class HybridLayer:
+    """A layer of the three-layer format product: weight pattern 'u50'
+    (unstructured, 50% kept per row) or '4of8' (4:8), dtype, output dtype."""
+    name: str
+    R: int
+    K: int
+    T: int
+    pattern: str
+    dt: str
+    out: str
+
+
+def hybrid_workloads():
+    """Layers of the three-layer format product: LLaMA-7B projections at 50%
+    unstructured sparsity in decode (16 tokens), fp16 and bf16, and the
+    ViT-B FC1 layer with 4:8 weights (a pattern the format holds in its first
+    two layers) at 16 and 197 tokens (one image)."""
+    out = []
+    for dt in ("f16", "bf16"):
+        for (R, K), pname in (((4096, 4096), "qkvo"), ((11008, 4096), "up"), ((4096, 11008), "down")):
+            out.append(HybridLayer(f"hy_llama_{pname}_u50_T16_{dt}", R, K, 16, "u50", dt, dt))
+    out.append(HybridLayer("hy_vitb_fc1_4of8_T16_f16", 3072, 768, 16, "4of8", "f16", "f16"))
+    out.append(HybridLayer("hy_vitb_fc1_4of8_T197_f16", 3072, 768, 197, "4of8", "f16", "f16"))
+    return out
+
+
+def structured(R: int, K: int, n: int, m: int, dt: str, seed: int, *names) -> np.ndarray:
+    """N(0, 0.02^2) weights with exactly n nonzeros in every group of m
+    consecutive columns, at positions drawn uniformly (an n:m pattern as a
+    pruned layer would carry it).  Raw bits for bf16."""
+    W = normal((R, K), 0.02, dt, seed, *names)
+    keys = rng(seed, *names, "mask").random((R, K // m, m))
+    order = np.argsort(keys, axis=2, kind="stable")
+    mask = np.zeros((R, K // m, m), bool)
+    np.put_along_axis(mask, order[:, :, :n], True, axis=2)
+    out = W.copy()
+    out[~mask.reshape(R, K)] = 0
+    return out
+
+
+def hybrid_inputs(L: HybridLayer, seed: int = 0):
+    """Host operands of a three-layer format layer: dict(W, X)."""
+    if L.pattern == "u50":
+        W = unstructured(L.R, L.K, 0.5, L.dt, seed, L.name, "W")
+    elif L.pattern == "4of8":
+        W = structured(L.R, L.K, 4, 8, L.dt, seed, L.name, "W")
+    else:
+        raise ValueError(L.pattern)
+    X = normal((L.K, L.T), 1.0, L.dt, seed, L.name, "X")
+    return dict(W=W, X=X)

@@ -41,6 +41,20 @@ class NmPacked(ctypes.Structure):
                 ("meta_bytes", ctypes.c_size_t)]
 
 
+class NmHybrid(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("K", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("format_version", ctypes.c_uint32),
+                ("values", ctypes.c_void_p), ("values_bytes", ctypes.c_size_t),
+                ("meta", ctypes.c_void_p), ("meta_bytes", ctypes.c_size_t),
+                ("codes", ctypes.c_void_p), ("codes_bytes", ctypes.c_size_t),
+                ("res_ptr", ctypes.c_void_p), ("res_ptr_bytes", ctypes.c_size_t),
+                ("res_ent", ctypes.c_void_p), ("res_ent_bytes", ctypes.c_size_t),
+                ("n_fill", ctypes.c_int64), ("n_res", ctypes.c_int64)]
+
+
+HYBRID_BUFFERS = ("values", "meta", "codes", "res_ptr", "res_ent")
+
+
 class NmError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -83,7 +97,12 @@ def lib() -> ctypes.CDLL:
         L.nm_spmm_noalloc.restype = ctypes.c_int
         L.nm_spmm_noalloc_max_bytes.argtypes = []
         L.nm_spmm_noalloc_max_bytes.restype = SZ
-        for f in ("nm_pack_size", "nm_pack", "nm_spmm_workspace_size", "nm_spmm"):
+        HP = ctypes.POINTER(NmHybrid)
+        L.nm_hybrid_pack_size.argtypes = [P, I64, I64, I64, I32, HP]
+        L.nm_hybrid_pack.argtypes = [P, I64, HP]
+        L.nm_hybrid_spmm.argtypes = [HP, P, I64, I64, P, I64, I32, P, I32, P]
+        for f in ("nm_pack_size", "nm_pack", "nm_spmm_workspace_size", "nm_spmm", "nm_hybrid_pack_size",
+                  "nm_hybrid_pack", "nm_hybrid_spmm"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -317,4 +336,106 @@ def linear(p: Packed, Xt: torch.Tensor, bias: torch.Tensor | None = None,
                           0 if workspace is None else workspace.numel() * workspace.element_size(),
                           _stream(Xt.device))
     _check(st, "nm_spmm_tk")
+    return out
+
+
+# ---------------------------------------------------------------- three-layer format
+@dataclass
+class Hybrid:
+    """A weight in the three-layer format (Sparse-TC 2:4, slot filling with
+    PDD codes, CSR residual) as five uint8 buffers on one device."""
+    rows: int
+    K: int
+    dtype: int
+    values: torch.Tensor
+    meta: torch.Tensor
+    codes: torch.Tensor
+    res_ptr: torch.Tensor
+    res_ent: torch.Tensor | None
+    n_fill: int
+    n_res: int
+    format_version: int = FORMAT_VERSION
+
+    def desc(self) -> NmHybrid:
+        d = NmHybrid()
+        d.rows, d.K, d.dtype, d.format_version = self.rows, self.K, self.dtype, self.format_version
+        d.n_fill, d.n_res = self.n_fill, self.n_res
+        for name in HYBRID_BUFFERS:
+            t = getattr(self, name)
+            setattr(d, name, None if t is None else t.data_ptr())
+            setattr(d, name + "_bytes", 0 if t is None else t.numel())
+        return d
+
+    @property
+    def torch_dtype(self):
+        return _NM_TO_TORCH[self.dtype]
+
+    def nbytes(self) -> int:
+        return sum(0 if getattr(self, n) is None else getattr(self, n).numel() for n in HYBRID_BUFFERS)
+
+
+def hybrid_pack_host(W: torch.Tensor) -> Hybrid:
+    """nm_hybrid_pack on the host: W (float16 / bfloat16, any device) is
+    copied to host memory and packed there; the buffers are CPU tensors."""
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D")
+    dt = _TORCH_TO_NM.get(W.dtype)
+    if dt not in (NM_F16, NM_BF16):
+        raise TypeError(f"the three-layer format takes float16 / bfloat16 weights, not {W.dtype}")
+    Wh = W.detach().to("cpu").contiguous()
+    R, K = Wh.shape
+    d = NmHybrid()
+    _check(lib().nm_hybrid_pack_size(Wh.data_ptr(), K, R, K, dt, ctypes.byref(d)), "nm_hybrid_pack_size")
+    bufs = {n: torch.empty(getattr(d, n + "_bytes"), dtype=torch.uint8) for n in HYBRID_BUFFERS}
+    h = Hybrid(R, K, dt, bufs["values"], bufs["meta"], bufs["codes"], bufs["res_ptr"],
+               bufs["res_ent"] if d.n_res else None, d.n_fill, d.n_res, 0)
+    dd = h.desc()
+    _check(lib().nm_hybrid_pack(Wh.data_ptr(), K, ctypes.byref(dd)), "nm_hybrid_pack")
+    h.format_version = dd.format_version
+    return h
+
+
+def pack_hybrid(W: torch.Tensor, device=None) -> Hybrid:
+    """Pack W into the three-layer format (host packer, offline) and place the
+    buffers on `device` (default: W's device, which must be a GPU)."""
+    device = torch.device(device) if device is not None else W.device
+    if device.type != "cuda":
+        raise ValueError(f"target device {device} is not a GPU")
+    h = hybrid_pack_host(W)
+    for n in HYBRID_BUFFERS:
+        t = getattr(h, n)
+        if t is not None:
+            setattr(h, n, t.to(device))
+    return h
+
+
+def spmm_hybrid(h: Hybrid, X: torch.Tensor, bias: torch.Tensor | None = None,
+                out_dtype: torch.dtype | None = None, out: torch.Tensor | None = None,
+                act: str = "none") -> torch.Tensor:
+    """nm_hybrid_spmm: Y[R, T] = epilogue(W @ X) for a three-layer weight,
+    X [K, T] (tokens contiguous)."""
+    if X.dim() != 2 or X.stride(1) != 1 or X.shape[0] != h.K:
+        raise ValueError("X must be [K, T] with unit stride along T")
+    if X.dtype != h.torch_dtype:
+        raise TypeError(f"X is {X.dtype}, the weight is {h.torch_dtype}")
+    T = X.shape[1]
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else h.torch_dtype
+    if out is None:
+        out = torch.empty((h.rows, T), dtype=out_dtype, device=X.device)
+    if out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (h.rows, T) or out.dtype != out_dtype:
+        raise ValueError("out must be [R, T] of out_dtype with unit stride along T")
+    tensors = [X, out] + [getattr(h, n) for n in HYBRID_BUFFERS if getattr(h, n) is not None]
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.numel() != h.rows or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous float32 [R] tensor")
+        tensors.append(bias)
+    for t in tensors:
+        if t.device != X.device:
+            raise ValueError(f"operand on {t.device}, X on {X.device}")
+    d = h.desc()
+    st = lib().nm_hybrid_spmm(ctypes.byref(d), X.data_ptr(), X.stride(0), T, out.data_ptr(), out.stride(0),
+                              _TORCH_TO_NM[out_dtype], None if bias is None else bias.data_ptr(),
+                              ACTS[act], _stream(X.device))
+    _check(st, "nm_hybrid_spmm")
     return out

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "nm_common.hpp"
+#include "nm_hybrid.hpp"
 
 using nm::Geometry;
 using nm::SpmmArgs;
@@ -103,6 +104,8 @@ enum Variant {
   V_EXPAND,         // any other N:M (int8, fp16, bf16): windows expanded in registers, dense MFMA
   V_EXPAND_DECODE,  // any N:M, decode shapes (T <= 16): K split across 8 waves, dense MFMA
   V_SMFMAC_I8TK,    // int8 2:4 persistent, [T][K] layout (X [T][K], Y [T][R])
+  V_STREAM24,       // fp16 / bf16 2:4, T <= 16 per token tile: one workgroup per CU walking row
+                    // blocks, values straight to registers one 512-column segment ahead
   V_COUNT
 };
 
@@ -116,6 +119,7 @@ const char* variant_name(Variant v) {
     case V_EXPAND: return "expand_mfma_persistent";
     case V_EXPAND_DECODE: return "expand_mfma_decode";
     case V_SMFMAC_I8TK: return "smfmac_i8_2of4_tk";
+    case V_STREAM24: return "smfmac_h_2of4_stream_decode";
     default: return "invalid";
   }
 }
@@ -178,6 +182,10 @@ bool eligible(Variant v, const Call& c) {
              aligned(c.X, 16) && (c.g->K + 128) * c.ldx * c.g->eb < (1ll << 31) &&
              c.g->values_bytes() + 2048 < (1ull << 31) && c.g->meta_bytes() + 1024 < (1ull << 31) &&
              c.g->R * c.ldy < (1ll << 40);
+    case V_STREAM24:
+      // fp16 / bf16 2:4 with at most 16 tokens; 32-bit buffer offsets
+      return (c.wdt == NM_F16 || c.wdt == NM_BF16) && c.g->N == 2 && c.g->M == 4 && c.T <= 16 &&
+             aligned(c.X, 2) && c.g->K * c.ldx * 2 < (1ll << 31) && c.g->values_bytes() < (1ull << 31);
     case V_SMFMAC_I8TK:
       // int8 2:4 in the [T][K] layout; token rows in whole 16-byte pieces;
       // 32-bit buffer offsets that do not wrap for the tokens a tile reaches
@@ -510,6 +518,38 @@ namespace {
 // One [K][T]-or-[T][K] product with variant v: K split into S slices (raw
 // partial sums at `part`, then the reduction applies a's epilogue) or one
 // launch.
+// The three-layer kernel's schedule on a plain 2:4 weight (its Sparse-TC
+// layer alone): same 16-row x 64-column blocks, same position words.
+hipError_t launch_stream24(const SpmmArgs& s24, hipStream_t s) {
+  nm::HybridArgs a{};
+  a.R = s24.g.R;
+  a.K = s24.g.K;
+  a.nRB = s24.g.nRB;
+  a.nKB = s24.g.nKB;
+  a.nSeg = (a.nKB + 7) / 8;
+  a.wdt = s24.wdt;
+  a.ydt = s24.ydt;
+  a.act = s24.act;
+  a.values = s24.values;
+  a.meta = s24.meta;
+  a.codes = s24.meta;          // unused by the plain form
+  a.res_ptr = nullptr;
+  a.res_ent = nullptr;
+  a.values_bytes = (int64_t)s24.g.values_bytes();
+  a.meta_bytes = (int64_t)s24.g.meta_bytes();
+  a.X = s24.X;
+  a.ldx = s24.ldx;
+  a.T = s24.T;
+  a.Y = s24.Y;
+  a.ldy = s24.ldy;
+  a.bias = static_cast<const float*>(s24.bias);
+  const int64_t cus = device_cus();
+  a.G = (int)std::max<int64_t>((a.nRB + nm::kHybridMaxRB - 1) / nm::kHybridMaxRB, std::min<int64_t>(a.nRB, cus));
+  a.nChunk = (int)((a.nSeg + 3) / 4);
+  a.patch_last = (a.T & 1) && a.ldx == a.T;
+  return nm::launch_spmm_hybrid(a, false, s);
+}
+
 nm_status run_variant(Variant v, int S, const SpmmArgs& a, void* part, hipStream_t s) {
   hipError_t e = hipSuccess;
   if (S > 1) {
@@ -543,6 +583,7 @@ nm_status run_variant(Variant v, int S, const SpmmArgs& a, void* part, hipStream
     case V_EXPAND: e = nm::launch_spmm_expand(a, s); break;
     case V_EXPAND_DECODE: e = nm::launch_spmm_expand_decode(a, s); break;
     case V_SMFMAC_I8TK: e = nm::launch_spmm_smfmac_i8tk(a, s); break;
+    case V_STREAM24: e = launch_stream24(a, s); break;
     default: return NM_EINVAL;
   }
   return e == hipSuccess ? NM_OK : NM_EHIP;
@@ -744,6 +785,76 @@ int32_t nm_spmm_ksplit(const nm_packed* w, int64_t T, int32_t y_dtype, int32_t a
   const Call c = make_call(g, w->dtype, y_dtype, T, T, T, al, al, act);
   const Plan p = plan_for(c);
   return p.repack ? 1 : ksplit_for(p.v, c);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- three-layer format
+namespace {
+
+bool hy_sizes_ok(const nm_hybrid* w, int64_t nRB, int64_t nKB, int64_t nSeg) {
+  if ((int64_t)w->values_bytes != nRB * nKB * 1024 || (int64_t)w->meta_bytes != nRB * nKB * 128) return false;
+  if ((int64_t)w->codes_bytes != nRB * nSeg * 512) return false;
+  if ((int64_t)w->res_ptr_bytes != (nRB * nSeg * 16 + 1) * 4) return false;
+  if (w->n_res < 0 || (int64_t)w->res_ent_bytes != w->n_res * 4) return false;
+  return w->values && w->meta && w->codes && w->res_ptr && (w->n_res == 0 || w->res_ent);
+}
+
+}  // namespace
+
+extern "C" {
+
+nm_status nm_hybrid_spmm(const nm_hybrid* w, const void* X, int64_t ldx, int64_t T, void* Y, int64_t ldy,
+                         int32_t y_dtype, const void* bias, int32_t act, void* stream) {
+  if (!w || !X || !Y || T < 1 || ldx < T || ldy < T) return NM_EINVAL;
+  if (w->rows < 1 || w->K < 4 || w->K % 4) return NM_EINVAL;
+  if (w->dtype != NM_F16 && w->dtype != NM_BF16) return NM_EUNSUPPORTED;
+  if (y_dtype != w->dtype && y_dtype != NM_F32) return NM_EUNSUPPORTED;
+  if (act != NM_ACT_NONE && act != NM_ACT_GELU) return NM_EINVAL;
+  if (w->format_version != NM_FORMAT_VERSION) return NM_EUNSUPPORTED;
+  const int64_t nRB = (w->rows + 15) / 16, nKB = (w->K + 63) / 64, nSeg = (nKB + 7) / 8;
+  if (!hy_sizes_ok(w, nRB, nKB, nSeg)) return NM_EINVAL;
+  if (!aligned(w->values, 16) || !aligned(w->meta, 16) || !aligned(w->codes, 16) || !aligned(w->res_ptr, 16) ||
+      (w->res_ent && !aligned(w->res_ent, 16)) || !aligned(X, 2))
+    return NM_EUNSUPPORTED;
+  // 32-bit buffer offsets
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)w->values_bytes >= lim || (int64_t)w->res_ent_bytes >= lim || w->K * ldx * 2 >= lim ||
+      (int64_t)w->codes_bytes >= lim)
+    return NM_EUNSUPPORTED;
+  nm::HybridArgs a{};
+  a.R = w->rows;
+  a.K = w->K;
+  a.nRB = nRB;
+  a.nKB = nKB;
+  a.nSeg = nSeg;
+  a.wdt = w->dtype;
+  a.ydt = y_dtype;
+  a.act = act;
+  a.values = static_cast<const uint8_t*>(w->values);
+  a.meta = static_cast<const uint8_t*>(w->meta);
+  a.codes = static_cast<const uint8_t*>(w->codes);
+  a.res_ptr = static_cast<const int32_t*>(w->res_ptr);
+  a.res_ent = w->n_res ? static_cast<const uint32_t*>(w->res_ent) : reinterpret_cast<const uint32_t*>(w->res_ptr);
+  a.values_bytes = (int64_t)w->values_bytes;
+  a.meta_bytes = (int64_t)w->meta_bytes;
+  a.codes_bytes = (int64_t)w->codes_bytes;
+  a.res_ptr_bytes = (int64_t)w->res_ptr_bytes;
+  // with no residual the entry loads read the row pointers instead (in range, unused)
+  a.res_ent_bytes = w->n_res ? (int64_t)w->res_ent_bytes : (int64_t)w->res_ptr_bytes;
+  a.X = X;
+  a.ldx = ldx;
+  a.T = T;
+  a.Y = Y;
+  a.ldy = ldy;
+  a.bias = static_cast<const float*>(bias);
+  // one workgroup per compute unit walking row blocks b, b + G, ...; at most
+  // kHybridMaxRB row blocks each
+  const int64_t cus = device_cus();
+  a.G = (int)std::max<int64_t>((nRB + nm::kHybridMaxRB - 1) / nm::kHybridMaxRB, std::min<int64_t>(nRB, cus));
+  a.nChunk = (int)((nSeg + 3) / 4);
+  a.patch_last = (T & 1) && ldx == T;
+  return nm::launch_spmm_hybrid(a, true, static_cast<hipStream_t>(stream)) == hipSuccess ? NM_OK : NM_EHIP;
 }
 
 }  // extern "C"

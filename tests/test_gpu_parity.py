@@ -357,6 +357,28 @@ def test_decode_h_variant(force_variant, dt, out, R, K, T):
     assert np.all(pad == want), "writes beyond T"
 
 
+@pytest.mark.parametrize("dt,out", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("R,K,T", [(16, 64, 16), (17, 4, 1), (300, 200, 3), (96, 4100, 16), (40, 512, 8),
+                                   (33, 11008, 16), (1100, 2048, 5), (64, 9000, 13)])
+def test_stream24_variant(force_variant, dt, out, R, K, T):
+    """fp16 / bf16 2:4 on the streaming decode schedule (one workgroup per
+    CU walking row blocks, segments of 512 columns per wave, activation
+    chunks of four segments): partial blocks and segments, ragged rows,
+    several row blocks per workgroup, several chunks, T < 16."""
+    import semi_structured_sparse_nm_amd as nm
+    from tests._parity import TORCH_DT, dev
+    force_variant("smfmac_h_2of4_stream_decode")
+    W, X, b, s = _inputs(dt, out, R, K, T, 2, 4, 12, f"s24-{dt}-{out}-{R}-{K}-{T}")
+    p = nm.pack(dev(W, dt), 2, 4)
+    assert nm.variant(p, T, TORCH_DT[out]) == "smfmac_h_2of4_stream_decode"
+    # odd T with dense rows: the last activation element's 4-byte piece ends past X
+    Y, _ = run(W, X, 2, 4, dt, out, bias=b, scale=s, ldx_pad=0 if T % 2 else 3, ldy_pad=3, sentinel=5)
+    compare(Y[:, :T], reference(W, X, 2, 4, dt, out, bias=b, scale=s), out, "stream24")
+    pad = Y[:, T:]
+    want = 5 if out != "bf16" else oracle.round_to(np.array([5.0]), "bf16")[0]
+    assert np.all(pad == want), "writes beyond T"
+
+
 EXPAND_NMS = [(1, 4), (3, 4), (4, 4), (1, 8), (2, 8), (4, 8), (8, 8)]
 EXPAND_SHAPES = [(300, 192, 144), (17, 8, 16), (259, 1288, 272)]
 
