@@ -503,6 +503,13 @@ def run_hybrid(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     names = [L.name for L in nm_inputs.hybrid_workloads()]
     want = names if args.hybrid == "all" else args.hybrid.split(",")
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
@@ -630,6 +637,8 @@ def main():
                          "X [T][K], Y [T][R] (tk)")
     ap.add_argument("--chain", action="store_true",
                     help="time the int8 ViT-B MLP: FC1 with GELU fused, chained into FC2 on the device")
+    ap.add_argument("--floor", action="store_true",
+                    help="also time a one-element kernel the same way (the per-call launch floor)")
     ap.add_argument("--hybrid", default="",
                     help="time the three-layer format product: 'all' or comma-separated workload names")
     ap.add_argument("--sweep", default="",
@@ -767,6 +776,28 @@ def main():
     ms, graphed = timed(list(range(args.steps)))
     # warm (no rotation) figure, labelled as such
     warm_ms, _ = timed([0] * args.steps)
+    # launch floor: a one-element kernel (torch's elementwise add) captured and
+    # replayed the same way, per call
+    floor_us = None
+    if args.floor:
+        z = torch.zeros(1, device=dev)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(args.steps):
+                    z.add_(1.0)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        g.replay()
+        f1.record()
+        torch.cuda.synchronize()
+        floor_us = f0.elapsed_time(f1) * 1e3 / args.steps
 
     # quick parity spot check of the timed configuration on sampled rows
     parity = None
@@ -825,6 +856,9 @@ def main():
         "effective_GBps": round(nbytes / t_s / 1e9, 1), "pack_ms": round(pack_ms, 4),
         "parity": parity,
     }
+    if floor_us is not None:
+        line["launch_floor_us_per_call"] = round(floor_us, 3)
+        line["us_per_call"] = round(ms * 1e3, 3)
     print(json.dumps(line), flush=True)
     if args.details:
         json.dump(line, open(args.details, "w"), indent=1)

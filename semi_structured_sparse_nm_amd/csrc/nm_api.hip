@@ -212,7 +212,12 @@ Variant choose(const Call& c) {
 
 Variant choose_auto(const Call& c) {
   if (eligible(V_SMFMAC_I8TK, c)) return V_SMFMAC_I8TK;
-  // decode shapes (few tokens): K split inside a workgroup per 16-row block
+  // decode shapes (few tokens), fp16 / bf16 2:4: with more 16-row blocks
+  // than compute units, one workgroup per CU walking row blocks with its
+  // loads a segment ahead; otherwise K split inside a workgroup per row
+  // block.  Measured on MI355X, LLaMA-7B T = 16 (streaming / split us): up
+  // (688 row blocks) 13.1 / 16.8, qkvo (256) 7.6 / 7.5, down (256) 15.4 / 15.1
+  if (eligible(V_STREAM24, c) && c.g->nRB > device_cus()) return V_STREAM24;
   if (eligible(V_SMFMAC_HD, c)) return V_SMFMAC_HD;
   if (eligible(V_EXPAND_DECODE, c)) return V_EXPAND_DECODE;
   // int8 2:4 persistent: 8-wave workgroups (512 x 128 tiles, one per CU,
@@ -544,8 +549,9 @@ hipError_t launch_stream24(const SpmmArgs& s24, hipStream_t s) {
   a.ldy = s24.ldy;
   a.bias = static_cast<const float*>(s24.bias);
   const int64_t cus = device_cus();
-  a.G = (int)std::max<int64_t>((a.nRB + nm::kHybridMaxRB - 1) / nm::kHybridMaxRB, std::min<int64_t>(a.nRB, cus));
-  a.nChunk = (int)((a.nSeg + 3) / 4);
+  const int64_t mrb = nm::kHybridMaxRB[0], nw = nm::kHybridWaves[0];
+  a.G = (int)std::max<int64_t>((a.nRB + mrb - 1) / mrb, std::min<int64_t>(a.nRB, cus));
+  a.nChunk = (int)((a.nSeg + nw - 1) / nw);
   a.patch_last = (a.T & 1) && a.ldx == a.T;
   return nm::launch_spmm_hybrid(a, false, s);
 }
@@ -849,10 +855,11 @@ nm_status nm_hybrid_spmm(const nm_hybrid* w, const void* X, int64_t ldx, int64_t
   a.ldy = ldy;
   a.bias = static_cast<const float*>(bias);
   // one workgroup per compute unit walking row blocks b, b + G, ...; at most
-  // kHybridMaxRB row blocks each
+  // kHybridMaxRB[1] row blocks each
   const int64_t cus = device_cus();
-  a.G = (int)std::max<int64_t>((nRB + nm::kHybridMaxRB - 1) / nm::kHybridMaxRB, std::min<int64_t>(nRB, cus));
-  a.nChunk = (int)((nSeg + 3) / 4);
+  const int64_t mrb = nm::kHybridMaxRB[1], nw = nm::kHybridWaves[1];
+  a.G = (int)std::max<int64_t>((nRB + mrb - 1) / mrb, std::min<int64_t>(nRB, cus));
+  a.nChunk = (int)((nSeg + nw - 1) / nw);
   a.patch_last = (T & 1) && ldx == T;
   return nm::launch_spmm_hybrid(a, true, static_cast<hipStream_t>(stream)) == hipSuccess ? NM_OK : NM_EHIP;
 }

@@ -31,8 +31,10 @@ struct HybridArgs {
   bool patch_last;
 };
 
-// Row blocks one workgroup takes at most.
-constexpr int kHybridMaxRB = 4;
+// Waves per workgroup (= 512-column segments per activation chunk) and row
+// blocks one workgroup takes at most, [plain 2:4, three-layer].
+constexpr int kHybridWaves[2] = {8, 4};
+constexpr int kHybridMaxRB[2] = {3, 4};
 
 // hy = false: the plain 2:4 layer alone (values / meta of an nm_pack 2:4
 // weight; codes and residual unused) with the same schedule.

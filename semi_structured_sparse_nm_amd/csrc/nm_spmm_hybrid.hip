@@ -23,22 +23,23 @@
 // descending: both empty).  The unit's codes, read in order, give the local
 // column of each slot-filled element; the k-th real point takes the value of
 // the k-th empty slot (a per-lane 128-byte copy of the values in LDS, laid
-// out without bank conflicts, gives random access to it).  The elements are
-// scattered into a second 2:4 operand of the same groups (value, position),
-// written to LDS and read back as registers.  The Sparse-TC operand has its empty slots zeroed.  Each
-// 64-column block then takes two sparse matrix instructions on the same B
-// fragment.  An element's group holds at most two surplus elements, so the
+// out without bank conflicts, gives random access to it; each slot read is
+// cleared in the copy, which then reads back as the Sparse-TC operand with
+// every empty slot zero).  The elements are scattered into a second 2:4
+// operand of the same groups (value, position) in a zeroed LDS area and read
+// back as registers.  Each 64-column block then takes two sparse matrix
+// instructions on the same B fragment.  An element's group holds at most two surplus elements, so the
 // second operand is a valid 2:4 operand; a single one sits in slot 0 with a
 // zero partner at the same position.
 //
 // Residual: lane l takes row l / 4 and tokens 4 (l % 4) .. + 3 of the item,
-// walks that row's CSR entries (staged in LDS) and multiplies with the
-// activation values already in LDS.
+// walks that row's CSR entries (staged in LDS, four at a time) and multiplies
+// with the activation values already in LDS.
 //
-// Partial sums per (wave, row block): one area for the matrix products, one
-// for the residual, each a 16 x 16 fp32 tile updated in program order; at
-// the end the four waves' tiles are added in wave order, matrix area first,
-// then the residual area (a fixed order: results do not depend on timing).
+// Partial sums per (wave, row block): a 16 x 16 fp32 tile in LDS.  Each item
+// adds its matrix products, then its residual sums (held apart in registers
+// until then); at the end the four waves' tiles are added in wave order (a
+// fixed order: results do not depend on timing).
 #include "nm_hybrid.hpp"
 
 namespace nm {
@@ -66,20 +67,26 @@ __device__ __forceinline__ float to_f32(uint32_t h) {
     return __builtin_bit_cast(float, h << 16);
 }
 
-constexpr int NW = 4;          // waves per workgroup = segments per chunk
 constexpr int SEGB = 8;        // column blocks per segment
-constexpr int MAXRB = kHybridMaxRB;
 constexpr int RESCAP = 256;    // residual entries staged per item (more are read from memory)
 
-// LDS map (bytes)
-constexpr int XS_OFF = 0;                                 // X chunk: NW segments x 8 blocks x 2 KB
-constexpr int STG_OFF = XS_OFF + NW * SEGB * 2048;        // per lane 128 B of values
-constexpr int IDX_OFF = STG_OFF + NW * 64 * 128;          // per lane 32 B of second-operand positions
-constexpr int PART_OFF = IDX_OFF + NW * 64 * 32;          // per wave, per row block: 1 KB products
-constexpr int RPART_OFF = PART_OFF + NW * MAXRB * 1024;   // per wave, per row block: 1 KB residual
-constexpr int RES_OFF = RPART_OFF + NW * MAXRB * 1024;    // per wave: RESCAP residual entries
-constexpr int LDS_BYTES = RES_OFF + NW * RESCAP * 4;
-static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+// Waves, row blocks per workgroup and the LDS map (bytes).  The three-layer
+// form: four waves (one per SIMD), with per-lane decode areas.  The plain
+// 2:4 form needs none of those: eight waves (two per SIMD) and twice the
+// activation chunk.
+template <bool HY>
+struct Lay {
+  static constexpr int NW = kHybridWaves[HY];                    // waves = segments per chunk
+  static constexpr int MAXRB = kHybridMaxRB[HY];
+  static constexpr int XS_OFF = 0;                               // X chunk: NW segments x 8 blocks x 2 KB
+  static constexpr int STG_OFF = XS_OFF + NW * SEGB * 2048;      // per lane 128 B: the Sparse-TC values
+  static constexpr int STG2_OFF = STG_OFF + (HY ? NW * 64 * 128 : 0);   // per lane 128 B: second operand
+  static constexpr int IDX_OFF = STG2_OFF + (HY ? NW * 64 * 128 : 0);   // per lane 32 B: its positions
+  static constexpr int PART_OFF = IDX_OFF + (HY ? NW * 64 * 32 : 0);    // per wave, row block: 1 KB partials
+  static constexpr int RES_OFF = PART_OFF + NW * MAXRB * 1024;   // per wave: RESCAP residual entries
+  static constexpr int BYTES = RES_OFF + (HY ? NW * RESCAP * 4 : 0);
+  static_assert(BYTES <= 160 * 1024, "LDS");
+};
 
 // One item's register-resident loads.
 struct Item {
@@ -97,9 +104,13 @@ typedef uint16_t __attribute__((may_alias)) u16a;
 typedef uint8_t __attribute__((may_alias)) u8a;
 
 template <int WT, int OUT, bool HY>
-__global__ void __launch_bounds__(NW * 64) hybrid_kernel(HybridArgs a) {
+__global__ void __launch_bounds__(Lay<HY>::NW * 64) hybrid_kernel(HybridArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+  typedef Lay<HY> L;
+  constexpr int NW = L::NW, MAXRB = L::MAXRB;
+  constexpr int XS_OFF = L::XS_OFF, STG_OFF = L::STG_OFF, STG2_OFF = L::STG2_OFF, IDX_OFF = L::IDX_OFF,
+                PART_OFF = L::PART_OFF, RES_OFF = L::RES_OFF;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::BYTES];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -112,34 +123,37 @@ __global__ void __launch_bounds__(NW * 64) hybrid_kernel(HybridArgs a) {
   const int nItems = ni * a.nChunk;
   const int ldx = (int)a.ldx;
 
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values), 0, (int)a.values_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rm =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.meta), 0, (int)a.meta_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.codes), 0, (int)a.codes_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rp =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.res_ptr), 0, (int)a.res_ptr_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t re =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a.res_ent), 0, (int)a.res_ent_bytes, 0x00020000);
+  // The weight buffers are read with plain global loads: every offset below
+  // lies inside its buffer by construction (blocks clamped to the last one,
+  // items to the wave's last item, residual entries to the last entry), and
+  // a buffer descriptor would hold four scalar registers each.
+  const uint8_t* const gv = a.values;
+  const uint8_t* const gm = a.meta;
+  const uint8_t* const gc = a.codes;
+  const int32_t* const gp = a.res_ptr;
+  const uint32_t* const ge = a.res_ent;
   const v4i rx = make_rsrc(a.X, (int)(a.K * a.ldx * 2));
 
   // per-lane decode areas, interleaved by dword (lane l's dword d at
   // (64 d + l) * 4): a wave's accesses to them hit 64 distinct banks whatever
   // slot each lane addresses
   u32a* const stg = reinterpret_cast<u32a*>(lds + STG_OFF + w * 64 * 128) + lane;   // 32 dwords
+  u32a* const stg2 = reinterpret_cast<u32a*>(lds + STG2_OFF + w * 64 * 128) + lane; // 32 dwords
   u32a* const idxs = reinterpret_cast<u32a*>(lds + IDX_OFF + w * 64 * 32) + lane;   // 8 dwords
   // byte b of a lane's interleaved area
   auto stg_b = [&](u32a* base, int b) { return reinterpret_cast<u8a*>(base + 64 * (b >> 2)) + (b & 3); };
   uint8_t* const xseg = lds + XS_OFF + w * SEGB * 2048;     // this wave's segment of the chunk
   uint8_t* const part = lds + PART_OFF + w * MAXRB * 1024;
-  uint8_t* const rpart = lds + RPART_OFF + w * MAXRB * 1024;
   uint32_t* const rstage = reinterpret_cast<uint32_t*>(lds + RES_OFF + w * RESCAP * 4);
 
-  // partial areas start at zero
-  for (int i = lane; i < MAXRB * 256; i += 64) {
-    reinterpret_cast<float*>(part)[i] = 0.f;
-    reinterpret_cast<float*>(rpart)[i] = 0.f;
+  // partial sums and the second operand's staging start at zero (the
+  // staging is cleared again after each use)
+  for (int i = lane; i < MAXRB * 256; i += 64) reinterpret_cast<float*>(part)[i] = 0.f;
+  if constexpr (HY) {
+#pragma unroll
+    for (int d = 0; d < 4 * SEGB; ++d) stg2[64 * d] = 0u;
+#pragma unroll
+    for (int d = 0; d < SEGB; ++d) idxs[64 * d] = 0u;
   }
 
   // item j: chunk j / ni, row block b + (j % ni) G, segment 4 (j / ni) + w
@@ -152,12 +166,11 @@ __global__ void __launch_bounds__(NW * 64) hybrid_kernel(HybridArgs a) {
     for (int bi = 0; bi < SEGB; ++bi) {
       const int kb = min(s * SEGB + bi, nKB - 1);            // past the segment: a valid block, unused
       const int blk = rb * nKB + kb;
-      it.a[bi] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, li * 64 + lg * 16, blk * 1024, 0));
-      it.m[bi] = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, li * 8 + (lg >> 1) * 4, blk * 128, 0);
+      it.a[bi] = *reinterpret_cast<const v4i*>(gv + (uint32_t)(blk * 1024 + li * 64 + lg * 16));
+      it.m[bi] = *reinterpret_cast<const int*>(gm + (uint32_t)(blk * 128 + li * 8 + (lg >> 1) * 4));
     }
     if constexpr (HY) {
-      const v2i c = __builtin_bit_cast(
-          v2i, __builtin_amdgcn_raw_buffer_load_b64(rc, lane * 8, (rb * nSeg + s) * 512, 0));
+      const v2i c = *reinterpret_cast<const v2i*>(gc + (uint32_t)((rb * nSeg + s) * 512 + lane * 8));
       it.c0 = c[0];
       it.c1 = c[1];
     }
@@ -165,19 +178,18 @@ __global__ void __launch_bounds__(NW * 64) hybrid_kernel(HybridArgs a) {
   // lane x <= 16 holds res_ptr[(rb nSeg + s) 16 + x]
   auto load_rp = [&](int j) -> int {
     const int s = seg_of(j), rb = rb_of(j);
-    return (int)__builtin_amdgcn_raw_buffer_load_b32(rp, min(lane, 16) * 4, (rb * nSeg + s) * 64, 0);
+    return gp[(uint32_t)((rb * nSeg + s) * 16 + min(lane, 16))];
   };
   // every load below is issued whatever the item (clamped to data inside
   // its buffer): the compiler's waits count loads in issue order, which
-  // holds only if each path issues the same loads and none is entirely out
-  // of range (such a load returns at once, ahead of older ones)
+  // holds only if each path through the loop issues the same loads
   const int n_ent = (int)(a.res_ent_bytes / 4);
   // (entries past the item's own are loaded too and never read)
   auto load_ent = [&](int rpv, uint32_t (&e)[4]) {
     const int r0 = __builtin_amdgcn_readlane(rpv, 0);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
-      e[m] = __builtin_amdgcn_raw_buffer_load_b32(re, min(r0 + lane + 64 * m, n_ent - 1) * 4, 0, 0);
+      e[m] = ge[(uint32_t)min(r0 + lane + 64 * m, n_ent - 1)];
   };
 
   // activation chunk c: segment NW c + w's 8 blocks, rows 64 kb .. + 63 of
@@ -224,7 +236,8 @@ __global__ void __launch_bounds__(NW * 64) hybrid_kernel(HybridArgs a) {
     rp_n1 = load_rp(min(1, jlast));
   }
 
-  for (int j = 0; j < nValid; ++j) {
+  auto step = [&](int j, auto pf) {
+    constexpr bool PF = decltype(pf)::value != 0;
     const int i = j % ni;
     const int s = seg_of(j);
     if (i == 0) {
@@ -245,12 +258,14 @@ __global__ void __launch_bounds__(NW * 64) hybrid_kernel(HybridArgs a) {
         }
       }
     }
-    // next item's loads overlap this one's decode and product (past the
-    // last item: the last item again, unused)
-    load_item(min(j + 1, jlast), nxt);
-    if constexpr (HY) {
-      load_ent(rp_n1, ent_nxt);
-      rp_n2 = load_rp(min(j + 2, jlast));
+    // next item's loads overlap this one's decode and product (the last
+    // item, run without them, issues none)
+    if constexpr (PF) {
+      load_item(j + 1, nxt);
+      if constexpr (HY) {
+        load_ent(rp_n1, ent_nxt);
+        rp_n2 = load_rp(min(j + 2, jlast));
+      }
     }
 
     {
@@ -283,16 +298,9 @@ __global__ void __launch_bounds__(NW * 64) hybrid_kernel(HybridArgs a) {
         for (int bi = 0; bi < SEGB; ++bi)
 #pragma unroll
           for (int t = 0; t < 4; ++t) stg[64 * (4 * bi + t)] = (uint32_t)a1[bi][t];
-        // the Sparse-TC operand without its empty slots
-#pragma unroll
-        for (int bi = 0; bi < SEGB; ++bi)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t lo = (e8[bi] >> (2 * t)) & 1u, hi = (e8[bi] >> (2 * t + 1)) & 1u;
-            const uint32_t keep = (lo ? 0u : 0xFFFFu) | (hi ? 0u : 0xFFFF0000u);
-            a1[bi][t] = (int)((uint32_t)a1[bi][t] & keep);
-          }
-        // PDD decode: positions of the slot-filled elements and their values
+        // PDD decode: the k-th real point takes the k-th empty slot's value;
+        // that slot is then cleared in the copy (LDS runs a wave's accesses
+        // in order, so the clear lands after the read)
         uint32_t lv[16];
         int lu[16];
         uint32_t clo = elo, chi = ehi;
@@ -306,14 +314,18 @@ __global__ void __launch_bounds__(NW * 64) hybrid_kernel(HybridArgs a) {
           const uint32_t clo2 = clo & (clo - 1u), chi2 = clo ? chi : (chi & (chi - 1u));
           clo = real ? clo2 : clo;
           chi = real ? chi2 : chi;
-          lv[k] = *reinterpret_cast<const u16a*>(stg_b(stg, 2 * (sg & 63)));
+          u16a* const sp = reinterpret_cast<u16a*>(stg_b(stg, 2 * (sg & 63)));
+          lv[k] = *sp;
+          if (real) *sp = 0;
           lu[k] = (real && pos < 16 * nb) ? pos : -1;
         }
-        // second operand: zero, then each element at (block, group, slot)
+        // every empty slot is now zero or was zero: the Sparse-TC operand
+        // without the slot-filled elements
 #pragma unroll
-        for (int d = 0; d < 4 * SEGB; ++d) stg[64 * d] = 0u;
+        for (int bi = 0; bi < SEGB; ++bi)
 #pragma unroll
-        for (int d = 0; d < SEGB; ++d) idxs[64 * d] = 0u;
+          for (int t = 0; t < 4; ++t) a1[bi][t] = (int)stg[64 * (4 * bi + t)];
+        // second operand: each element at (block, group, slot) of the zeroed staging
         int pg = -1, pp = 0;
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -321,7 +333,7 @@ __global__ void __launch_bounds__(NW * 64) hybrid_kernel(HybridArgs a) {
           if (u >= 0) {
             const int g = u >> 2, p = u & 3;
             const bool second = g == pg;
-            *reinterpret_cast<u16a*>(stg_b(stg, 4 * g + 2 * (int)second)) = (uint16_t)lv[k];
+            *reinterpret_cast<u16a*>(stg_b(stg2, 4 * g + 2 * (int)second)) = (uint16_t)lv[k];
             *stg_b(idxs, g) = (uint8_t)(second ? (pp | (p << 2)) : (p | (p << 2)));
             pg = g;
             pp = p;
@@ -330,12 +342,17 @@ __global__ void __launch_bounds__(NW * 64) hybrid_kernel(HybridArgs a) {
 #pragma unroll
         for (int bi = 0; bi < SEGB; ++bi)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) a2[bi][t] = (int)stg[64 * (4 * bi + t)];
+          for (int t = 0; t < 4; ++t) a2[bi][t] = (int)stg2[64 * (4 * bi + t)];
 #pragma unroll
         for (int bi = 0; bi < SEGB; ++bi) {
           const uint32_t d = idxs[64 * bi];
           i2[bi] = (int)((d & 0xFu) | ((d >> 4) & 0xF0u) | ((d >> 8) & 0xF00u) | ((d >> 12) & 0xF000u));
         }
+        // cleared for the next item (after the reads above, in LDS order)
+#pragma unroll
+        for (int d = 0; d < 4 * SEGB; ++d) stg2[64 * d] = 0u;
+#pragma unroll
+        for (int d = 0; d < SEGB; ++d) idxs[64 * d] = 0u;
       }
 
       // products: every block of the segment on this wave's activation columns
@@ -364,10 +381,11 @@ __global__ void __launch_bounds__(NW * 64) hybrid_kernel(HybridArgs a) {
         const int beg = __shfl(rp_cur, rr) - r0, end = __shfl(rp_cur, rr + 1) - r0;
 #pragma unroll
         for (int m = 0; m < 4; ++m) rstage[lane + 64 * m] = ent_cur[m];
+        // the residual's own sums (registers), added to the tile after the products
         float racc[4] = {0.f, 0.f, 0.f, 0.f};
-        auto res_fma = [&](uint32_t ent) {
+        auto res_fma = [&](uint32_t ent, bool on) {
           const int col = (int)(ent >> 16), bi = col >> 6, r = col & 63;
-          const float wv = to_f32<WT>(ent & 0xFFFFu);
+          const float wv = on ? to_f32<WT>(ent & 0xFFFFu) : 0.f;
           const uint8_t* xp = xseg + bi * 2048 + r * 32 + 16 * ((tq >> 1) ^ ((r >> 3) & 1)) + 8 * (tq & 1);
           const v2i xv = *reinterpret_cast<const v2i*>(xp);
 #pragma unroll
@@ -376,39 +394,48 @@ __global__ void __launch_bounds__(NW * 64) hybrid_kernel(HybridArgs a) {
             racc[x] = __builtin_fmaf(wv, to_f32<WT>(h), racc[x]);
           }
         };
-        for (int e = beg; e < min(end, RESCAP); ++e) res_fma(rstage[e]);
+        // four entries at a time, so their LDS reads overlap (padding
+        // entries past the row's end count with weight 0)
+        const int estg = min(end, RESCAP);
+        for (int e = beg; e < estg; e += 4) {
+          uint32_t en[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) en[q] = rstage[min(e + q, RESCAP - 1)];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) res_fma(en[q], e + q < estg);
+        }
         // entries past the staged ones (more than RESCAP in this item): read
         // from memory, in order, after everything else of the item
         if (__builtin_amdgcn_readlane(rp_cur, 16) - r0 > RESCAP)
           for (int e = max(beg, RESCAP); e < end; ++e)
-            res_fma(__builtin_amdgcn_raw_buffer_load_b32(re, (r0 + e) * 4, 0, 0));
-        float* rpt = reinterpret_cast<float*>(rpart + i * 1024) + rr * 16 + 4 * tq;
+            res_fma(ge[(uint32_t)(r0 + e)], true);
+        float* rpt = reinterpret_cast<float*>(part + i * 1024) + rr * 16 + 4 * tq;
 #pragma unroll
         for (int x = 0; x < 4; ++x) rpt[x] += racc[x];
       }
     }
-    cur = nxt;
-    if constexpr (HY) {
-      rp_cur = rp_n1;
-      rp_n1 = rp_n2;
+    if constexpr (PF) {
+      cur = nxt;
+      if constexpr (HY) {
+        rp_cur = rp_n1;
+        rp_n1 = rp_n2;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) ent_cur[m] = ent_nxt[m];
+        for (int m = 0; m < 4; ++m) ent_cur[m] = ent_nxt[m];
+      }
     }
-  }
+  };
+  for (int j = 0; j < nValid - 1; ++j) step(j, ic<1>{});
+  step(nValid - 1, ic<0>{});
   }
 
-  // the four waves' partial tiles, in wave order, then the epilogue
+  // the waves' partial tiles, in wave order, then the epilogue
   __syncthreads();
-  const int t = threadIdx.x;
-  const int row = t >> 4, tok = t & 15;
-  for (int i = 0; i < ni; ++i) {
+  for (int o = threadIdx.x; o < ni * 256; o += NW * 64) {
+    const int i = o >> 8, t = o & 255;
+    const int row = t >> 4, tok = t & 15;
     float y = 0.f;
 #pragma unroll
     for (int v = 0; v < NW; ++v) y += reinterpret_cast<const float*>(lds + PART_OFF + (v * MAXRB + i) * 1024)[t];
-    if constexpr (HY) {
-#pragma unroll
-      for (int v = 0; v < NW; ++v) y += reinterpret_cast<const float*>(lds + RPART_OFF + (v * MAXRB + i) * 1024)[t];
-    }
     const int64_t r = (int64_t)(b + i * G) * 16 + row;
     const int64_t tt = (int64_t)ty * 16 + tok;
     if (r < a.R && tt < a.T) {
@@ -428,7 +455,7 @@ __global__ void __launch_bounds__(NW * 64) hybrid_kernel(HybridArgs a) {
 
 template <int WT, bool HY>
 hipError_t launch_wt(const HybridArgs& a, dim3 grid, hipStream_t s) {
-  const dim3 block(NW * 64);
+  const dim3 block(Lay<HY>::NW * 64);
   if (a.ydt == NM_F32)
     hipLaunchKernelGGL((hybrid_kernel<WT, NM_F32, HY>), grid, block, 0, s, a);
   else

@@ -678,6 +678,12 @@ def test_gelu_decode(force_variant, dt, out, N, M, R, K, T):
     _gelu_case(force_variant, variant, dt, out, N, M, R, K, T, 34)
 
 
+@pytest.mark.parametrize("dt,out", GELU_FP)
+@pytest.mark.parametrize("R,K,T", [(40, 512, 8), (600, 1280, 16)])
+def test_gelu_stream24(force_variant, dt, out, R, K, T):
+    _gelu_case(force_variant, "smfmac_h_2of4_stream_decode", dt, out, 2, 4, R, K, T, 36)
+
+
 @pytest.mark.parametrize("dt,out", [("i8", "i8"), ("f16", "f16"), ("bf16", "f32")])
 @pytest.mark.parametrize("R,K,T", [(70, 192, 197), (17, 64, 5)])
 def test_gelu_generic(force_variant, dt, out, R, K, T):
