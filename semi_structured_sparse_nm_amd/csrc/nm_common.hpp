@@ -118,6 +118,31 @@ hipError_t launch_splitk_reduce(const SpmmArgs& a, hipStream_t s);
 // threads at once: a racing first call only repeats the query).
 int cu_count(int device);
 
+// Row tiles per group of a persistent kernel's grouped tile order (groups of
+// gm row tiles, row tile fastest inside a group, then the next token tile).
+// The nconc workgroups of one XCD that run together cover about gm row tiles
+// x nconc / gm token tiles; per 128-column step they fetch a weight block of
+// wk bytes per row tile and an activation block of xk bytes per token tile,
+// and share them through the XCD's L2.  A weight that fits in the L2 (4 MB)
+// stays there across token tiles, so only the activation counts: all row
+// tiles in one group.  Otherwise the gm with the fewest bytes per step.
+inline int tile_group_rows(int mtiles, int ntiles, int nconc, double wk, double xk, double w_total) {
+  if (w_total <= 4.0 * 1024 * 1024 || mtiles <= 1) return mtiles;
+  int best = mtiles;
+  double best_cost = 0;
+  for (int gm = 1; gm <= mtiles; ++gm) {
+    const int rows = gm < nconc ? gm : nconc;
+    int toks = (nconc + rows - 1) / rows;
+    if (toks > ntiles) toks = ntiles;
+    const double cost = rows * wk + toks * xk;
+    if (gm == 1 || cost < best_cost) {
+      best_cost = cost;
+      best = gm;
+    }
+  }
+  return best;
+}
+
 // ---------------------------------------------------------------- device
 // Cache policy of the output stores (gfx950 buffer-store cache bits: sc0 |
 // nt).  The output is written once and never read back by the kernel;

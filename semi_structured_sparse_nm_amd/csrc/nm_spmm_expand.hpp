@@ -56,7 +56,7 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 template <int WT, int NN, int MM, int OUT>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
+expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd, int gm) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr bool I8 = WT == NM_I8;
   typedef Run<WT, NN, MM> RG;
@@ -80,8 +80,10 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   const int ldx = (int)a.ldx;
   const int nRB = (int)g.nRB;
 
-  // work items: (tile, K slice); the tiles of one slice are contiguous,
-  // row tiles fastest, so an XCD's run shares activation strips in its L2
+  // work items: (tile, K slice); the tiles of one slice are contiguous, in
+  // groups of gm row tiles (row tile fastest inside a group, then the next
+  // token tile; tile_group_rows), so the workgroups an XCD runs together
+  // share both operands' blocks through its L2
   const int kbs = a.kbs;                     // column blocks per work item
   const int ntile = mtiles * ntiles;
   const int ntot = ntile * a.ksplit;
@@ -96,8 +98,11 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     const int L = lo + jw + k * nwg_xcd;
     ks = L / ntile;
     const int Lt = L - ks * ntile;
-    const int nt = Lt / mtiles;
-    r0 = (Lt - nt * mtiles) * BM;
+    const int grp = Lt / (gm * ntiles);
+    const int in = Lt - grp * gm * ntiles;
+    const int rows = min(gm, mtiles - grp * gm);
+    const int nt = in / rows;
+    r0 = (grp * gm + in - nt * rows) * BM;
     t0 = nt * BN;
   };
 
@@ -520,8 +525,12 @@ hipError_t launch_one(const SpmmArgs& a, hipStream_t s) {
   int nwg_xcd = cu_count(dev) / 8;                // one eight-wave workgroup per CU
   if (nwg_xcd > per_xcd) nwg_xcd = per_xcd;
   if (nwg_xcd < 1) nwg_xcd = 1;
+  // operand bytes one row tile / one token tile brings per 128 columns
+  const double eb = a.g.eb;
+  const double wk = 256.0 * 128 * NN / MM * (eb + (NN == MM ? 0.0 : a.g.w / 8.0)), xk = 128.0 * BN * eb;
+  const int gm = tile_group_rows(mtiles, ntiles, nwg_xcd, wk, xk, (double)(a.g.values_bytes() + a.g.meta_bytes()));
   hipLaunchKernelGGL((expand_kernel<WT, NN, MM, OUT>), dim3(8 * nwg_xcd), dim3(NW * 64), 0, s, a, mtiles, ntiles,
-                     nwg_xcd);
+                     nwg_xcd, gm);
   return hipGetLastError();
 }
 

@@ -73,7 +73,7 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 // made the main loop spill)
 template <int NW, int WT, int OUT, bool ACT = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
+smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd, int gm) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr bool OUT16 = OUT != NM_F32;
   // row blocks (16 rows) per wave: 4 with 4-wave workgroups (two per CU),
@@ -96,8 +96,12 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   const int ldx = (int)a.ldx;
   const int nRB = (int)g.nRB;
 
-  // work items: (tile, K slice); the tiles of one slice are contiguous,
-  // row tiles fastest, so an XCD's run shares activation strips in its L2
+  // work items: (tile, K slice); the tiles of one slice are contiguous, in
+  // groups of gm row tiles, row tile fastest inside a group, then the next
+  // token tile: the workgroups of an XCD running at the same time cover
+  // about gm row tiles x (their number / gm) token tiles, so both operands'
+  // blocks are shared through its L2 (gm = all row tiles: one token strip at
+  // a time, for weights small enough to stay in L2)
   const int kbs = a.kbs;                     // column blocks per work item
   const int ntile = mtiles * ntiles;
   const int ntot = ntile * a.ksplit;
@@ -112,8 +116,11 @@ smfmac_h_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     const int L = lo + jw + k * nwg_xcd;
     ks = L / ntile;
     const int Lt = L - ks * ntile;
-    const int nt = Lt / mtiles;
-    r0 = (Lt - nt * mtiles) * BM;
+    const int grp = Lt / (gm * ntiles);
+    const int in = Lt - grp * gm * ntiles;
+    const int rows = min(gm, mtiles - grp * gm);
+    const int nt = in / rows;
+    r0 = (grp * gm + in - nt * rows) * BM;
     t0 = nt * BN;
   };
 
@@ -426,22 +433,25 @@ hipError_t launch_nw(const SpmmArgs& a, hipStream_t s) {
   if (nwg_xcd > per_xcd) nwg_xcd = per_xcd;
   if (nwg_xcd < 1) nwg_xcd = 1;
   const int grid = 8 * nwg_xcd;
+  // operand bytes one row tile / one token tile brings per 128-column step
+  const double wk = 256.0 * (64 * 2 + 16), xk = 128.0 * BN * 2;
+  const int gm = tile_group_rows(mtiles, ntiles, nwg_xcd, wk, xk, (double)(a.g.values_bytes() + a.g.meta_bytes()));
   if (a.act) {
     if (a.ydt == NM_F32)
       hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_F32, true>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles,
-                         nwg_xcd);
+                         nwg_xcd, gm);
     else if (WT == NM_F16)
       hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_F16, true>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles,
-                         nwg_xcd);
+                         nwg_xcd, gm);
     else
       hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_BF16, true>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles,
-                         nwg_xcd);
+                         nwg_xcd, gm);
   } else if (a.ydt == NM_F32) {
-    hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_F32>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles, nwg_xcd);
+    hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_F32>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles, nwg_xcd, gm);
   } else if (WT == NM_F16) {
-    hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_F16>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles, nwg_xcd);
+    hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_F16>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles, nwg_xcd, gm);
   } else {
-    hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_BF16>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles, nwg_xcd);
+    hipLaunchKernelGGL((smfmac_h_kernel<NW, WT, NM_BF16>), dim3(grid), dim3(NW * 64), 0, s, a, mtiles, ntiles, nwg_xcd, gm);
   }
   return hipGetLastError();
 }

@@ -20,11 +20,12 @@ Solvers:
 - ``solve_greedy``: start from the best-scoring choice of every layer and
   repeatedly take the downgrade with the least score lost per microsecond
   saved until the budget holds, then spend the slack on upgrades;
-- ``solve_evolutionary``: a population of assignments evolved by crossover
-  and mutation; the budget starts relaxed and tightens to the target over
-  the generations, and an individual over the (current) budget is repaired
-  by the greedy downgrade rule, so the search moves between the disconnected
-  feasible pieces rather than discarding what lies between them.
+- ``solve_evolutionary``: the pages' three-stage heuristic with constraint
+  relaxation (seeding and exploration under a relaxed budget, then
+  convergence with the budget tightened to the target and a local search);
+  an individual over the current budget is repaired by the greedy downgrade
+  rule, so the search moves between the disconnected feasible pieces rather
+  than discarding what lies between them.
 """
 from __future__ import annotations
 
@@ -166,47 +167,104 @@ def solve_greedy(p: Problem) -> Solution:
     return _solution(p, _fill(p, a, p.budget))
 
 
+def _local_search(p: Problem, a: List[int], budget: float, passes: int = 3) -> List[int]:
+    """Moves on a feasible assignment: set one layer, then two layers, to
+    other choices, repair the rest to the budget, spend the slack; keep a
+    move when the score rises.  A few passes over all such moves."""
+    best = list(a)
+    C = p.score.shape[1]
+
+    def attempt(b):
+        nonlocal best
+        b = _fill(p, _repair(p, b, budget), budget)
+        if p.latency(b) <= budget + 1e-9 and p.value(b) > p.value(best) + 1e-12:
+            best = b
+            return True
+        return False
+
+    for _ in range(passes):
+        improved = False
+        for l in range(p.layers):
+            for c in range(C):
+                if c != best[l]:
+                    b = list(best)
+                    b[l] = c
+                    improved |= attempt(b)
+        for l in range(p.layers):
+            for m in range(l + 1, p.layers):
+                for c in range(C):
+                    for d in range(C):
+                        if c != best[l] and d != best[m]:
+                            b = list(best)
+                            b[l], b[m] = c, d
+                            improved |= attempt(b)
+        if not improved:
+            break
+    return best
+
+
 def solve_evolutionary(p: Problem, pop: int = 64, generations: int = 200, relax: float = 0.25,
                        mutation: float = 0.05, seed: int = 0) -> Solution:
-    """Evolutionary search over assignments with a budget relaxed by
-    ``relax`` at the start and tightened linearly to the target; repair keeps
-    every individual within the current budget; elitist."""
+    """Three-stage heuristic search with constraint relaxation (the pages'
+    search, Sec. 3: relaxation keeps the search from converging early inside
+    one piece of a fragmented feasible region):
+
+    1. seeding under a relaxed budget (1 + relax) x target: the greedy
+       assignment and random assignments, each repaired to the relaxed budget
+       and its slack spent;
+    2. exploration, a third of the generations, at the relaxed budget:
+       crossover and mutation, every child repaired to it, so individuals
+       between the target-feasible pieces survive;
+    3. convergence, the rest of the generations, with the budget tightened
+       linearly to the target (then held there), elitist, and a local search
+       of single-layer moves on the best target-feasible individual.
+    """
     rng = random.Random(seed)
     L, C = p.score.shape
+    fitness = p.value
+    relaxed = p.budget * (1.0 + relax)
+    mutation = max(mutation, 1.0 / L)          # at least one changed layer per child on average
+    g1 = max(1, generations // 3)
+    g2 = max(1, generations - g1)
 
-    def fitness(a):
-        return p.value(a)
+    def evolve(popl, bud):
+        elite = popl[: max(2, pop // 8)]
+        nxt = [list(a) for a in elite]
+        while len(nxt) < pop:
+            x, y = rng.sample(popl[: max(2, pop // 2)], 2)     # parents from the better half
+            child = [x[i] if rng.random() < 0.5 else y[i] for i in range(L)]
+            for i in range(L):
+                if rng.random() < mutation:
+                    child[i] = rng.randrange(C)
+            nxt.append(_fill(p, _repair(p, child, bud), bud))
+        return nxt
 
-    def budget_at(g):
-        return p.budget * (1.0 + relax * max(0.0, 1.0 - g / max(1, generations * 0.75)))
-
-    b0 = budget_at(0)
-    popl = [_fill(p, _repair(p, [rng.randrange(C) for _ in range(L)], b0), b0) for _ in range(pop - 1)]
-    popl.append(_fill(p, _repair(p, list(np.argmax(p.score, axis=1)), b0), b0))
+    # stage 1: seeds under the relaxed budget
+    popl = [_fill(p, _repair(p, list(np.argmax(p.score, axis=1)), relaxed), relaxed)]
+    popl += [_fill(p, _repair(p, [rng.randrange(C) for _ in range(L)], relaxed), relaxed) for _ in range(pop - 1)]
+    # stage 2: exploration at the relaxed budget
+    for _ in range(g1):
+        popl.sort(key=fitness, reverse=True)
+        popl = evolve(popl, relaxed)
+    # stage 3: tighten to the target, converge, refine
     best = None
-    for g in range(generations + 1):
-        bud = budget_at(g)
+    for g in range(g2 + 1):
+        bud = p.budget + (relaxed - p.budget) * max(0.0, 1.0 - g / max(1, 0.75 * g2))
         popl = [_repair(p, a, bud) for a in popl]
         popl.sort(key=fitness, reverse=True)
         for a in popl:
             if p.feasible(a) and (best is None or fitness(a) > fitness(best)):
                 best = list(a)
                 break
-        if g == generations:
+        if g == g2:
             break
-        elite = popl[: max(2, pop // 8)]
-        nxt = [list(a) for a in elite]
-        while len(nxt) < pop:
-            x, y = rng.sample(popl[: pop // 2], 2)        # parents from the better half
-            child = [x[i] if rng.random() < 0.5 else y[i] for i in range(L)]
-            for i in range(L):
-                if rng.random() < mutation:
-                    child[i] = rng.randrange(C)
-            nxt.append(_fill(p, _repair(p, child, bud), bud))
-        popl = nxt
+        popl = evolve(popl, bud)
     if best is None:
         best = _repair(p, popl[0], p.budget)
-    return _solution(p, _fill(p, best, p.budget))
+    best = _fill(p, best, p.budget)
+    if p.feasible(best):
+        best = _local_search(p, best, p.budget)
+    return _solution(p, best)
 
 
 def brute_force(p: Problem) -> Solution:

@@ -187,8 +187,8 @@ def _full_size_rows(L):
     cost allows, else a fixed set -- the first and last row of every 64-row
     band (one wave's rows), and every row of each 256- or 512-row tile that is
     some workgroup's second (or later) tile under the persistent kernels'
-    tile order (row tile fastest, XCD x owning a contiguous range of tiles,
-    one workgroup per 4-wave / 8-wave slot of 256 CUs)."""
+    tile orders (XCD x owning a contiguous range of tiles, one workgroup per
+    4-wave / 8-wave slot of 256 CUs; row tile fastest, or grouped)."""
     if L.R * L.K * L.T * L.N / L.M <= FULL_COMPARE_MACS:
         return np.arange(L.R)
     rows = set()
@@ -199,11 +199,39 @@ def _full_size_rows(L):
         mt = (L.R + BM - 1) // BM
         ntot = mt * ntok
         per_xcd = (ntot + 7) // 8
-        for x in range(8):
-            for L2 in range(x * per_xcd + nwg, min((x + 1) * per_xcd, ntot)):
-                r0 = (L2 % mt) * BM
-                rows.update(range(r0, min(r0 + BM, L.R)))
+        # the fp16 / bf16 tile kernel orders tiles in groups of gm row tiles
+        # (gm = all of them for weights that fit in L2): both orders' rows
+        for gm in {mt, _group_rows(L, mt, ntok, 64, True), _group_rows(L, mt, ntok, 32, False)}:
+            for x in range(8):
+                for L2 in range(x * per_xcd + nwg, min((x + 1) * per_xcd, ntot)):
+                    grp, inn = divmod(L2, gm * ntok)
+                    r0 = (grp * gm + inn % min(gm, mt - grp * gm)) * BM
+                    rows.update(range(r0, min(r0 + BM, L.R)))
     return np.array(sorted(rows))
+
+
+def _group_rows(L, mt, ntok, nconc, sparse24):
+    """gm of the tile kernels' grouped tile order (the host's choice
+    restated: fewest operand bytes per 128-column step for the workgroups one
+    XCD runs at once, all row tiles when the weight fits in L2), for the
+    fp16 / bf16 2:4 kernel (64 workgroups per XCD) or the dense-expand one (32)."""
+    eb = 1 if L.dt == "i8" else 2
+    w_total = L.R * L.K * L.N // L.M * eb * 1.125
+    if w_total <= 4 * 1024 * 1024 or mt <= 1:
+        return mt
+    if sparse24:
+        wk, xk = 256.0 * (64 * 2 + 16), 128.0 * 128 * 2
+    else:
+        bits = 0 if L.N == L.M else (2 if L.M == 4 else 3)
+        wk, xk = 256.0 * 128 * L.N / L.M * (eb + bits / 8.0), 128.0 * 128 * eb
+    best, best_cost = mt, None
+    for gm in range(1, mt + 1):
+        rows = min(gm, nconc)
+        toks = min((nconc + rows - 1) // rows, ntok)
+        cost = rows * wk + toks * xk
+        if best_cost is None or cost < best_cost:
+            best, best_cost = gm, cost
+    return best
 
 
 def _full_size_case(L, out=None):

@@ -77,14 +77,18 @@ def test_json_round_trip():
 @pytest.mark.gpu
 def test_measured_table_predicts_a_measured_stack():
     """Calibrate the per-launch gap on one mixed stack and predict another
-    (other order and mix) within 35%."""
+    (other order and mix) within 10%.  These stacks are short (6 and 8
+    launches of small layers) and timed a few times, so launch jitter weighs
+    more than in the 48-layer ViT-B stacks `bench.py --lut` predicts (0.6-2.1%
+    there)."""
     from semi_structured_sparse_nm_amd.lut import measure_layers, time_stack
     shapes = [L(T=4096, R=2048, K=1024, N=n, M=m) for n, m in ((1, 4), (2, 4), (4, 8), (8, 8))]
     lut = measure_layers(shapes, reps=10)
     assert len(lut) == 4 and all(lut.lookup(s) > 0 for s in shapes)
     calib = [shapes[i] for i in (0, 1, 2, 3, 1, 2)]
-    lut.calibrate(calib, time_stack(calib, reps=3))
+    lut.calibrate(calib, time_stack(calib, reps=5))
     other = [shapes[i] for i in (3, 3, 0, 2, 1, 0, 1, 3)]
-    measured = time_stack(other, reps=3, seed=5)
+    measured = time_stack(other, reps=5, seed=5)
     pred = lut.predict(other)
-    assert abs(pred - measured) / measured < 0.35, (pred, measured)
+    print(f"predicted {pred:.1f} us, measured {measured:.1f} us", flush=True)
+    assert abs(pred - measured) / measured < 0.10, (pred, measured)

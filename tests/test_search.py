@@ -75,3 +75,16 @@ def test_generous_budget_takes_every_best_choice():
     best = list(np.argmax(p.score, axis=1))
     for s in (solve_exact(p, res=1.0), solve_greedy(p), solve_evolutionary(p, pop=16, generations=20)):
         assert s.choice == best
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_three_stage_search_finds_the_optimum_of_small_problems(seed):
+    """The staged search (relaxed seeding and exploration, tightening,
+    local search) reaches the exhaustive optimum on small problems and its
+    answer always fits the target budget."""
+    rng = np.random.default_rng(300 + seed)
+    p = _random_problem(rng, L=7, C=4, slack=0.2 + 0.6 * rng.random())
+    bf = brute_force(p)
+    ev = solve_evolutionary(p, pop=24, generations=30, seed=seed)
+    assert ev.feasible
+    assert ev.value == pytest.approx(bf.value, abs=1e-9)
