@@ -63,6 +63,8 @@ def _traffic(kernel_name: str, launches_per_step: int = 1):
 KERNEL_SOURCES = {
     "smfmac_i8_2of4_persistent": ["semi_structured_sparse_nm_amd/csrc/nm_spmm_smfmac_i8p.hip",
                                   "semi_structured_sparse_nm_amd/csrc/nm_common.hpp", "include/nm_sparse.h"],
+    "smfmac_i8_2of4_stationary": ["semi_structured_sparse_nm_amd/csrc/nm_spmm_smfmac_i8ws.hip",
+                                  "semi_structured_sparse_nm_amd/csrc/nm_common.hpp", "include/nm_sparse.h"],
 }
 
 

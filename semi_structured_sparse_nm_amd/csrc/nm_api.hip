@@ -99,6 +99,7 @@ enum Variant {
   V_GENERIC,
   V_SMFMAC_I8P,     // int8 2:4 sparse MFMA, persistent 256 x 128 tiles, cross-tile pipeline
   V_SMFMAC_I8P8,    // persistent, 8-wave workgroups (512 x 128 tiles, one per CU)
+  V_SMFMAC_I8WS,    // int8 2:4, K <= 768: packed rows held in registers, activations streamed
   V_SMFMAC_H,       // fp16 / bf16 2:4 sparse MFMA, persistent 256 x 128 tiles
   V_SMFMAC_HD,      // fp16 / bf16 2:4, decode shapes (T <= 16): K split across 8 waves
   V_EXPAND,         // any other N:M (int8, fp16, bf16): windows expanded in registers, dense MFMA
@@ -114,6 +115,7 @@ const char* variant_name(Variant v) {
     case V_GENERIC: return "generic_dense_expand";
     case V_SMFMAC_I8P: return "smfmac_i8_2of4_persistent";
     case V_SMFMAC_I8P8: return "smfmac_i8_2of4_persistent_w8";
+    case V_SMFMAC_I8WS: return "smfmac_i8_2of4_stationary";
     case V_SMFMAC_H: return "smfmac_h_2of4_persistent";
     case V_SMFMAC_HD: return "smfmac_h_2of4_decode";
     case V_EXPAND: return "expand_mfma_persistent";
@@ -148,6 +150,11 @@ bool eligible(Variant v, const Call& c) {
              aligned(c.X, 16) && (c.g->K + 128) * c.ldx < (1ll << 31) &&
              c.g->values_bytes() < (1ull << 31) && (c.g->R + 512) * c.ldy * 4 < (1ll << 31) &&
              (c.ydt == NM_I32 || (c.ydt == NM_I8 && c.ldy % 16 == 0 && aligned(c.Y, 16)));
+    case V_SMFMAC_I8WS:
+      // as the persistent kernels, and K in (640, 768] (six column blocks
+      // held in registers) with every XCD's workgroups (one per CU)
+      // covering the row tiles of 512 rows
+      return eligible(V_SMFMAC_I8P, c) && c.g->nKB == 6 && (c.g->R + 511) / 512 <= device_cus() / 8;
     case V_SMFMAC_H:
       // fp16 / bf16 2:4; X rows in whole 16-byte pieces; 32-bit buffer
       // offsets that do not wrap for the rows a tile reaches past K and R;
@@ -220,13 +227,22 @@ Variant choose_auto(const Call& c) {
   if (eligible(V_STREAM24, c) && c.g->nRB > device_cus()) return V_STREAM24;
   if (eligible(V_SMFMAC_HD, c)) return V_SMFMAC_HD;
   if (eligible(V_EXPAND_DECODE, c)) return V_EXPAND_DECODE;
+  // int8 2:4, K in (640, 768]: the weight-stationary kernel when its
+  // workgroups (one per CU) get at least 3.5 token steps of 64 each, so the
+  // one-time load of their packed rows is spread over enough products.
+  // Measured on MI355X at T = 12608, rotated operands (stationary /
+  // persistent us): FC1 R 3072 (4.6 steps) 31.3 / 38.8 (4-wave); QKV R 2304
+  // (3.8) 29.7 / 30.7 (8-wave); proj R 768 (1.5) 18.0 / 16.7 (8-wave).
+  if (eligible(V_SMFMAC_I8WS, c)) {
+    const int64_t steps = ((c.g->R + 511) / 512) * ((c.T + 63) / 64);
+    if (2 * steps >= 7 * (int64_t)device_cus()) return V_SMFMAC_I8WS;
+  }
   // int8 2:4 persistent: 8-wave workgroups (512 x 128 tiles, one per CU,
   // two waves per SIMD) unless the 256 x 128 tiles of the 4-wave kernel
   // (two workgroups per CU) number at least four per CU.  Measured on MI355X
-  // at T = 12608 (4-wave tiles; 4-wave / 8-wave / weight-stationary us):
-  // proj R 768 (297): 17.6 / 15.0 / 15.6; FC2 R 768, K 3072 (297): 43.3 /
-  // 36.5; QKV R 2304 (891): 30.2 / 25.7 / 28.7; FC1 R 3072 (1188): 31.5 /
-  // 33.1.  The weight-stationary kernel is no longer picked (forced only).
+  // at T = 12608 (4-wave tiles; 4-wave / 8-wave us): proj R 768 (297): 17.6
+  // / 15.0; FC2 R 768, K 3072 (297): 43.3 / 36.5; QKV R 2304 (891): 30.2 /
+  // 25.7; FC1 R 3072 (1188): 31.5 / 33.1.
   if (eligible(V_SMFMAC_I8P, c)) {
     const int64_t tiles4 = ((c.g->R + 255) / 256) * ((c.T + 127) / 128);
     if (tiles4 < 4 * (int64_t)device_cus() && eligible(V_SMFMAC_I8P8, c)) return V_SMFMAC_I8P8;
@@ -333,7 +349,7 @@ size_t repack_meta_off(const Geometry& g24) { return (g24.values_bytes() + 255) 
 size_t repack_bytes(const Geometry& g24) { return repack_meta_off(g24) + g24.meta_bytes(); }
 
 bool repack_inner(Variant v) {
-  return v == V_SMFMAC_I8P || v == V_SMFMAC_I8P8 || v == V_SMFMAC_H || v == V_SMFMAC_I8TK;
+  return v == V_SMFMAC_I8P || v == V_SMFMAC_I8P8 || v == V_SMFMAC_I8WS || v == V_SMFMAC_H || v == V_SMFMAC_I8TK;
 }
 
 // ---- [T][K] calls without a kernel of their own.  The generic kernel takes
@@ -435,6 +451,7 @@ const char* plan_name(const Plan& p) {
   switch (p.v) {
     case V_SMFMAC_I8P: return "repack24_smfmac_i8_2of4_persistent";
     case V_SMFMAC_I8P8: return "repack24_smfmac_i8_2of4_persistent_w8";
+    case V_SMFMAC_I8WS: return "repack24_smfmac_i8_2of4_stationary";
     case V_SMFMAC_H: return "repack24_smfmac_h_2of4_persistent";
     case V_SMFMAC_I8TK: return "repack24_smfmac_i8_2of4_tk";
     default: return "invalid";
@@ -584,6 +601,7 @@ nm_status run_variant(Variant v, int S, const SpmmArgs& a, void* part, hipStream
     case V_GENERIC: e = nm::launch_spmm_generic(a, s); break;
     case V_SMFMAC_I8P: e = nm::launch_spmm_smfmac_i8p(a, 0, s); break;
     case V_SMFMAC_I8P8: e = nm::launch_spmm_smfmac_i8p(a, 1, s); break;
+    case V_SMFMAC_I8WS: e = nm::launch_spmm_smfmac_i8ws(a, s); break;
     case V_SMFMAC_H: e = nm::launch_spmm_smfmac_h(a, s); break;
     case V_SMFMAC_HD: e = nm::launch_spmm_smfmac_hd(a, s); break;
     case V_EXPAND: e = nm::launch_spmm_expand(a, s); break;

@@ -95,6 +95,7 @@ hipError_t launch_pack(const void* W, int64_t ldw, const Geometry& g, int wdt, u
 hipError_t launch_spmm_generic(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8p(const SpmmArgs& a, int cfg, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8tk(const SpmmArgs& a, hipStream_t s);   // [T][K] layout
+hipError_t launch_spmm_smfmac_i8ws(const SpmmArgs& a, hipStream_t s);   // weight-stationary, K <= 768
 hipError_t launch_spmm_smfmac_h(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_smfmac_hd(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_expand(const SpmmArgs& a, hipStream_t s);
@@ -284,6 +285,28 @@ __device__ __forceinline__ float i8_pre(int acc, float s, float os) {
   float f = __fmul_rn((float)acc, s);
   if constexpr (ACT) f = __fmul_rn(gelu_f32(f), os);
   return f;
+}
+
+// Byte B of d = the low byte of f + m, the other bytes kept (B = 0: set to
+// zero).  With m = 1.5 * 2^23 and f in [-128, 127] the sum is exact in
+// binary32 after rounding f half-to-even to an integer, and its low byte is
+// that integer as two's-complement int8: the requantised value lands in
+// its packed position in one instruction (an SDWA destination select).
+template <int B>
+__device__ __forceinline__ void rne_i8_byte(uint32_t& d, float f, float m) {
+  static_assert(B >= 0 && B < 4, "byte 0..3");
+  if constexpr (B == 0)
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD"
+        : "=v"(d) : "v"(f), "v"(m));
+  else if constexpr (B == 1)
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(d) : "v"(f), "v"(m));
+  else if constexpr (B == 2)
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(d) : "v"(f), "v"(m));
+  else
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(d) : "v"(f), "v"(m));
 }
 
 // int8 requantisation: sat(rne(f32(a) * s)); `a` already includes the bias.

@@ -218,9 +218,9 @@ def test_activation_validation_and_variant_choice():
     L = nm.lib()
     va = lambda d, T, y, a: L.nm_spmm_variant_act(ctypes.byref(d), T, y, a).decode()
     fc1 = _desc(R=3072, K=768)
-    assert va(fc1, 12608, nm.NM_I8, 0) == "smfmac_i8_2of4_persistent"
-    assert va(fc1, 12608, nm.NM_I8, 1) == "smfmac_i8_2of4_persistent"
-    assert va(_desc(R=2304, K=768), 12608, nm.NM_I8, 1) == "smfmac_i8_2of4_persistent_w8"
+    assert va(fc1, 12608, nm.NM_I8, 0) == "smfmac_i8_2of4_stationary"
+    assert va(fc1, 12608, nm.NM_I8, 1) == "smfmac_i8_2of4_stationary"
+    assert va(_desc(R=768, K=768), 12608, nm.NM_I8, 1) == "smfmac_i8_2of4_persistent_w8"
     deep = _desc(R=3072, K=3072, N=1, M=4)
     assert va(deep, 12608, nm.NM_I8, 1) == "repack24_smfmac_i8_2of4_persistent"
     assert va(_desc(R=3072, K=3072, N=4, M=8), 12608, nm.NM_I8, 1) == "expand_mfma_persistent"
@@ -255,15 +255,19 @@ def test_tk_layout_validation():
 
 
 def test_int8_workgroup_size_choice():
-    """int8 2:4: 8-wave persistent workgroups unless the 4-wave kernel's
-    256 x 128 tiles number at least four per CU (256 CUs assumed without a
-    GPU): the ViT-B shapes at batch 64."""
+    """int8 2:4 (256 CUs assumed without a GPU), the ViT-B shapes at batch
+    64: the weight-stationary kernel for K in (640, 768] with at least 3.5
+    token steps per CU; else 8-wave persistent workgroups unless the 4-wave
+    kernel's 256 x 128 tiles number at least four per CU."""
     L = nm.lib()
     v = lambda R, K, T: L.nm_spmm_variant(ctypes.byref(_desc(R=R, K=K)), T, nm.NM_I8).decode()
-    assert v(3072, 768, 12608) == "smfmac_i8_2of4_persistent"        # FC1: 1188 tiles
-    assert v(2304, 768, 12608) == "smfmac_i8_2of4_persistent_w8"     # QKV: 891
-    assert v(768, 3072, 12608) == "smfmac_i8_2of4_persistent_w8"     # FC2: 297
-    assert v(768, 768, 12608) == "smfmac_i8_2of4_persistent_w8"      # proj: 297
+    assert v(3072, 768, 12608) == "smfmac_i8_2of4_stationary"        # FC1: 4.6 steps per CU
+    assert v(2304, 768, 12608) == "smfmac_i8_2of4_stationary"        # QKV: 3.8
+    assert v(768, 3072, 12608) == "smfmac_i8_2of4_persistent_w8"     # FC2: K past 768
+    assert v(768, 768, 12608) == "smfmac_i8_2of4_persistent_w8"      # proj: 1.5 steps, 297 tiles
+    assert v(3072, 768, 4096) == "smfmac_i8_2of4_persistent_w8"      # 1.5 steps: 384 tiles
+    assert v(3072, 640, 12608) == "smfmac_i8_2of4_persistent"        # K 640: five column blocks
+    assert v(16896, 768, 12608) == "smfmac_i8_2of4_persistent"       # 33 row tiles > 32 per XCD
 
 
 @pytest.mark.parametrize("N,M", [(1, 4), (1, 8), (2, 8)])
@@ -286,7 +290,7 @@ def test_repack24_choice_and_workspace(monkeypatch, N, M):
         return (vb + 255) // 256 * 256 + mb
 
     fc1 = _desc(R=3072, K=768, N=N, M=M)
-    assert q(fc1, 12608, nm.NM_I8) == ("repack24_smfmac_i8_2of4_persistent", copy_bytes(3072, 768, nm.NM_I8), 1)
+    assert q(fc1, 12608, nm.NM_I8) == ("repack24_smfmac_i8_2of4_stationary", copy_bytes(3072, 768, nm.NM_I8), 1)
     fc2 = _desc(R=768, K=3072, N=N, M=M)
     assert q(fc2, 12608, nm.NM_I8) == ("repack24_smfmac_i8_2of4_persistent_w8", copy_bytes(768, 3072, nm.NM_I8), 1)
     h = _desc(R=3072, K=768, N=N, M=M, dt=nm.NM_F16)

@@ -339,6 +339,37 @@ def test_fast_i8_variants(force_variant, variant, out, R, K, T):
     assert np.all(Y[:, T:] == 5), "writes beyond T"
 
 
+# the weight-stationary int8 2:4 kernel takes K in (640, 768] (six column
+# blocks in registers) and R <= 16384 (a workgroup per 512-row tile on each XCD)
+STAT_SHAPES = [(300, 768, 144), (17, 700, 16), (520, 768, 400), (1000, 656, 272), (2304, 768, 1040),
+               (3072, 768, 12608), (16384, 768, 64), (777, 768, 48)]
+
+
+@pytest.mark.parametrize("out", ["i8", "i32"])
+@pytest.mark.parametrize("R,K,T", STAT_SHAPES)
+def test_stationary_i8_variant(force_variant, out, R, K, T):
+    """Weight-stationary int8 2:4 kernel forced: ragged rows (row blocks past
+    R re-read the last one), a partial last column block, one to 197 token
+    steps over the XCDs, padded strides; nothing written past T."""
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    variant = "smfmac_i8_2of4_stationary"
+    force_variant(variant)
+    W, X, b, s = _inputs("i8", out, R, K, T, 2, 4, 8, f"stat-{out}-{R}-{K}-{T}")
+    p = nm.pack(torch.from_numpy(W).cuda(), 2, 4)
+    assert nm.variant(p, T, torch.int8 if out == "i8" else torch.int32) == variant
+    Y, _ = run(W, X, 2, 4, "i8", out, bias=b, scale=s, ldx_pad=32, ldy_pad=16 if out == "i8" else 3,
+               sentinel=5)
+    compare(Y[:, :T], reference(W, X, 2, 4, "i8", out, bias=b, scale=s), out, variant)
+    assert np.all(Y[:, T:] == 5), "writes beyond T"
+
+
+@pytest.mark.parametrize("R,K,T", [(300, 768, 144), (520, 768, 400), (1000, 656, 272)])
+def test_gelu_i8_stationary(force_variant, R, K, T):
+    """GELU between the two scales on the weight-stationary kernel."""
+    _gelu_case(force_variant, "smfmac_i8_2of4_stationary", "i8", "i8", 2, 4, R, K, T, 38)
+
+
 FAST_H = ["smfmac_h_2of4_persistent"]
 
 
@@ -792,7 +823,7 @@ def test_mlp_chain_full_size_sampled_columns():
     assert np.array_equal(y_gpu[:, agree], y_ref[:, agree])
 
 
-@pytest.mark.parametrize("variant", ["smfmac_i8_2of4_persistent", "smfmac_i8_2of4_persistent_w8"])
+@pytest.mark.parametrize("variant", FAST_I8)
 @pytest.mark.parametrize("R,K,T", [(300, 192, 144), (520, 768, 400), (259, 1280, 272)])
 def test_gelu_i8_persistent(force_variant, variant, R, K, T):
     """int8 2:4 persistent kernels (the ViT-B FC1 default) with GELU fused
