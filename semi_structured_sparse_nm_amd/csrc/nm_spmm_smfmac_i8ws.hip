@@ -114,9 +114,8 @@ smfmac_i8ws_kernel(SpmmArgs a, int mtiles, int nsteps, int nwg_xcd) {
 
   // ---- the wave's packed rows (lane (i, g): 16 bytes at row i, offset
   // 16 g of a block, meta dword g of row i; row blocks past R re-read the
-  // last one).  Column block 0 comes with the prologue; the first step
-  // loads the rest, so their latency overlaps its products (each waits only
-  // for its own registers).
+  // last one), all loaded in the prologue together with the first stage
+  // (56 loads per wave, within the 63 a wave can have outstanding).
   const int voff_v = li * 64 + lg * 16;
   const int voff_m = li * 16 + lg * 4;
   v4i av[NKB][RB];
@@ -126,10 +125,12 @@ smfmac_i8ws_kernel(SpmmArgs a, int mtiles, int nsteps, int nwg_xcd) {
     av[kb][rb] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, blk * 1024, 0));
     ai[kb][rb] = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, voff_m, blk * 256, 0);
   };
-  // prologue: block 0 of the rows, the bias and scale rows (zeros past R or
-  // when absent) and the first stage
+  // prologue: the rows, the bias and scale rows (zeros past R or when
+  // absent) and the first stage
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) load_a(0, rb);
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) load_a(kb, rb);
   uint8_t* const bsw = bsbuf + wave * 512;      // bias 256 B, then scale 256 B
   {
     const uint32_t bs = lds_addr(bsw);
@@ -270,13 +271,6 @@ smfmac_i8ws_kernel(SpmmArgs a, int mtiles, int nsteps, int nwg_xcd) {
   auto run_step = [&](auto stc, int s) __attribute__((always_inline)) {
     constexpr int ST = decltype(stc)::value;
     barrier_nofence();
-    if constexpr (ST == 2) {
-      // the first step: the rest of the packed rows first
-#pragma unroll
-      for (int kb = 1; kb < NKB; ++kb)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) load_a(kb, rb);
-    }
     Acc acc;
     compute(acc, ST == 1 ? xs1 : xs0, s + 1, ST == 1 ? xs0 : xs1);
     // the next stage (issued this step) and the previous step's stores:
@@ -284,15 +278,13 @@ smfmac_i8ws_kernel(SpmmArgs a, int mtiles, int nsteps, int nwg_xcd) {
     __builtin_amdgcn_s_waitcnt(waitcnt(0, 15));
     finish(acc, s * BN);
   };
-  // stage of step s: xs0 for s - sa even, xs1 for odd (ic<2>: the first
-  // step, in xs0)
-  run_step(ic<2>(), sa);
-  int s = sa + 1;
+  // stage of step s: xs0 for s - sa even, xs1 for odd
+  int s = sa;
   for (; s + 1 < sb; s += 2) {
-    run_step(ic<1>(), s);
-    run_step(ic<0>(), s + 1);
+    run_step(ic<0>(), s);
+    run_step(ic<1>(), s + 1);
   }
-  if (s < sb) run_step(ic<1>(), s);
+  if (s < sb) run_step(ic<0>(), s);
   __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
 #endif
 }
