@@ -100,6 +100,7 @@ enum Variant {
   V_SMFMAC_I8P,     // int8 2:4 sparse MFMA, persistent 256 x 128 tiles, cross-tile pipeline
   V_SMFMAC_I8P8,    // persistent, 8-wave workgroups (512 x 128 tiles, one per CU)
   V_SMFMAC_I8WS,    // int8 2:4, K <= 768: packed rows held in registers, activations streamed
+  V_SMFMAC_I8SM,    // int8 2:4, any T and row alignment: one wave per 16 x 16 output tile
   V_SMFMAC_H,       // fp16 / bf16 2:4 sparse MFMA, persistent 256 x 128 tiles
   V_SMFMAC_HD,      // fp16 / bf16 2:4, decode shapes (T <= 16): K split across 8 waves
   V_EXPAND,         // any other N:M (int8, fp16, bf16): windows expanded in registers, dense MFMA
@@ -116,6 +117,7 @@ const char* variant_name(Variant v) {
     case V_SMFMAC_I8P: return "smfmac_i8_2of4_persistent";
     case V_SMFMAC_I8P8: return "smfmac_i8_2of4_persistent_w8";
     case V_SMFMAC_I8WS: return "smfmac_i8_2of4_stationary";
+    case V_SMFMAC_I8SM: return "smfmac_i8_2of4_small";
     case V_SMFMAC_H: return "smfmac_h_2of4_persistent";
     case V_SMFMAC_HD: return "smfmac_h_2of4_decode";
     case V_EXPAND: return "expand_mfma_persistent";
@@ -150,6 +152,13 @@ bool eligible(Variant v, const Call& c) {
              aligned(c.X, 16) && (c.g->K + 128) * c.ldx < (1ll << 31) &&
              c.g->values_bytes() < (1ull << 31) && (c.g->R + 512) * c.ldy * 4 < (1ll << 31) &&
              (c.ydt == NM_I32 || (c.ydt == NM_I8 && c.ldy % 16 == 0 && aligned(c.Y, 16)));
+    case V_SMFMAC_I8SM:
+      // 2:4 int8, int8 or int32 output, any T and row alignment (byte
+      // gathers and byte / dword stores); 32-bit buffer offsets that do not
+      // wrap for the rows a block reaches past K and R
+      return c.wdt == NM_I8 && c.g->N == 2 && c.g->M == 4 && (c.ydt == NM_I8 || c.ydt == NM_I32) &&
+             (c.g->K + 128) * c.ldx < (1ll << 31) && c.g->values_bytes() < (1ull << 31) &&
+             (c.g->R + 16) * c.ldy * 4 < (1ll << 31);
     case V_SMFMAC_I8WS:
       // as the persistent kernels, and K in (640, 768] (six column blocks
       // held in registers) with every XCD's workgroups (one per CU)
@@ -248,6 +257,10 @@ Variant choose_auto(const Call& c) {
     if (tiles4 < 4 * (int64_t)device_cus() && eligible(V_SMFMAC_I8P8, c)) return V_SMFMAC_I8P8;
     return V_SMFMAC_I8P;
   }
+  // int8 2:4 the tile kernels do not take (T not a multiple of 16, rows not
+  // 16-byte aligned): one wave per output tile.  ViT-Tiny slice 192 x 192 x
+  // 197: see the measured figure in the variant's documentation
+  if (eligible(V_SMFMAC_I8SM, c)) return V_SMFMAC_I8SM;
   if (eligible(V_SMFMAC_H, c)) return V_SMFMAC_H;
   if (eligible(V_EXPAND, c)) return V_EXPAND;
   return V_GENERIC;
@@ -602,6 +615,7 @@ nm_status run_variant(Variant v, int S, const SpmmArgs& a, void* part, hipStream
     case V_SMFMAC_I8P: e = nm::launch_spmm_smfmac_i8p(a, 0, s); break;
     case V_SMFMAC_I8P8: e = nm::launch_spmm_smfmac_i8p(a, 1, s); break;
     case V_SMFMAC_I8WS: e = nm::launch_spmm_smfmac_i8ws(a, s); break;
+    case V_SMFMAC_I8SM: e = nm::launch_spmm_smfmac_i8small(a, s); break;
     case V_SMFMAC_H: e = nm::launch_spmm_smfmac_h(a, s); break;
     case V_SMFMAC_HD: e = nm::launch_spmm_smfmac_hd(a, s); break;
     case V_EXPAND: e = nm::launch_spmm_expand(a, s); break;

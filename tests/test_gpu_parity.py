@@ -370,6 +370,46 @@ def test_gelu_i8_stationary(force_variant, R, K, T):
     _gelu_case(force_variant, "smfmac_i8_2of4_stationary", "i8", "i8", 2, 4, R, K, T, 38)
 
 
+# the small int8 2:4 kernel: any T, rows at any byte alignment
+SMALL_SHAPES = [(192, 192, 197), (17, 8, 5), (300, 200, 33), (64, 768, 1), (520, 1000, 61), (16, 4096, 16),
+                (33, 132, 300)]
+
+
+@pytest.mark.parametrize("out", ["i8", "i32"])
+@pytest.mark.parametrize("R,K,T", SMALL_SHAPES)
+def test_small_i8_variant(force_variant, out, R, K, T):
+    """The one-wave-per-tile int8 2:4 kernel forced on odd token counts and
+    row pitches that are not multiples of 16 bytes (byte gathers, masked
+    token tails, ragged rows and column blocks); nothing written past T."""
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    variant = "smfmac_i8_2of4_small"
+    force_variant(variant)
+    W, X, b, s = _inputs("i8", out, R, K, T, 2, 4, 8, f"small-{out}-{R}-{K}-{T}")
+    p = nm.pack(torch.from_numpy(W).cuda(), 2, 4)
+    assert nm.variant(p, T, torch.int8 if out == "i8" else torch.int32) == variant
+    Y, _ = run(W, X, 2, 4, "i8", out, bias=b, scale=s, ldx_pad=3, ldy_pad=5, sentinel=5)
+    compare(Y[:, :T], reference(W, X, 2, 4, "i8", out, bias=b, scale=s), out, variant)
+    assert np.all(Y[:, T:] == 5), "writes beyond T"
+
+
+@pytest.mark.parametrize("R,K,T", [(192, 192, 197), (300, 200, 33)])
+def test_gelu_i8_small(force_variant, R, K, T):
+    """GELU between the two scales on the small kernel."""
+    _gelu_case(force_variant, "smfmac_i8_2of4_small", "i8", "i8", 2, 4, R, K, T, 39)
+
+
+def test_config1_runs_on_the_small_kernel():
+    """The ViT-Tiny slice (T = 197, 197-byte rows) takes the small sparse
+    kernel, not the generic fallback."""
+    import torch
+    import nm_inputs
+    import semi_structured_sparse_nm_amd as nm
+    L = nm_inputs.config1()[0]
+    p = nm.pack(torch.zeros((L.R, L.K), dtype=torch.int8, device="cuda"), L.N, L.M)
+    assert nm.variant(p, L.T, torch.int32) == "smfmac_i8_2of4_small"
+
+
 FAST_H = ["smfmac_h_2of4_persistent"]
 
 
