@@ -310,6 +310,18 @@ __device__ __forceinline__ void rne_i8_byte(uint32_t& d, float f, float m) {
         : "+v"(d) : "v"(f), "v"(m));
 }
 
+// Four values already clamped to [-128, 127], rounded half-to-even and
+// packed as the int8 bytes 0..3 of a dword (rne_i8_byte for each).
+__device__ __forceinline__ uint32_t pack_rne_i8x4(float f0, float f1, float f2, float f3) {
+  const float m = 12582912.0f;   // 1.5 * 2^23
+  uint32_t d;
+  rne_i8_byte<0>(d, f0, m);
+  rne_i8_byte<1>(d, f1, m);
+  rne_i8_byte<2>(d, f2, m);
+  rne_i8_byte<3>(d, f3, m);
+  return d;
+}
+
 // int8 requantisation: sat(rne(f32(a) * s)); `a` already includes the bias.
 // The product is one rounded binary32 multiply (no contraction into an fma),
 // then round-half-even and saturation.

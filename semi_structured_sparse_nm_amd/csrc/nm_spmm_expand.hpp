@@ -357,15 +357,11 @@ expand_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd, int gm) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const v4f sv = scale_vec(k, rb);
-          uint32_t bb[4];
+          float f[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float f = i8_pre<ACT>(acc[rb][tt][v], sv[v], osc);
-            f = __builtin_amdgcn_fmed3f(f, -128.0f, 127.0f);
-            bb[v] = __builtin_bit_cast(uint32_t, f + 12582912.0f);
-          }
-          d[rb] = (int)(__builtin_amdgcn_perm(bb[1], bb[0], 0x0c0c0400u) |
-                        __builtin_amdgcn_perm(bb[3], bb[2], 0x04000c0cu));
+          for (int v = 0; v < 4; ++v)
+            f[v] = __builtin_amdgcn_fmed3f(i8_pre<ACT>(acc[rb][tt][v], sv[v], osc), -128.0f, 127.0f);
+          d[rb] = (int)pack_rne_i8x4(f[0], f[1], f[2], f[3]);
         }
         // token 16 u + li: f = 2 (u & 1)
         *reinterpret_cast<v2i*>(os + ((512 * u + wb) ^ (16 * (u & 1)))) = v2i{d[0], d[1]};

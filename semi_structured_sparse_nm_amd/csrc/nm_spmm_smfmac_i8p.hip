@@ -38,7 +38,8 @@
 // Epilogue (int8 output), per half tile (64 tokens): f32(acc) * scale[r] (a
 // separately rounded product; the bias is the accumulator's start value),
 // clamp to [-128, 127], add 1.5 * 2^23 so the low byte is the round-half-even
-// int8; the four rows a lane holds for one token are packed into a dword, the
+// int8, written straight into its byte of the packed dword (SDWA); the four
+// rows a lane holds for one token are packed into a dword, the
 // four row blocks' dwords of one token into 16 bytes, written token-major to
 // a per-wave LDS area (16-byte chunk c of token t stored at c ^ f(t), which
 // keeps the 16-byte writes and the transpose reads conflict-free), then read
@@ -317,16 +318,11 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const v4f sv = scale_vec(k, rb);
-          uint32_t b[4];
+          float f[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float f = i8_pre<ACT>(acc[rb][tt][v], sv[v], osc);
-            f = __builtin_amdgcn_fmed3f(f, -128.0f, 127.0f);
-            b[v] = __builtin_bit_cast(uint32_t, f + 12582912.0f);
-          }
-          const uint32_t lo2 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
-          const uint32_t hi2 = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
-          d[rb] = (int)(lo2 | hi2);
+          for (int v = 0; v < 4; ++v)
+            f[v] = __builtin_amdgcn_fmed3f(i8_pre<ACT>(acc[rb][tt][v], sv[v], osc), -128.0f, 127.0f);
+          d[rb] = (int)pack_rne_i8x4(f[0], f[1], f[2], f[3]);
         }
         *reinterpret_cast<v4i*>(os + 1024 * u + wb[u & 1]) = v4i{d[0], d[1], d[2], d[3]};
       }

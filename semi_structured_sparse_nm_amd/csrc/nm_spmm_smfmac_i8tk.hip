@@ -279,16 +279,11 @@ smfmac_i8tk_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const v4f sv = scale_vec(k, rb);
-          uint32_t b[4];
+          float f[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float f = i8_pre<ACT>(acc[rb][tt][v], sv[v], osc);
-            f = __builtin_amdgcn_fmed3f(f, -128.0f, 127.0f);
-            b[v] = __builtin_bit_cast(uint32_t, f + 12582912.0f);
-          }
-          const uint32_t lo2 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
-          const uint32_t hi2 = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
-          *reinterpret_cast<uint32_t*>(os + 1024 * u + wr + 16 * (rb ^ sw)) = lo2 | hi2;
+          for (int v = 0; v < 4; ++v)
+            f[v] = __builtin_amdgcn_fmed3f(i8_pre<ACT>(acc[rb][tt][v], sv[v], osc), -128.0f, 127.0f);
+          *reinterpret_cast<uint32_t*>(os + 1024 * u + wr + 16 * (rb ^ sw)) = pack_rne_i8x4(f[0], f[1], f[2], f[3]);
         }
       }
       // the wave reads back only what it wrote (LDS operations of one wave
