@@ -114,8 +114,11 @@ smfmac_i8ws_kernel(SpmmArgs a, int mtiles, int nsteps, int nwg_xcd) {
 
   // ---- the wave's packed rows (lane (i, g): 16 bytes at row i, offset
   // 16 g of a block, meta dword g of row i; row blocks past R re-read the
-  // last one), all loaded in the prologue together with the first stage
-  // (56 loads per wave, within the 63 a wave can have outstanding).
+  // last one).  Column block 0 comes with the prologue; the first step
+  // issues its next-stage loads and then the other blocks' rows, so each
+  // block's products wait only for that block (the compiler counts the
+  // register loads issued after it, and the earlier direct-to-LDS loads
+  // can only make such a wait stricter).
   const int voff_v = li * 64 + lg * 16;
   const int voff_m = li * 16 + lg * 4;
   v4i av[NKB][RB];
@@ -125,12 +128,10 @@ smfmac_i8ws_kernel(SpmmArgs a, int mtiles, int nsteps, int nwg_xcd) {
     av[kb][rb] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, blk * 1024, 0));
     ai[kb][rb] = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, voff_m, blk * 256, 0);
   };
-  // prologue: the rows, the bias and scale rows (zeros past R or when
-  // absent) and the first stage
+  // prologue: block 0 of the rows, the bias and scale rows (zeros past R or
+  // when absent) and the first stage
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) load_a(kb, rb);
+  for (int rb = 0; rb < RB; ++rb) load_a(0, rb);
   uint8_t* const bsw = bsbuf + wave * 512;      // bias 256 B, then scale 256 B
   {
     const uint32_t bs = lds_addr(bsw);
@@ -170,7 +171,7 @@ smfmac_i8ws_kernel(SpmmArgs a, int mtiles, int nsteps, int nwg_xcd) {
   // of the next stage (step nx into stage np, when nx < sb) are issued
   // between the products of the first six fragments, one each.
   typedef v4i Acc[RB][TN];
-  auto compute = [&](Acc& acc, const uint8_t* sp, int nx, uint8_t* np) __attribute__((always_inline)) {
+  auto compute = [&](Acc& acc, const uint8_t* sp, int nx, uint8_t* np, bool spread) __attribute__((always_inline)) {
     constexpr int NF = NKB * TN;
     constexpr int PF = 1;
     v8i bf[PF + 1];
@@ -184,7 +185,7 @@ smfmac_i8ws_kernel(SpmmArgs a, int mtiles, int nsteps, int nwg_xcd) {
       for (int rb = 0; rb < RB; ++rb)
         acc[rb][tt] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(av[kb][rb], bf[f % (PF + 1)],
                                                               kb == 0 ? bias_vec(rb) : acc[rb][tt], ai[kb][rb], 0, 0);
-      if (f < NKB && nx < sb) issue_xb(nx, np, f);
+      if (f < NKB && nx < sb && spread) issue_xb(nx, np, f);
     }
   };
 
@@ -271,20 +272,33 @@ smfmac_i8ws_kernel(SpmmArgs a, int mtiles, int nsteps, int nwg_xcd) {
   auto run_step = [&](auto stc, int s) __attribute__((always_inline)) {
     constexpr int ST = decltype(stc)::value;
     barrier_nofence();
+    if constexpr (ST == 2) {
+      // the first step: its next-stage loads, then the rest of the rows
+      if (s + 1 < sb) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) issue_xb(s + 1, xs1, kb);
+      }
+#pragma unroll
+      for (int kb = 1; kb < NKB; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) load_a(kb, rb);
+    }
     Acc acc;
-    compute(acc, ST == 1 ? xs1 : xs0, s + 1, ST == 1 ? xs0 : xs1);
+    compute(acc, ST == 1 ? xs1 : xs0, s + 1, ST == 1 ? xs0 : xs1, ST != 2);
     // the next stage (issued this step) and the previous step's stores:
     // nothing else is outstanding
     __builtin_amdgcn_s_waitcnt(waitcnt(0, 15));
     finish(acc, s * BN);
   };
-  // stage of step s: xs0 for s - sa even, xs1 for odd
-  int s = sa;
+  // stage of step s: xs0 for s - sa even, xs1 for odd (ic<2>: the first
+  // step, in xs0)
+  run_step(ic<2>(), sa);
+  int s = sa + 1;
   for (; s + 1 < sb; s += 2) {
-    run_step(ic<0>(), s);
-    run_step(ic<1>(), s + 1);
+    run_step(ic<1>(), s);
+    run_step(ic<0>(), s + 1);
   }
-  if (s < sb) run_step(ic<0>(), s);
+  if (s < sb) run_step(ic<1>(), s);
   __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
 #endif
 }
