@@ -58,6 +58,14 @@ constexpr int TN = 8;              // token tiles (16 tokens) per wave
 constexpr int BN = TN * 16;        // 128 tokens per tile
 constexpr int STAGE = 128 * BN;    // bytes per X stage (16 KB)
 
+// X stages in LDS: three with 4-wave workgroups (two per CU), six with
+// 8-wave ones (one per CU), whose activation then arrives PX = stages - 1
+// blocks ahead of its products while the A fragments stay two ahead (three
+// register sets).  Shapes with a large activation per weight (ViT-B FC2:
+// K 3072, 38.7 MB of X) stream it from HBM, where two blocks of lead time
+// leave the waves waiting on memory.
+template <int NW> constexpr int x_stages() { return NW == 8 ? 6 : 3; }
+
 // ACT: the fused activation, a template parameter so that the plain
 // epilogue's kernel is unchanged by it
 template <int NW, bool OUT_I8, bool ACT = false>
@@ -67,12 +75,12 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BM = NW * RB * 16;           // rows per tile
   constexpr int DPW = STAGE / 1024 / NW;     // 1 KB direct-to-LDS loads per wave per block
-  // one group of loads per block and wave: A values + meta, X (+ bias and
-  // scale on a tile's first block)
+  constexpr int XS = x_stages<NW>();
+  constexpr int PX = XS - 1;                 // blocks the X loads run ahead
+  // per block and wave: an A group (A values + meta, and the bias and scale
+  // rows on a tile's first block) two blocks ahead, an X group PX ahead
 
-  __shared__ __attribute__((aligned(1024))) uint8_t xs0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs2[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t xsb[XS][STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t ostage[OUT_I8 ? NW * 4096 : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t bsbuf[NW * 4 * 512];
 
@@ -123,10 +131,7 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     const int c = (lane & 7) ^ (row & 7) ^ ((row >> 4) & 1);
     return row * ldx + 16 * c;
   };
-  auto xstage = [&](auto st) -> uint8_t* {
-    constexpr int S = decltype(st)::value;
-    return S == 0 ? xs0 : (S == 1 ? xs1 : xs2);
-  };
+  auto xstage = [&](auto st) -> uint8_t* { return xsb[decltype(st)::value]; };
 
   // ---- A fragments (lane (i, g): 16 bytes at row i, offset 16 g of a block,
   // meta dword g of row i) of this wave's row blocks
@@ -149,52 +154,42 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     return *reinterpret_cast<const v4f*>(bsw + 512 * (k & 3) + 256 + 4 * (16 * rb + 4 * lg));
   };
 
-  // ---- load cursor: tile lk (rows lr0, tokens lt0), block lkb; ln groups
-  // issued.  A group is issued in parts between the token tiles of a block:
-  // part rb < RB the A fragment of row block rb, then the X loads in two
-  // halves, then (first block of a tile) bias and scale.  Groups past the
-  // end (at most two) still issue their A and X loads, at the last block's
-  // addresses, into a stage and register set nobody reads again, so every
-  // group but a tile's first has the same number of direct-to-LDS loads.
-  // No load has all its lanes outside its operand (such a load returns at
-  // once, ahead of older loads; see nm_zero_page): row blocks past R read
-  // the last row block, X rows entirely past K read the zero page, absent
-  // bias / scale rows too.
-  int ln = 0, lk = 0, lkb = 0, lr0 = 0, lt0 = 0;
-  tile_of(0, lr0, lt0);
+  // ---- load cursors: the A cursor (tile ak, rows ar0, block akb; an
+  // groups issued) and the X cursor (tile xk, tokens xt0, block xkb; xn
+  // groups issued).  The loads of a block are issued in parts between the
+  // token tiles of an earlier block: parts rb < RB the A fragment of row
+  // block rb (A cursor), part RB (first block of a tile) the tile's bias and
+  // scale rows, then the A cursor moves on; parts RB + 1 and RB + 2 the X
+  // loads in two halves (X cursor), then the X cursor moves on.  Groups past
+  // the end still issue their A and X loads, at the last block's addresses,
+  // into a stage and register set nobody reads again, so every X group has
+  // the same number of direct-to-LDS loads.  No load has all its lanes
+  // outside its operand (such a load returns at once, ahead of older loads;
+  // see nm_zero_page): row blocks past R read the last row block, X rows
+  // entirely past K read the zero page, absent bias / scale rows too.
+  int an = 0, ak = 0, akb = 0, ar0 = 0, at0 = 0;
+  int xn = 0, xk = 0, xkb = 0, xr0 = 0, xt0 = 0;
+  tile_of(0, ar0, at0);
+  tile_of(0, xr0, xt0);
   int g_live = 0, g_rb0 = 0, g_soff = 0, g_krem = 0;
   const v4i rz = zero_rsrc();
-  auto load_part = [&](auto st, auto part) {
-    constexpr int S = decltype(st)::value;
+  auto load_part = [&](auto ast, auto xst, auto part) {
+    constexpr int AS = decltype(ast)::value;
     constexpr int P = decltype(part)::value;
     if constexpr (P == 0) {
-      g_live = __builtin_amdgcn_readfirstlane(ln < total ? 1 : 0);
-      g_rb0 = __builtin_amdgcn_readfirstlane((lr0 >> 4) + RB * wave);
-      g_soff = __builtin_amdgcn_readfirstlane(lkb * 128 * ldx + lt0);
-      g_krem = __builtin_amdgcn_readfirstlane((int)g.K - lkb * 128);   // rows of this block inside K
+      g_live = __builtin_amdgcn_readfirstlane(an < total ? 1 : 0);
+      g_rb0 = __builtin_amdgcn_readfirstlane((ar0 >> 4) + RB * wave);
     }
     if constexpr (P < RB) {
       // A first: the compiler's waits for these registers may then hold
       // back at most later A loads, never an X stage.
-      const int blk = __builtin_amdgcn_readfirstlane(min(g_rb0 + P, nRB - 1) * nKB + lkb);
-      av[S][P] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, blk * 1024, 0));
-      ai[S][P] = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, voff_m, blk * 256, 0);
-    } else if constexpr (P == RB || P == RB + 1) {
-      uint8_t* sp = xstage(st);
-      constexpr int H = DPW / 2, J0 = (P - RB) * H;
-#pragma unroll
-      for (int j = J0; j < J0 + H; ++j) {
-        const int d = wave * DPW + j;
-        // load d fills rows 8 d .. 8 d + 7 of the stage
-        if (8 * d < g_krem)
-          lds_dma16(rx, lds_addr(sp + d * 1024), xoff(j), g_soff);
-        else
-          lds_dma16(rz, lds_addr(sp + d * 1024), 16 * lane, 0);
-      }
-    } else {
-      if (g_live && lkb == 0) {
-        const uint32_t bs = bs_lds + 512 * (lk & 3);
-        const int row0 = __builtin_amdgcn_readfirstlane(lr0 + 64 * wave);
+      const int blk = __builtin_amdgcn_readfirstlane(min(g_rb0 + P, nRB - 1) * nKB + akb);
+      av[AS][P] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, blk * 1024, 0));
+      ai[AS][P] = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, voff_m, blk * 256, 0);
+    } else if constexpr (P == RB) {
+      if (g_live && akb == 0) {
+        const uint32_t bs = bs_lds + 512 * (ak & 3);
+        const int row0 = __builtin_amdgcn_readfirstlane(ar0 + 64 * wave);
         const int boff = 4 * row0;
         if (a.bias && row0 < (int)g.R)
           lds_dma4(rbias, bs, 4 * lane, boff);
@@ -205,20 +200,48 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         else
           lds_dma4(rz, bs + 256, 4 * lane, 0);
       }
-      ++ln;
-      if (g_live && ++lkb == nKB) {
-        lkb = 0;
-        if (++lk < nmine) tile_of(lk, lr0, lt0);
+      ++an;
+      if (g_live && ++akb == nKB) {
+        akb = 0;
+        if (++ak < nmine) tile_of(ak, ar0, at0);
+      }
+    } else {
+      if constexpr (P == RB + 1) {
+        g_soff = __builtin_amdgcn_readfirstlane(xkb * 128 * ldx + xt0);
+        g_krem = __builtin_amdgcn_readfirstlane((int)g.K - xkb * 128);   // rows of this block inside K
+      }
+      uint8_t* sp = xstage(xst);
+      constexpr int H = DPW / 2, J0 = (P - RB - 1) * H;
+#pragma unroll
+      for (int j = J0; j < J0 + H; ++j) {
+        const int d = wave * DPW + j;
+        // load d fills rows 8 d .. 8 d + 7 of the stage
+        if (8 * d < g_krem)
+          lds_dma16(rx, lds_addr(sp + d * 1024), xoff(j), g_soff);
+        else
+          lds_dma16(rz, lds_addr(sp + d * 1024), 16 * lane, 0);
+      }
+      if constexpr (P == RB + 2) {
+        const int live = __builtin_amdgcn_readfirstlane(xn < total ? 1 : 0);
+        ++xn;
+        if (live && ++xkb == nKB) {
+          xkb = 0;
+          if (++xk < nmine) tile_of(xk, xr0, xt0);
+        }
       }
     }
   };
   constexpr int NPART = RB + 3;
-  auto load_group = [&](auto st) {
-    load_part(st, ic<0>()); load_part(st, ic<1>()); load_part(st, ic<2>()); load_part(st, ic<3>());
-    load_part(st, ic<4>()); load_part(st, ic<5>()); load_part(st, ic<6>());
-  };
   static_assert(RB == 4 && NPART == 7, "load parts are spelled out for four row blocks");
-  // direct-to-LDS loads per group: DPW (plus 2 on a live tile's first block)
+  auto load_a_group = [&](auto ast) {
+    load_part(ast, ic<0>(), ic<0>()); load_part(ast, ic<0>(), ic<1>()); load_part(ast, ic<0>(), ic<2>());
+    load_part(ast, ic<0>(), ic<3>()); load_part(ast, ic<0>(), ic<4>());
+  };
+  auto load_x_group = [&](auto xst) {
+    load_part(ic<0>(), xst, ic<5>()); load_part(ic<0>(), xst, ic<6>());
+  };
+  // bias and scale loads issued with block m's A group: 2 on a live tile's
+  // first block
   auto group_size_extra = [&](int m) { return (m < total && m % nKB == 0) ? 2 : 0; };
 
   v4i acc[RB][TN];
@@ -245,13 +268,13 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   };
 
   // acc += A x B over one block (acc starts a tile at the tile's bias).  B
-  // fragments are read two token tiles ahead of their products; the next
-  // load group is issued right after the first token tile's products (see
-  // the header on waits).  One code path for every block: a second variant
+  // fragments are read two token tiles ahead of their products; the loads
+  // of later blocks (A set nas, X stage nxs) are issued in parts after the
+  // token tiles' products (see the header on waits).  One code path for every block: a second variant
   // for a tile's first block would give the compiler's load-wait bookkeeping
   // merged paths on which the A registers look freshly loaded, and it then
   // waits for every load in flight.
-  auto compute = [&](auto st, auto ast, auto nxt) {
+  auto compute = [&](auto st, auto ast, auto nas, auto nxs) {
     constexpr int AS = decltype(ast)::value;
     const uint8_t* sb = xstage(st);
     v8i bf[3];
@@ -265,7 +288,7 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
         acc[rb][tt] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(av[AS][rb], bf[tt % 3], acc[rb][tt], ai[AS][rb], 0, 0);
       // one part of the next load group after each token tile but the last
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (tt < NPART) load_part(nxt, ic<tt>());
+      if constexpr (tt < NPART) load_part(nas, nxs, ic<tt>());
       __builtin_amdgcn_sched_barrier(0);
     };
     static_assert(TN == 8 && NPART < TN, "token tiles are spelled out");
@@ -366,36 +389,64 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   int n = 0, ck = 0, ckb = 0, cr0, ct0;
   tile_of(0, cr0, ct0);
 
-  // wait until the stage of L(m) (and a tile's bias / scale rows) has
-  // landed, given the group issued after it.  Only direct-to-LDS loads are
-  // counted: they complete in issue order among themselves, but register
-  // loads of a later group (A fragments hitting in L2) may complete before
-  // them, so a count that included those could pass with the stage still in
-  // flight.  The group after holds DPW of them, plus 2 when it starts a
-  // live tile; the compiler's own waits cover the A registers.
-  auto wait_for_group = [&](int extra_after) {
-    if (extra_after)
-      __builtin_amdgcn_s_waitcnt(waitcnt(DPW + 2, 15));
+  // Waits count only direct-to-LDS loads: they complete in issue order
+  // among themselves, but register loads (A fragments hitting in L2) may
+  // complete before older ones, so a count that included those could pass
+  // with a stage still in flight; extra loads outstanding only make a wait
+  // stricter.  The compiler's own waits cover the A registers.
+  // - Block n's stage.  With PX = 2 the loads issued after X(n) are block
+  //   n + 1's bias and scale (2 on a live tile's first block) and X(n + 1)
+  //   (DPW); with PX > 2 at least the X groups n + 1 .. n + PX - 1.
+  // - A tile's bias and scale rows (issued with its first block's A group,
+  //   two blocks ahead, before that block's X group): with PX = 2 the same
+  //   count; with PX > 2 at least the next two X groups follow them.
+  auto wait_stage = [&](int m) {
+    if constexpr (PX == 2) {
+      if (group_size_extra(m + 1))
+        __builtin_amdgcn_s_waitcnt(waitcnt(DPW + 2, 15));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt(DPW, 15));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt((PX - 1) * DPW, 15));
+    }
+  };
+  auto wait_bias = [&](int m) {
+    if constexpr (PX == 2)
+      wait_stage(m);
     else
-      __builtin_amdgcn_s_waitcnt(waitcnt(DPW, 15));
+      __builtin_amdgcn_s_waitcnt(waitcnt(2 * DPW, 15));
   };
 
-  load_group(ic<0>());
-  load_group(ic<1>());
-  // tile 0's bias (group 0) has landed once group 1 is all that is left
-  wait_for_group(group_size_extra(1));
+  // prologue: A groups 0 and 1 (with the bias rows) and X groups 0 .. PX-1
+  load_a_group(ic<0>());
+  load_x_group(ic<0>());
+  load_a_group(ic<1>());
+  load_x_group(ic<1>());
+  if constexpr (PX > 2) {
+    load_x_group(ic<2 % XS>());
+    load_x_group(ic<3 % XS>());
+    load_x_group(ic<4 % XS>());
+    static_assert(PX == 2 || PX == 5, "prologue X groups are spelled out for 3 or 6 stages");
+    // one drain at the start
+    __builtin_amdgcn_s_waitcnt(waitcnt(0, 15));
+  } else {
+    // tile 0's bias (group 0) has landed once group 1 is all that is left
+    wait_stage(0);
+  }
   init_acc(0);
 
-  // One block: stage / register set ST = n % 3; its loads were issued two
-  // steps ago (or in the prologue).
+  // One block: X stage ST = n % XS, A register set ST % 3; its loads were
+  // issued PX and two blocks ago (or in the prologue).
   auto step = [&](auto st) {
     constexpr int ST = decltype(st)::value;
-    constexpr int NX = (ST + 2) % 3;
-    // groups past the end are issued too (see load_group), so L(n + 1) is
-    // always in flight behind L(n)
-    wait_for_group(group_size_extra(n + 1));
+    constexpr int AS = ST % 3;
+    constexpr int NA = (AS + 2) % 3;
+    constexpr int NXS = (ST + PX) % XS;
+    // groups past the end are issued too, so the counted loads are always
+    // in flight behind block n's
+    wait_stage(n);
     barrier_nofence();
-    compute(st, ic<ST>(), ic<NX>());
+    compute(st, ic<AS>(), ic<NA>(), ic<NXS>());
     ++n;
     if (++ckb < nKB) return;
     ckb = 0;
@@ -406,9 +457,9 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     ++ck;
     if (ck < nmine) {
       tile_of(ck, cr0, ct0);
-      // the next tile's bias rows arrive with its first group, L(n); the
-      // group after it and the epilogue's stores may still be in flight
-      wait_for_group(group_size_extra(n + 1));
+      // the next tile's bias rows arrived with block n's A group; later
+      // groups and the epilogue's stores may still be in flight
+      wait_bias(n);
       init_acc(ck);
     }
   };
@@ -416,14 +467,24 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   // test: no path from a step's end leads back to the loop head except the
   // real back edge (the compiler's own load-wait bookkeeping merges the
   // states of every edge into the head).
-  const int trips = total / 3, rest = total - 3 * trips;
+  const int trips = total / XS, rest = total - XS * trips;
   for (int it = 0; it < trips; ++it) {
     step(ic<0>());
     step(ic<1>());
     step(ic<2>());
+    if constexpr (XS == 6) {
+      step(ic<3 % XS>());
+      step(ic<4 % XS>());
+      step(ic<5 % XS>());
+    }
   }
   if (rest > 0) step(ic<0>());
   if (rest > 1) step(ic<1>());
+  if constexpr (XS == 6) {
+    if (rest > 2) step(ic<2>());
+    if (rest > 3) step(ic<3 % XS>());
+    if (rest > 4) step(ic<4 % XS>());
+  }
   __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
 #endif
 }
