@@ -6,15 +6,15 @@
 // parallelism ("Realizable N:M Sparse Transformer Inference via Search-Kernel
 // Co-Design", Sec. 4.1: keep enough blocks in flight at inference-sized
 // shapes) becomes a split of K inside a workgroup: one workgroup per 16-row
-// block, its eight waves each take an eighth of K, and their partial sums
-// meet in LDS at the end, added in wave order (deterministic).
+// block, its eight waves each take every eighth 64-column block, and their
+// partial sums meet in LDS at the end, added in wave order (deterministic).
 //
 // Per wave and 64-column block, four direct-to-LDS loads bring X (64 k x 16
 // tokens), the packed A fragment (1 KB) and its index words into one of
-// four LDS slots of the wave; the wave waits for its own loads with an exact
+// three LDS slots of the wave; the wave waits for its own loads with an exact
 // vmcnt count (no barrier in the loop) and reads A, the index words and the
-// B fragment (ds_read_b64_tr_b16) from LDS.  Groups past the end of the
-// wave's K range load nothing but zeros, which keeps the count exact.
+// B fragment (ds_read_b64_tr_b16) from LDS.  Groups past the wave's last
+// block re-read a valid block, which keeps the count exact.
 // Operand mapping as in the large-T fp16 kernel (B lane group h: elements
 // 0..7 = k 8 h .., 8..15 = k 32 + 8 h ..).
 #include "nm_common.hpp"
@@ -60,8 +60,11 @@ __global__ void __launch_bounds__(NWD * 64) smfmac_hd_kernel(SpmmArgs a) {
   const int nKB = (int)g.nKB;
   const int ldx = (int)a.ldx;
   const int rb = blockIdx.x;                    // 16-row block
-  const int kb0 = (wave * nKB) / NWD, kb1 = ((wave + 1) * nKB) / NWD;
-  const int nblk = kb1 - kb0;
+  // the waves take interleaved blocks (wave w: w, w + 8, ...), so the eight
+  // waves of a workgroup stream adjacent blocks of its row block at a time
+  // (measured on LLaMA-7B down 2:4, T = 16: 15.0 -> 14.5 us against
+  // contiguous eighths of K)
+  const int nblk = wave < nKB ? (nKB - 1 - wave) / NWD + 1 : 0;
 
   const v4i rx = make_rsrc(a.X, (int)(g.K * a.ldx * 2));
   const v4i rv = make_rsrc(a.values, (int)g.values_bytes());
@@ -80,15 +83,15 @@ __global__ void __launch_bounds__(NWD * 64) smfmac_hd_kernel(SpmmArgs a) {
   // index words: 128 bytes per block; lanes 32..63 repeat lanes 0..31
   const int moff = 4 * (lane & 31);
 
-  // group m (0 <= m < nblk: block kb0 + m) into slot m % D.  No load has all
+  // group m (0 <= m < nblk: block w + 8 m) into slot m % D.  No load has all
   // its lanes outside its operand (such a load returns at once, ahead of
   // older loads; see nm_zero_page): groups past the wave's last block re-read
   // a valid block into a slot nobody reads, X rows entirely past K read the
   // zero page, so every group is the same NLG in-order loads.
   const v4i rz = zero_rsrc();
-  const int kb_last = min(max(kb1 - 1, kb0), nKB - 1);
+  const int kb_last = nblk > 0 ? wave + NWD * (nblk - 1) : nKB - 1;
   auto issue = [&](int m, int s) {
-    const int kb = __builtin_amdgcn_readfirstlane(m < nblk ? kb0 + m : kb_last);
+    const int kb = __builtin_amdgcn_readfirstlane(m < nblk ? wave + NWD * m : kb_last);
     const int krem = __builtin_amdgcn_readfirstlane((int)g.K - kb * 64);
     uint8_t* sp = ws + s * SLOT;
     const int xs = __builtin_amdgcn_readfirstlane(kb * 64 * ldx * 2);
