@@ -274,18 +274,23 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
   // for a tile's first block would give the compiler's load-wait bookkeeping
   // merged paths on which the A registers look freshly loaded, and it then
   // waits for every load in flight.
-  auto compute = [&](auto st, auto ast, auto nas, auto nxs) {
+  auto compute = [&](auto st, auto ast, auto nas, auto nxs, bool live) {
     constexpr int AS = decltype(ast)::value;
     const uint8_t* sb = xstage(st);
     v8i bf[3];
+    if (live) {
 #pragma unroll
-    for (int tt = 0; tt < 3; ++tt) bf[tt] = bfrag(sb, tt);
+      for (int tt = 0; tt < 3; ++tt) bf[tt] = bfrag(sb, tt);
+    }
     auto tile = [&](auto ttc) {
       constexpr int tt = decltype(ttc)::value;
-      if constexpr (tt >= 1 && tt + 2 < TN) bf[(tt + 2) % 3] = bfrag(sb, tt + 2);
+      if (live) {
+        if constexpr (tt >= 1 && tt + 2 < TN) bf[(tt + 2) % 3] = bfrag(sb, tt + 2);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        acc[rb][tt] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(av[AS][rb], bf[tt % 3], acc[rb][tt], ai[AS][rb], 0, 0);
+        for (int rb = 0; rb < RB; ++rb)
+          acc[rb][tt] =
+              __builtin_amdgcn_smfmac_i32_16x16x128_i8(av[AS][rb], bf[tt % 3], acc[rb][tt], ai[AS][rb], 0, 0);
+      }
       // one part of the next load group after each token tile but the last
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (tt < NPART) load_part(nas, nxs, ic<tt>());
@@ -446,14 +451,20 @@ smfmac_i8p_kernel(SpmmArgs a, int mtiles, int ntiles, int nwg_xcd) {
     // in flight behind block n's
     wait_stage(n);
     barrier_nofence();
-    compute(st, ic<AS>(), ic<NA>(), ic<NXS>());
+    // a wave whose 64 rows of the tile lie past R (the last row tile of a
+    // shape that is not a multiple of BM) skips its products and epilogue;
+    // it still issues its share of the workgroup's loads and barriers
+    const bool live = __builtin_amdgcn_readfirstlane(cr0 + 64 * wave < (int)g.R ? 1 : 0) != 0;
+    compute(st, ic<AS>(), ic<NA>(), ic<NXS>(), live);
     ++n;
     if (++ckb < nKB) return;
     ckb = 0;
-    if constexpr (OUT_I8)
-      epilogue_i8(ck, cr0, ct0);
-    else
-      store_i32(cr0, ct0);
+    if (live) {
+      if constexpr (OUT_I8)
+        epilogue_i8(ck, cr0, ct0);
+      else
+        store_i32(cr0, ct0);
+    }
     ++ck;
     if (ck < nmine) {
       tile_of(ck, cr0, ct0);
