@@ -106,6 +106,7 @@ enum Variant {
   V_EXPAND,         // any other N:M (int8, fp16, bf16): windows expanded in registers, dense MFMA
   V_EXPAND_DECODE,  // any N:M, decode shapes (T <= 16): K split across 8 waves, dense MFMA
   V_SMFMAC_I8TK,    // int8 2:4 persistent, [T][K] layout (X [T][K], Y [T][R])
+  V_SMFMAC_I8WSTK,  // int8 2:4, K <= 768, [T][K] layout: packed rows held in registers
   V_STREAM24,       // fp16 / bf16 2:4, T <= 16 per token tile: one workgroup per CU walking row
                     // blocks, values straight to registers one 512-column segment ahead
   V_COUNT
@@ -123,6 +124,7 @@ const char* variant_name(Variant v) {
     case V_EXPAND: return "expand_mfma_persistent";
     case V_EXPAND_DECODE: return "expand_mfma_decode";
     case V_SMFMAC_I8TK: return "smfmac_i8_2of4_tk";
+    case V_SMFMAC_I8WSTK: return "smfmac_i8_2of4_stationary_tk";
     case V_STREAM24: return "smfmac_h_2of4_stream_decode";
     default: return "invalid";
   }
@@ -140,7 +142,7 @@ struct Call {
 
 bool eligible(Variant v, const Call& c) {
   // the [T][K] layout has kernels of its own (and the generic one)
-  if ((c.layout == NM_LAYOUT_TK) != (v == V_SMFMAC_I8TK) && v != V_GENERIC) return false;
+  if ((c.layout == NM_LAYOUT_TK) != (v == V_SMFMAC_I8TK || v == V_SMFMAC_I8WSTK) && v != V_GENERIC) return false;
   switch (v) {
     case V_GENERIC: return true;
     case V_SMFMAC_I8P:
@@ -211,6 +213,10 @@ bool eligible(Variant v, const Call& c) {
              (c.T + 128) * c.ldx < (1ll << 31) && c.g->values_bytes() < (1ull << 31) && c.g->R % 16 == 0 &&
              (c.T + 128) * c.ldy * 4 < (1ll << 31) && aligned(c.Y, 16) &&
              ((c.ydt == NM_I8 && c.ldy % 16 == 0) || (c.ydt == NM_I32 && c.ldy % 4 == 0));
+    case V_SMFMAC_I8WSTK:
+      // as the [T][K] persistent kernel, and K in (640, 768] with every
+      // XCD's workgroups (one per CU) covering the row tiles of 512 rows
+      return eligible(V_SMFMAC_I8TK, c) && c.g->nKB == 6 && (c.g->R + 511) / 512 <= device_cus() / 8;
     default: return false;
   }
 }
@@ -227,6 +233,14 @@ Variant choose(const Call& c) {
 }
 
 Variant choose_auto(const Call& c) {
+  // [T][K] layout, int8 2:4: the weight-stationary form under the same rule
+  // as in [K][T] (below), else the persistent kernel.  Measured on MI355X at
+  // T = 12608, rotated operands (stationary / persistent us): see the
+  // variant's documentation
+  if (eligible(V_SMFMAC_I8WSTK, c)) {
+    const int64_t steps = ((c.g->R + 511) / 512) * ((c.T + 63) / 64);
+    if (2 * steps >= 7 * (int64_t)device_cus()) return V_SMFMAC_I8WSTK;
+  }
   if (eligible(V_SMFMAC_I8TK, c)) return V_SMFMAC_I8TK;
   // decode shapes (few tokens), fp16 / bf16 2:4: with more 16-row blocks
   // than compute units, one workgroup per CU walking row blocks with its
@@ -362,7 +376,8 @@ size_t repack_meta_off(const Geometry& g24) { return (g24.values_bytes() + 255) 
 size_t repack_bytes(const Geometry& g24) { return repack_meta_off(g24) + g24.meta_bytes(); }
 
 bool repack_inner(Variant v) {
-  return v == V_SMFMAC_I8P || v == V_SMFMAC_I8P8 || v == V_SMFMAC_I8WS || v == V_SMFMAC_H || v == V_SMFMAC_I8TK;
+  return v == V_SMFMAC_I8P || v == V_SMFMAC_I8P8 || v == V_SMFMAC_I8WS || v == V_SMFMAC_H || v == V_SMFMAC_I8TK ||
+         v == V_SMFMAC_I8WSTK;
 }
 
 // ---- [T][K] calls without a kernel of their own.  The generic kernel takes
@@ -467,6 +482,7 @@ const char* plan_name(const Plan& p) {
     case V_SMFMAC_I8WS: return "repack24_smfmac_i8_2of4_stationary";
     case V_SMFMAC_H: return "repack24_smfmac_h_2of4_persistent";
     case V_SMFMAC_I8TK: return "repack24_smfmac_i8_2of4_tk";
+    case V_SMFMAC_I8WSTK: return "repack24_smfmac_i8_2of4_stationary_tk";
     default: return "invalid";
   }
 }
@@ -621,6 +637,7 @@ nm_status run_variant(Variant v, int S, const SpmmArgs& a, void* part, hipStream
     case V_EXPAND: e = nm::launch_spmm_expand(a, s); break;
     case V_EXPAND_DECODE: e = nm::launch_spmm_expand_decode(a, s); break;
     case V_SMFMAC_I8TK: e = nm::launch_spmm_smfmac_i8tk(a, s); break;
+    case V_SMFMAC_I8WSTK: e = nm::launch_spmm_smfmac_i8wstk(a, s); break;
     case V_STREAM24: e = launch_stream24(a, s); break;
     default: return NM_EINVAL;
   }

@@ -96,6 +96,7 @@ hipError_t launch_spmm_generic(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8p(const SpmmArgs& a, int cfg, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8tk(const SpmmArgs& a, hipStream_t s);   // [T][K] layout
 hipError_t launch_spmm_smfmac_i8ws(const SpmmArgs& a, hipStream_t s);   // weight-stationary, K <= 768
+hipError_t launch_spmm_smfmac_i8wstk(const SpmmArgs& a, hipStream_t s);   // weight-stationary, [T][K] layout
 hipError_t launch_spmm_smfmac_i8small(const SpmmArgs& a, hipStream_t s);   // any T, unaligned rows
 hipError_t launch_spmm_smfmac_h(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_smfmac_hd(const SpmmArgs& a, hipStream_t s);

@@ -298,7 +298,7 @@ def test_repack24_choice_and_workspace(monkeypatch, N, M):
     assert q(fc1, 256, nm.NM_I8)[:2] == ("expand_mfma_persistent", 0)        # R K T < 2^31
     assert q(fc1, 16, nm.NM_I8)[:2] == ("expand_mfma_decode", 0)
     tk = lambda d, T: L.nm_spmm_variant_tk(ctypes.byref(d), T, nm.NM_I8, 0).decode()
-    assert tk(fc1, 12608) == "repack24_smfmac_i8_2of4_tk"
+    assert tk(fc1, 12608) == "repack24_smfmac_i8_2of4_stationary_tk"
     assert tk(fc1, 256) == "transpose_expand_mfma_persistent"               # below the re-pack size
     monkeypatch.setenv("NM_SPMM_VARIANT", "expand_mfma_persistent")
     assert q(fc1, 12608, nm.NM_I8)[:2] == ("expand_mfma_persistent", 0)
@@ -330,7 +330,9 @@ def test_tk_transpose_choice_and_workspace(monkeypatch):
     assert tk(h, 3137, nm.NM_F16) == "transpose_smfmac_h_2of4_persistent"
     assert ws(h, 3137, nm.NM_F16) == r256(768 * 3152 * 2) + r256(3072 * 3152 * 2)
     assert tk(_desc(R=192, K=192, N=4, M=8), 197, nm.NM_I32) == "generic_dense_expand"
-    assert tk(_desc(R=3072, K=768), 12608, nm.NM_I8) == "smfmac_i8_2of4_tk"
+    assert tk(_desc(R=3072, K=768), 12608, nm.NM_I8) == "smfmac_i8_2of4_stationary_tk"
+    assert tk(_desc(R=768, K=768), 12608, nm.NM_I8) == "smfmac_i8_2of4_tk"      # proj: 1.5 steps per CU
+    assert tk(_desc(R=768, K=3072), 12608, nm.NM_I8) == "smfmac_i8_2of4_tk"     # FC2: K past 768
     assert ws(_desc(R=3072, K=768), 12608, nm.NM_I8) == 0
     assert _ws(d48, 12608, nm.NM_I8) == 0          # the [K][T] query: no transposes
     monkeypatch.setenv("NM_SPMM_VARIANT", "generic_dense_expand")

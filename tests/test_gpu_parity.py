@@ -936,6 +936,34 @@ def test_tk_fast_i8_gelu(force_variant):
     _tk_case("i8", "i8", 2, 4, 528, 768, 400, 44, act="gelu", xpad=16, variant="smfmac_i8_2of4_tk")
 
 
+# the weight-stationary int8 2:4 kernel of the [T][K] layout: K in (640, 768]
+# (six column blocks in registers), R a multiple of 16
+STAT_TK_SHAPES = [(528, 768, 400), (304, 700, 37), (16, 656, 16), (3072, 768, 1008), (2304, 768, 1040),
+                  (3072, 768, 12608)]
+
+
+@pytest.mark.parametrize("out", ["i8", "i32"])
+@pytest.mark.parametrize("R,K,T", STAT_TK_SHAPES)
+def test_tk_stationary_i8(force_variant, out, R, K, T):
+    """The weight-stationary kernel in the [T][K] layout: several row tiles
+    (rows of the last one past R), token steps with tokens past T, K not a
+    multiple of 128 (a token row's bytes past K meet zero weights), padded
+    strides, the full ViT-B FC1; nothing written past R."""
+    force_variant("smfmac_i8_2of4_stationary_tk")
+    _tk_case("i8", out, 2, 4, R, K, T, 51, xpad=(-K) % 16 + 16, variant="smfmac_i8_2of4_stationary_tk")
+
+
+def test_tk_stationary_i8_gelu(force_variant):
+    force_variant("smfmac_i8_2of4_stationary_tk")
+    _tk_case("i8", "i8", 2, 4, 528, 768, 400, 52, act="gelu", xpad=16, variant="smfmac_i8_2of4_stationary_tk")
+
+
+@pytest.mark.parametrize("N,M", [(1, 4), (2, 8)])
+def test_tk_stationary_repack24(force_variant, N, M):
+    force_variant("repack24_smfmac_i8_2of4_stationary_tk")
+    _tk_case("i8", "i8", N, M, 528, 768, 400, 53, xpad=16, variant="repack24_smfmac_i8_2of4_stationary_tk")
+
+
 @pytest.mark.parametrize("out", ["i8", "i32"])
 @pytest.mark.parametrize("N,M", [(1, 4), (1, 8), (2, 8)])
 @pytest.mark.parametrize("R,K,T", [(256, 192, 144), (528, 1288, 272), (304, 200, 37)])
