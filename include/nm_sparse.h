@@ -126,8 +126,14 @@ nm_status nm_pack(const void* W, int64_t ldw, nm_packed* desc, void* stream);
  * (R K T >= 2^31; either operand layout) it instead holds a copy of the weight re-packed
  * into the 2:4 layout (such a pattern is also a 2:4 pattern), which the 2:4
  * sparse-MFMA kernels then multiply: the 2:4 values_bytes rounded up to 256,
- * then the 2:4 meta_bytes.  Given less than that (or a workspace not 256-byte
- * aligned), nm_spmm runs the N:M kernel instead, with the same result.
+ * then the 2:4 meta_bytes.  For another int8 N:M (3:4, 4:4, 3:8 .. 8:8) with
+ * K in (640, 768] and a large product ([K][T] layout) it holds the weight
+ * split exactly into two 2:4 layers (every aligned group of four columns
+ * keeps at most four members: the first two nonzero ones in the first layer,
+ * the rest in the second), each laid out as the re-pack copy above and
+ * rounded up to 256 bytes, the second after the first.  Given less than that
+ * (or a workspace not 256-byte aligned), nm_spmm runs the N:M kernel
+ * instead, with the same result.
  * (nm_spmm_tk sizes its workspace with nm_spmm_tk_workspace_size.)
  * The caller owns the buffer; nm_spmm only writes it and
  * reads it back within the call's stream order, so calls that share one
@@ -213,11 +219,11 @@ nm_status nm_spmm_tk(const nm_packed* w, const void* Xt, int64_t ldx, int64_t T,
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation).  It allocates nothing: the workspace nm_spmm_act
  * would take (K-split partial sums, a 2:4 re-pack of a 1:4 / 1:8 / 2:8 int8
- * weight) is a scratch array of nm_spmm_noalloc_max_bytes() = 32 MiB that the
+ * weight, the two-layer split of another int8 N:M) is a scratch array of nm_spmm_noalloc_max_bytes() = 32 MiB that the
  * library holds on each device it runs on until the process ends.  Same
  * arguments, arithmetic and results as nm_spmm_act ([K][T] layout).  A call
  * whose K split needs more partial-sum bytes than the scratch holds returns
- * NM_EINVAL before launching anything; a re-pack copy that does not fit makes
+ * NM_EINVAL before launching anything; a re-pack or split copy that does not fit makes
  * the call run the N:M kernel instead (same result).  No kernel relies on
  * what an earlier call left in the scratch.  Every call on one device shares
  * its scratch: calls that overlap on one device (different streams, threads
@@ -238,7 +244,8 @@ const char* nm_status_str(nm_status s);
  * Name of the kernel variant nm_spmm would launch for these arguments
  * (static string; "invalid" when the arguments would be rejected).  A 1:4,
  * 1:8 or 2:8 product re-packed to 2:4 in the workspace is named
- * "repack24_" + the 2:4 kernel's name, a [T][K] call run through the [K][T]
+ * "repack24_" + the 2:4 kernel's name, the two-layer split
+ * "split24_smfmac_i8_stationary", a [T][K] call run through the [K][T]
  * kernels "transpose_" + that kernel's name (assuming the workspace
  * nm_spmm_workspace_size asks for).  For tests and profiling; launches
  * nothing.

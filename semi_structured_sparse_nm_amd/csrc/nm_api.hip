@@ -109,6 +109,8 @@ enum Variant {
   V_SMFMAC_I8WSTK,  // int8 2:4, K <= 768, [T][K] layout: packed rows held in registers
   V_STREAM24,       // fp16 / bf16 2:4, T <= 16 per token tile: one workgroup per CU walking row
                     // blocks, values straight to registers one 512-column segment ahead
+  V_SPLIT24_I8WS,   // int8 N:M, K <= 768: the weight split into two 2:4 layers in the
+                    // workspace, then a weight-stationary kernel over both
   V_COUNT
 };
 
@@ -126,6 +128,7 @@ const char* variant_name(Variant v) {
     case V_SMFMAC_I8TK: return "smfmac_i8_2of4_tk";
     case V_SMFMAC_I8WSTK: return "smfmac_i8_2of4_stationary_tk";
     case V_STREAM24: return "smfmac_h_2of4_stream_decode";
+    case V_SPLIT24_I8WS: return "split24_smfmac_i8_stationary";
     default: return "invalid";
   }
 }
@@ -139,6 +142,11 @@ struct Call {
   int act;
   int layout;
 };
+
+bool eligible(Variant v, const Call& c);
+
+// the 2:4 geometry of a weight's two-layer split (and of its 2:4 re-pack)
+Geometry geometry24(const Geometry& g) { return Geometry::make(g.R, g.K, 2, 4, g.eb); }
 
 bool eligible(Variant v, const Call& c) {
   // the [T][K] layout has kernels of its own (and the generic one)
@@ -217,22 +225,37 @@ bool eligible(Variant v, const Call& c) {
       // as the [T][K] persistent kernel, and K in (640, 768] with every
       // XCD's workgroups (one per CU) covering the row tiles of 512 rows
       return eligible(V_SMFMAC_I8TK, c) && c.g->nKB == 6 && (c.g->R + 511) / 512 <= device_cus() / 8;
+    case V_SPLIT24_I8WS: {
+      // int8, any N:M; the 2:4 layers' product as the persistent kernels
+      // take it, K in (640, 768] (six column blocks held in registers), at
+      // most one 256-row tile per workgroup (one per CU)
+      if (c.wdt != NM_I8 || !nm::split24_supported(*c.g)) return false;
+      const Geometry g24 = geometry24(*c.g);
+      Call c24 = c;
+      c24.g = &g24;
+      return eligible(V_SMFMAC_I8P, c24) && g24.nKB == 6 && (c.g->R + 255) / 256 <= device_cus() / 8 * 8;
+    }
     default: return false;
   }
 }
 
-Variant choose_auto(const Call& c);
+Variant choose_auto(const Call& c, bool ws_ok = true);
 
-Variant choose(const Call& c) {
+// ws_ok: variants that need a workspace copy of the weight may be chosen
+Variant choose(const Call& c, bool ws_ok = true) {
   const Forced f = forced();
   if (f.name[0]) {
     for (int v = V_GENERIC; v < V_COUNT; ++v)
-      if (strcmp(f.name, variant_name((Variant)v)) == 0 && eligible((Variant)v, c)) return (Variant)v;
+      if (strcmp(f.name, variant_name((Variant)v)) == 0 && eligible((Variant)v, c) &&
+          (ws_ok || v != V_SPLIT24_I8WS))
+        return (Variant)v;
   }
-  return choose_auto(c);
+  return choose_auto(c, ws_ok);
 }
 
-Variant choose_auto(const Call& c) {
+constexpr double kRepackMinWork = 2147483648.0;
+
+Variant choose_auto(const Call& c, bool ws_ok) {
   // [T][K] layout, int8 2:4: the weight-stationary form under the same rule
   // as in [K][T] (below), else the persistent kernel.  Measured on MI355X at
   // T = 12608, rotated operands, one box (stationary / persistent us): FC1
@@ -276,6 +299,13 @@ Variant choose_auto(const Call& c) {
   // 197: see the measured figure in the variant's documentation
   if (eligible(V_SMFMAC_I8SM, c)) return V_SMFMAC_I8SM;
   if (eligible(V_SMFMAC_H, c)) return V_SMFMAC_H;
+  // int8 N:M with up to four kept members per group of four columns (3:4,
+  // 4:4, 3:8 .. 8:8), K in (640, 768], large enough for the extra launch:
+  // the two-layer split and the weight-stationary kernel over both layers
+  // (1:4, 1:8, 2:8 take the single-layer re-pack below instead)
+  if (ws_ok && eligible(V_SPLIT24_I8WS, c) && !(c.g->N == 2 && c.g->M == 4) && !nm::repack24_supported(*c.g) &&
+      (double)c.g->R * (double)c.g->K * (double)c.T >= kRepackMinWork)
+    return V_SPLIT24_I8WS;
   if (eligible(V_EXPAND, c)) return V_EXPAND;
   return V_GENERIC;
 }
@@ -360,12 +390,12 @@ size_t workspace_for(Variant v, const Call& c) {
 // one.
 // NM_SPMM_VARIANT=repack24_<2:4 tile variant> forces it (fp16 / bf16 too)
 // where the 2:4 kernel's requirements hold.
-constexpr double kRepackMinWork = 2147483648.0;
 constexpr const char* kRepackPrefix = "repack24_";
 
 struct Plan {
   Variant v = V_INVALID;
   bool repack = false;
+  bool split = false;        // two 2:4 layers in the workspace (g24 each)
   Geometry g24;              // the 2:4 geometry of the re-packed copy
   bool transpose = false;    // [T][K] call run as transpose, [K][T] product, transpose
   int64_t Tp = 0;            // tokens of the [K][T] product (T rounded up to 16)
@@ -374,6 +404,9 @@ struct Plan {
 
 size_t repack_meta_off(const Geometry& g24) { return (g24.values_bytes() + 255) / 256 * 256; }
 size_t repack_bytes(const Geometry& g24) { return repack_meta_off(g24) + g24.meta_bytes(); }
+// the two layers of a split: layer l's values at l * split_layer_bytes, its
+// meta repack_meta_off further
+size_t split_layer_bytes(const Geometry& g24) { return (repack_bytes(g24) + 255) / 256 * 256; }
 
 bool repack_inner(Variant v) {
   return v == V_SMFMAC_I8P || v == V_SMFMAC_I8P8 || v == V_SMFMAC_I8WS || v == V_SMFMAC_H || v == V_SMFMAC_I8TK ||
@@ -402,6 +435,7 @@ Call transposed_call(const Call& c, int64_t Tp) {
 
 size_t plan_workspace(const Plan& p, const Call& c) {
   if (p.repack) return repack_bytes(p.g24);
+  if (p.split) return 2 * split_layer_bytes(p.g24);
   if (p.transpose)
     return xkt_bytes(*c.g, p.Tp) + ykt_bytes(*c.g, p.Tp, c.ydt) + (p.S > 1 ? (size_t)p.S * c.g->R * p.Tp * 4 : 0);
   return workspace_for(p.v, c);
@@ -416,6 +450,13 @@ Plan plan_for(const Call& c) {
   const bool forced_rp = forced && strncmp(force, kRepackPrefix, strlen(kRepackPrefix)) == 0;
   const bool forced_tr = forced && strncmp(force, kTransposePrefix, strlen(kTransposePrefix)) == 0;
   const double work = (double)c.g->R * (double)c.g->K * (double)c.T;
+
+  // two-layer split (its own variant)
+  if (p.v == V_SPLIT24_I8WS) {
+    p.split = true;
+    p.g24 = geometry24(*c.g);
+    return p;
+  }
 
   // 2:4 re-pack
   if (nm::repack24_supported(*c.g) && (!forced || forced_rp) &&
@@ -452,9 +493,9 @@ Plan plan_for(const Call& c) {
       for (int v = V_GENERIC + 1; v < V_COUNT; ++v)
         if (strcmp(name, variant_name((Variant)v)) == 0 && eligible((Variant)v, ckt)) inner = (Variant)v;
     } else {
-      inner = choose_auto(ckt);
+      inner = choose_auto(ckt, false);
     }
-    if (inner != V_INVALID && inner != V_GENERIC) {
+    if (inner != V_INVALID && inner != V_GENERIC && inner != V_SPLIT24_I8WS) {
       p.v = inner;
       p.transpose = true;
       p.Tp = Tp;
@@ -639,6 +680,7 @@ nm_status run_variant(Variant v, int S, const SpmmArgs& a, void* part, hipStream
     case V_SMFMAC_I8TK: e = nm::launch_spmm_smfmac_i8tk(a, s); break;
     case V_SMFMAC_I8WSTK: e = nm::launch_spmm_smfmac_i8wstk(a, s); break;
     case V_STREAM24: e = launch_stream24(a, s); break;
+    case V_SPLIT24_I8WS: e = nm::launch_spmm_smfmac_i8ws2(a, s); break;
     default: return NM_EINVAL;
   }
   return e == hipSuccess ? NM_OK : NM_EHIP;
@@ -667,10 +709,10 @@ nm_status spmm_call(const nm_packed* w, const void* X, int64_t ldx, int64_t T, v
   // a workspace too small (or not 256-byte aligned) for the re-packed copy
   // or the transposed operands: the kernel the plain choice gives (same
   // result)
-  if ((pl.repack || pl.transpose) &&
+  if ((pl.repack || pl.transpose || pl.split) &&
       (!workspace || workspace_bytes < plan_workspace(pl, call) || !aligned(workspace, 256))) {
     pl = Plan();
-    pl.v = choose(call);
+    pl.v = choose(call, false);
   }
   const Variant v = pl.v;
   const int S = pl.repack ? 1 : pl.transpose ? pl.S : ksplit_for(v, call);
@@ -709,6 +751,18 @@ nm_status spmm_call(const nm_packed* w, const void* X, int64_t ldx, int64_t T, v
     a.g = pl.g24;
     a.values = wv;
     a.meta = wm;
+  }
+  if (pl.split) {
+    uint8_t* l0 = static_cast<uint8_t*>(workspace);
+    uint8_t* l1 = l0 + split_layer_bytes(pl.g24);
+    const size_t mo = repack_meta_off(pl.g24);
+    e = nm::launch_split24(g, a.values, a.meta, pl.g24, l0, l0 + mo, l1, l1 + mo, s);
+    if (e != hipSuccess) return NM_EHIP;
+    a.g = pl.g24;
+    a.values = l0;
+    a.meta = l0 + mo;
+    a.values2 = l1;
+    a.meta2 = l1 + mo;
   }
   if (pl.transpose) {
     // X [T][K] -> X' [K][T'], the [K][T] product into Y' [R][T'], Y' -> Y [T][R]

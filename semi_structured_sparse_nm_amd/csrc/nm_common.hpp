@@ -87,6 +87,10 @@ struct SpmmArgs {
   // operand layout: NM_LAYOUT_KT (X [K][ldx], Y [R][ldy]) or NM_LAYOUT_TK
   // (X [T][ldx] with K contiguous, Y [T][ldy] with R contiguous)
   int layout;
+  // second 2:4 layer of a weight split into two (launch_split24; values /
+  // meta hold the first): same geometry g, same block layout; nullptr else
+  const uint8_t* values2 = nullptr;
+  const uint8_t* meta2 = nullptr;
 };
 
 // Kernel variants; each launcher returns hipSuccess or the launch error.
@@ -96,6 +100,9 @@ hipError_t launch_spmm_generic(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8p(const SpmmArgs& a, int cfg, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8tk(const SpmmArgs& a, hipStream_t s);   // [T][K] layout
 hipError_t launch_spmm_smfmac_i8ws(const SpmmArgs& a, hipStream_t s);   // weight-stationary, K <= 768
+// weight-stationary over a weight split into two 2:4 layers (a.values /
+// a.meta and a.values2 / a.meta2), K <= 768
+hipError_t launch_spmm_smfmac_i8ws2(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8wstk(const SpmmArgs& a, hipStream_t s);   // weight-stationary, [T][K] layout
 hipError_t launch_spmm_smfmac_i8small(const SpmmArgs& a, hipStream_t s);   // any T, unaligned rows
 hipError_t launch_spmm_smfmac_h(const SpmmArgs& a, hipStream_t s);
@@ -109,6 +116,13 @@ bool expand_supported(int N, int M);   // N:M instantiated by launch_spmm_expand
 bool repack24_supported(const Geometry& g);
 hipError_t launch_repack24(const Geometry& gs, const uint8_t* values, const uint8_t* meta, const Geometry& gd,
                            uint8_t* dvalues, uint8_t* dmeta, hipStream_t s);
+// Any N:M weight (M 4 or 8) split exactly into two 2:4 layers of the same
+// matrix (gd: Geometry::make(R, K, 2, 4, eb)): in every aligned group of four
+// columns the first two nonzero kept members (ascending position) go to the first
+// layer, the others (at most two) to the second.
+bool split24_supported(const Geometry& g);
+hipError_t launch_split24(const Geometry& gs, const uint8_t* values, const uint8_t* meta, const Geometry& gd,
+                          uint8_t* dvalues0, uint8_t* dmeta0, uint8_t* dvalues1, uint8_t* dmeta1, hipStream_t s);
 // dst[j][i] = src[i][j] (i < rows, j < cols), zeros for rows <= i < dst_cols;
 // elements of eb bytes, row pitches lds / ldd in elements.
 hipError_t launch_transpose(const void* src, int64_t rows, int64_t cols, int64_t lds, void* dst, int64_t ldd,

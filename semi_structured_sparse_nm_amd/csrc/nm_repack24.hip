@@ -135,6 +135,131 @@ __global__ void __launch_bounds__(256) repack24_kernel(Geometry gs, const uint8_
   *reinterpret_cast<uint32_t*>(dm + blk * gd.mblk + (int64_t)rr * gd.MR + 4 * j) = dpos;
 }
 
+// ---- split into two 2:4 layers.  Any N:M pattern (M = 4 or 8) holds at
+// most four kept members in an aligned group of four columns, so two 2:4
+// layers hold it exactly: the first layer takes the group's first two
+// nonzero members in ascending position, the second the rest (the product
+// is the sum of the two layers' products, each on the sparse matrix
+// instructions; members holding zero add nothing and are left out, so
+// padding stays in the packed format's padding form).
+// A layer's group with two members stores them at their positions; with
+// one member v at q, (v, 0) at (0, 1) when q = 0, else (0, v) at (0, q);
+// with none, (0, 0) at (0, 1): two distinct ascending positions always.
+// For M = 8 a group of eight is two groups of four: members below position
+// 4 belong to the lower one, in order, the rest to the upper one.
+//
+// int8 only.  One thread per (row, column block, 8 columns): it loads the
+// source's kept values and position bits of those 8 columns (a few dwords,
+// all issued before any is used) and writes, per layer, the 4 value bytes
+// (one dword) and the 8 position bits (one byte) of the 2:4 layout.
+template <int M, int N>
+__global__ void __launch_bounds__(256) split24_kernel(Geometry gs, const uint8_t* __restrict__ sv,
+                                                      const uint8_t* __restrict__ sm, Geometry gd,
+                                                      uint8_t* __restrict__ dv0, uint8_t* __restrict__ dm0,
+                                                      uint8_t* __restrict__ dv1, uint8_t* __restrict__ dm1) {
+  constexpr int SG = 8 / M;             // source groups per thread
+  constexpr int NS = SG * N;            // source slots per thread (at most 8)
+  constexpr int W = N == M ? 0 : (M == 4 ? 2 : 3);   // position bits (none when N = M)
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = gs.nRB * 16 * gs.nKB * 16;
+  if (tid >= total) return;
+  const int t = (int)(tid & 15);         // 8-column group of the block row
+  const int64_t rk = tid >> 4;
+  const int64_t kb = rk % gs.nKB;
+  const int64_t r = rk / gs.nKB;         // row, padding rows included
+  const int64_t blk = (r >> 4) * gs.nKB + kb;
+  const int rr = (int)(r & 15);
+  const int c0 = t * NS;                 // first source slot
+
+  // every load up front: the dwords holding the NS value bytes (reads past
+  // the row stay inside the values buffer or are skipped) and the two
+  // dwords of the row's position bitstream holding the NS W bits
+  const int64_t vb = blk * gs.vblk + (int64_t)rr * gs.C + c0;
+  const int64_t va = vb & ~(int64_t)3;
+  const int64_t vend = (int64_t)gs.values_bytes();
+  const uint32_t* vw = reinterpret_cast<const uint32_t*>(sv + va);
+  uint32_t w0 = vw[0];
+  uint32_t w1 = va + 4 < vend ? vw[1] : 0u;
+  uint32_t w2 = va + 8 < vend ? vw[2] : 0u;
+  uint64_t pbits = 0;
+  if constexpr (W != 0) {
+    const uint32_t* mrow = reinterpret_cast<const uint32_t*>(sm + blk * gs.mblk + (int64_t)rr * gs.MR);
+    const int b0 = c0 * W, wi = b0 >> 5, nd = gs.MR / 4;
+    const uint32_t m0 = mrow[wi];
+    const uint32_t m1 = wi + 1 < nd ? mrow[wi + 1] : 0u;
+    pbits = ((uint64_t)m0 | (uint64_t)m1 << 32) >> (b0 & 31);
+  }
+  const int sh = (int)(vb & 3);
+  const uint64_t lo = ((uint64_t)w0 | (uint64_t)w1 << 32) >> (8 * sh);
+  const uint64_t vbits = sh ? lo | ((uint64_t)w2 << (64 - 8 * sh)) : lo;
+  auto value = [&](int sl) { return (uint32_t)(vbits >> (8 * sl)) & 0xFFu; };
+  auto position = [&](int sl) -> uint32_t {
+    if constexpr (W == 0)
+      return (uint32_t)(sl % M);
+    else
+      return (uint32_t)(pbits >> (sl * W)) & (uint32_t)(M - 1);
+  };
+
+  uint32_t dval[2] = {0u, 0u};           // per layer: 4 slots, one byte each
+  uint32_t dpos[2] = {0u, 0u};           // per layer: 4 slots, 2 bits each
+#pragma unroll
+  for (int q = 0; q < SG; ++q) {
+    constexpr int H = M / 4;             // groups of four per source group
+    uint32_t v[N], p[N], rank[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      v[i] = value(q * N + i);
+      p[i] = position(q * N + i);
+    }
+    // rank of each nonzero member among the nonzero members of its group of four
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      rank[i] = 0;
+#pragma unroll
+      for (int j = 0; j < i; ++j)
+        rank[i] += (v[j] != 0u && (M == 4 || (p[j] >> 2) == (p[i] >> 2))) ? 1u : 0u;
+    }
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const int d = q * H + h;           // destination group of four (0 or 1)
+#pragma unroll
+      for (int L = 0; L < 2; ++L) {
+        // the nonzero members of rank 2L and 2L + 1 within this group of four
+        uint32_t xa = 0, pa = 0, xb = 0, pb = 0;
+        bool ha = false, hb = false;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const bool in = v[i] != 0u && (M == 4 || (p[i] >> 2) == (uint32_t)h);
+          const bool a = in && rank[i] == (uint32_t)(2 * L), b = in && rank[i] == (uint32_t)(2 * L + 1);
+          xa |= a ? v[i] : 0u;
+          pa |= a ? (p[i] & 3u) : 0u;
+          ha = ha || a;
+          xb |= b ? v[i] : 0u;
+          pb |= b ? (p[i] & 3u) : 0u;
+          hb = hb || b;
+        }
+        uint32_t s0, s1, q0, q1;
+        if (hb) {                        // two members (ascending positions)
+          s0 = xa; s1 = xb; q0 = pa; q1 = pb;
+        } else if (ha) {                 // one member
+          s0 = pa == 0 ? xa : 0u; s1 = pa == 0 ? 0u : xa; q0 = 0u; q1 = pa == 0 ? 1u : pa;
+        } else {                         // none
+          s0 = 0u; s1 = 0u; q0 = 0u; q1 = 1u;
+        }
+        dval[L] |= (s0 | (s1 << 8)) << (16 * d);
+        dpos[L] |= (q0 | (q1 << 2)) << (4 * d);
+      }
+    }
+  }
+
+  const int64_t ov = blk * gd.vblk + (int64_t)rr * gd.C + 4 * t;
+  const int64_t om = blk * gd.mblk + (int64_t)rr * gd.MR + t;
+  *reinterpret_cast<uint32_t*>(dv0 + ov) = dval[0];
+  *reinterpret_cast<uint32_t*>(dv1 + ov) = dval[1];
+  dm0[om] = (uint8_t)dpos[0];
+  dm1[om] = (uint8_t)dpos[1];
+}
+
 }  // namespace
 
 bool repack24_supported(const Geometry& g) {
@@ -155,6 +280,28 @@ hipError_t launch_repack24(const Geometry& gs, const uint8_t* values, const uint
   }
   NM_REPACK(1, 4, 1) NM_REPACK(1, 8, 1) NM_REPACK(1, 8, 2) NM_REPACK(2, 4, 1) NM_REPACK(2, 8, 1) NM_REPACK(2, 8, 2)
 #undef NM_REPACK
+  return hipErrorInvalidValue;
+}
+
+
+bool split24_supported(const Geometry& g) { return g.eb == 1 && (g.M == 4 || g.M == 8); }
+
+hipError_t launch_split24(const Geometry& gs, const uint8_t* values, const uint8_t* meta, const Geometry& gd,
+                          uint8_t* dvalues0, uint8_t* dmeta0, uint8_t* dvalues1, uint8_t* dmeta1, hipStream_t s) {
+  if (!split24_supported(gs) || gd.N != 2 || gd.M != 4 || gd.eb != gs.eb || gd.nRB != gs.nRB || gd.nKB != gs.nKB)
+    return hipErrorInvalidValue;
+  const int64_t total = gs.nRB * 16 * gs.nKB * 16;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+#define NM_SPLIT(M_, N_)                                                                                 \
+  if (gs.M == M_ && gs.N == N_) {                                                                        \
+    hipLaunchKernelGGL((split24_kernel<M_, N_>), grid, block, 0, s, gs, values, meta, gd, dvalues0, dmeta0, \
+                       dvalues1, dmeta1);                                                                \
+    return hipGetLastError();                                                                            \
+  }
+  NM_SPLIT(4, 1) NM_SPLIT(4, 2) NM_SPLIT(4, 3) NM_SPLIT(4, 4)
+  NM_SPLIT(8, 1) NM_SPLIT(8, 2) NM_SPLIT(8, 3) NM_SPLIT(8, 4) NM_SPLIT(8, 5) NM_SPLIT(8, 6) NM_SPLIT(8, 7)
+  NM_SPLIT(8, 8)
+#undef NM_SPLIT
   return hipErrorInvalidValue;
 }
 

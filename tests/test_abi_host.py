@@ -308,6 +308,47 @@ def test_repack24_choice_and_workspace(monkeypatch, N, M):
     assert q(h, 3136, nm.NM_F16) == ("repack24_smfmac_h_2of4_persistent", copy_bytes(3072, 768, nm.NM_F16), 1)
 
 
+def _split_bytes(R, K):
+    """Workspace of the two-layer split: two 2:4 copies (values, then meta at
+    the next 256-byte boundary), each rounded up to 256 bytes."""
+    vb, mb = nm.pack_size(R, K, 2, 4, nm.NM_I8)
+    return 2 * (((vb + 255) // 256 * 256 + mb + 255) // 256 * 256)
+
+
+@pytest.mark.parametrize("N,M", [(3, 4), (4, 4), (3, 8), (4, 8), (8, 8)])
+def test_split24_choice_and_workspace(monkeypatch, N, M):
+    """int8 N:M with more than two kept members per group of four, K in
+    (640, 768], large enough (R K T >= 2^31): split into two 2:4 layers and
+    the weight-stationary kernel over both, with the two copies' workspace;
+    deeper K, small products, fp16 weights, decode shapes, more than 256
+    row tiles and the [T][K] layout do not; forcing works on any N:M (1:4
+    included)."""
+    monkeypatch.delenv("NM_SPMM_VARIANT", raising=False)
+    L = nm.lib()
+    v = lambda d, T, y=nm.NM_I8: L.nm_spmm_variant(ctypes.byref(d), T, y).decode()
+    split = "split24_smfmac_i8_stationary"
+    for R in (3072, 2304, 768):                          # ViT-B FC1, QKV, proj
+        d = _desc(R=R, K=768, N=N, M=M)
+        assert v(d, 12608) == split
+        assert v(d, 12608, nm.NM_I32) == split
+        assert _ws(d, 12608, nm.NM_I8) == _split_bytes(R, 768)
+        assert L.nm_spmm_ksplit(ctypes.byref(d), 12608, nm.NM_I8, 0) == 1
+    assert v(_desc(R=3072, K=704, N=N, M=M), 12608) == split          # six column blocks, the last partial
+    assert v(_desc(R=768, K=3072, N=N, M=M), 12608) != split   # FC2: K past 768
+    assert v(_desc(R=3072, K=640, N=N, M=M), 12608) != split   # five column blocks
+    assert v(_desc(R=3072, K=768, N=N, M=M), 256) != split     # R K T < 2^31
+    assert v(_desc(R=3072, K=768, N=N, M=M), 16) != split
+    assert v(_desc(R=3072, K=768, N=N, M=M, dt=nm.NM_F16), 12608, nm.NM_F16) != split
+    assert v(_desc(R=65792, K=768, N=N, M=M), 4096) != split   # 257 row tiles
+    tk = L.nm_spmm_variant_tk(ctypes.byref(_desc(R=3072, K=768, N=N, M=M)), 12608, nm.NM_I8, 0).decode()
+    assert split not in tk
+    monkeypatch.setenv("NM_SPMM_VARIANT", split)
+    small = _desc(R=40, K=768, N=1, M=4)
+    assert v(small, 64) == split
+    assert _ws(small, 64, nm.NM_I8) == _split_bytes(40, 768)
+    assert v(_desc(R=40, K=1024, N=N, M=M), 64) != split                # K past 768: not eligible
+
+
 def test_tk_transpose_choice_and_workspace(monkeypatch):
     """Large [T][K] calls without a kernel of their own in that layout run
     through the [K][T] kernels between two transposes, and ask for X', Y'
@@ -334,7 +375,8 @@ def test_tk_transpose_choice_and_workspace(monkeypatch):
     assert tk(_desc(R=768, K=768), 12608, nm.NM_I8) == "smfmac_i8_2of4_tk"      # proj: 1.5 steps per CU
     assert tk(_desc(R=768, K=3072), 12608, nm.NM_I8) == "smfmac_i8_2of4_tk"     # FC2: K past 768
     assert ws(_desc(R=3072, K=768), 12608, nm.NM_I8) == 0
-    assert _ws(d48, 12608, nm.NM_I8) == 0          # the [K][T] query: no transposes
+    # the [K][T] query: no transposes, the two-layer split of the 4:8 weight
+    assert _ws(d48, 12608, nm.NM_I8) == _split_bytes(3072, 768)
     monkeypatch.setenv("NM_SPMM_VARIANT", "generic_dense_expand")
     assert tk(d48, 12608, nm.NM_I8) == "generic_dense_expand"
 

@@ -611,6 +611,108 @@ def test_repack24_small_workspace_runs_the_nm_kernel():
         compare(Y.cpu().numpy(), ref, "i8", "small workspace")
 
 
+# any int8 N:M split into two 2:4 layers in the workspace, then multiplied by
+# the weight-stationary kernel over both layers (K in (640, 768])
+SPLIT = "split24_smfmac_i8_stationary"
+SPLIT_NMS = [(2, 4), (3, 4), (4, 4), (1, 8), (3, 8), (4, 8), (5, 8), (7, 8), (8, 8)]
+
+
+@pytest.mark.parametrize("out", ["i8", "i32"])
+@pytest.mark.parametrize("N,M", SPLIT_NMS)
+@pytest.mark.parametrize("R,K,T", [(300, 768, 144), (520, 704, 400), (17, 648, 16), (1040, 768, 1008)])
+def test_split24_variant(force_variant, out, N, M, R, K, T):
+    """The two-layer path forced on ragged rows (partial row tiles and row
+    blocks), a partial last column block (K 648, 704), partial last token
+    steps, workgroups with no steps, and padded row strides: the result of
+    the N:M product, element by element."""
+    _expand_case(force_variant, SPLIT, "i8", out, N, M, R, K, T, 61)
+
+
+@pytest.mark.parametrize("out", ["i8", "i32"])
+@pytest.mark.parametrize("N,M", [(3, 4), (4, 8), (8, 8)])
+def test_split24_many_steps(force_variant, out, N, M):
+    """Eight row tiles of 256 rows over 256 workgroups: three 64-token steps
+    per workgroup, so both stages alternate and each workgroup's steps
+    follow its first."""
+    _expand_case(force_variant, SPLIT, "i8", out, N, M, 2048, 768, 6144, 62)
+
+
+@pytest.mark.parametrize("N,M", [(3, 4), (4, 4), (1, 8), (4, 8), (6, 8), (8, 8)])
+@pytest.mark.parametrize("R,K", [(17, 648), (40, 768), (33, 704)])
+def test_split24_copy_describes_the_same_matrix(force_variant, N, M, R, K):
+    """The two 2:4 layers in the workspace, each decoded by the oracle as a
+    2:4 packing, add up bit for bit to the dense matrix the N:M packing
+    describes (ties, zeros and -128 included); each layer has two distinct
+    ascending positions per group of four and clean padding; no position
+    holds a nonzero in both layers."""
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    force_variant(SPLIT)
+    T = 16
+    W = nm_inputs.uniform_int8((R, K), 5, "split", N, M, R, lo=-3, hi=3)
+    W[0, :M] = -128
+    W[1, :M] = 0
+    p = nm.pack(torch.from_numpy(W).cuda(), N, M)
+    assert nm.variant(p, T, torch.int32) == SPLIT
+    vb, mb = nm.pack_size(R, K, 2, 4, nm.NM_I8)
+    moff = (vb + 255) // 256 * 256
+    layer = (moff + mb + 255) // 256 * 256
+    need = nm.workspace_size(p, T, torch.int32)
+    assert need == 2 * layer
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
+    X = torch.zeros((K, T), dtype=torch.int8, device="cuda")
+    nm.spmm(p, X, out_dtype=torch.int32, workspace=ws)
+    torch.cuda.synchronize()
+    h = ws.cpu().numpy()
+    cv, ci = oracle.compress(W, N, M, "i8")
+    want = oracle.decompress(cv, ci, R, K, N, M, "i8").astype(np.int32)
+    got = np.zeros((R, K), np.int32)
+    nonzero = np.zeros((R, K), np.int32)
+    for l in range(2):
+        v24, m24 = h[l * layer:l * layer + vb], h[l * layer + moff:l * layer + moff + mb]
+        vals, idx = oracle.read_packed(v24, m24, R, K, 2, 4, "i8")
+        assert np.all(idx[:, :, 0] < idx[:, :, 1]), l
+        assert oracle.check_padding(v24, m24, R, K, 2, 4, "i8") == 0, l
+        d = oracle.decompress(vals, idx, R, K, 2, 4, "i8").astype(np.int32)
+        got += d
+        nonzero += d != 0
+    assert np.array_equal(got, want)
+    assert nonzero.max() <= 1
+
+
+@pytest.mark.parametrize("N,M", [(3, 4), (4, 8)])
+def test_gelu_split24(force_variant, N, M):
+    """GELU fused into the two-layer kernel's epilogue."""
+    _gelu_case(force_variant, SPLIT, "i8", "i8", N, M, 300, 768, 144, 63)
+
+
+def test_split24_small_workspace_runs_the_nm_kernel():
+    """Given less workspace than the two layers need, the call runs the
+    dense-expand kernel instead, with the same (bit-exact) result."""
+    import ctypes
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    R, K, T, N, M = 3072, 768, 1024, 4, 8
+    W, X, b, s = _inputs("i8", "i8", R, K, T, N, M, 64, "split-small-ws")
+    p = nm.pack(torch.from_numpy(W).cuda(), N, M)
+    assert nm.variant(p, T, torch.int8) == SPLIT
+    need = nm.workspace_size(p, T, torch.int8)
+    assert need > 0
+    Xd = torch.from_numpy(X).cuda()
+    bd, sd = torch.from_numpy(b).cuda(), torch.from_numpy(s).cuda()
+    ref = reference(W, X, N, M, "i8", "i8", bias=b, scale=s)
+    small = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    full = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for ws, wsb in ((None, 0), (small, need - 1), (full, need)):
+        Y = torch.full((R, T), 5, dtype=torch.int8, device="cuda")
+        d = p.desc()
+        st = nm.lib().nm_spmm(ctypes.byref(d), Xd.data_ptr(), T, T, Y.data_ptr(), T, nm.NM_I8, bd.data_ptr(),
+                              sd.data_ptr(), None if ws is None else ws.data_ptr(), wsb, None)
+        assert st == nm.NM_OK
+        torch.cuda.synchronize()
+        compare(Y.cpu().numpy(), ref, "i8", f"workspace {wsb}")
+
+
 def _expand_decode_case(force_variant, dt, out, N, M, R, K, T, seed):
     import semi_structured_sparse_nm_amd as nm
     from tests._parity import TORCH_DT, dev
