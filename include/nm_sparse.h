@@ -126,12 +126,14 @@ nm_status nm_pack(const void* W, int64_t ldw, nm_packed* desc, void* stream);
  * (R K T >= 2^31; either operand layout) it instead holds a copy of the weight re-packed
  * into the 2:4 layout (such a pattern is also a 2:4 pattern), which the 2:4
  * sparse-MFMA kernels then multiply: the 2:4 values_bytes rounded up to 256,
- * then the 2:4 meta_bytes.  For another int8 N:M (3:4, 4:4, 3:8 .. 8:8) with
+ * then the 2:4 meta_bytes.  For another int8 N:M (3:4, 3:8 .. 7:8) with
  * K in (640, 768] and a large product ([K][T] layout) it holds the weight
  * split exactly into two 2:4 layers (every aligned group of four columns
  * keeps at most four members: the first two nonzero ones in the first layer,
  * the rest in the second), each laid out as the re-pack copy above and
- * rounded up to 256 bytes, the second after the first.  Given less than that
+ * rounded up to 256 bytes, the second after the first (a dense int8 weight,
+ * N = M, needs no copy: the kernel takes the two layers in registers).
+ * Given less than that
  * (or a workspace not 256-byte aligned), nm_spmm runs the N:M kernel
  * instead, with the same result.
  * (nm_spmm_tk sizes its workspace with nm_spmm_tk_workspace_size.)
@@ -245,7 +247,8 @@ const char* nm_status_str(nm_status s);
  * (static string; "invalid" when the arguments would be rejected).  A 1:4,
  * 1:8 or 2:8 product re-packed to 2:4 in the workspace is named
  * "repack24_" + the 2:4 kernel's name, the two-layer split
- * "split24_smfmac_i8_stationary", a [T][K] call run through the [K][T]
+ * "split24_smfmac_i8_stationary" (a dense int8 weight taken as two layers
+ * in registers: "dense24_smfmac_i8_stationary"), a [T][K] call run through the [K][T]
  * kernels "transpose_" + that kernel's name (assuming the workspace
  * nm_spmm_workspace_size asks for).  For tests and profiling; launches
  * nothing.

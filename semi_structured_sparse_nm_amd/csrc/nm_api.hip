@@ -111,6 +111,7 @@ enum Variant {
                     // blocks, values straight to registers one 512-column segment ahead
   V_SPLIT24_I8WS,   // int8 N:M, K <= 768: the weight split into two 2:4 layers in the
                     // workspace, then a weight-stationary kernel over both
+  V_DENSE24_I8WS,   // int8 N = M, K <= 768: the same kernel, the two layers taken in registers
   V_COUNT
 };
 
@@ -129,6 +130,7 @@ const char* variant_name(Variant v) {
     case V_SMFMAC_I8WSTK: return "smfmac_i8_2of4_stationary_tk";
     case V_STREAM24: return "smfmac_h_2of4_stream_decode";
     case V_SPLIT24_I8WS: return "split24_smfmac_i8_stationary";
+    case V_DENSE24_I8WS: return "dense24_smfmac_i8_stationary";
     default: return "invalid";
   }
 }
@@ -235,6 +237,10 @@ bool eligible(Variant v, const Call& c) {
       c24.g = &g24;
       return eligible(V_SMFMAC_I8P, c24) && g24.nKB == 6 && (c.g->R + 255) / 256 <= device_cus() / 8 * 8;
     }
+    case V_DENSE24_I8WS:
+      // int8 N = M (dense rows of 2048-byte blocks), otherwise as the split
+      return c.wdt == NM_I8 && c.g->N == c.g->M && c.g->values_bytes() < (1ull << 31) &&
+             eligible(V_SPLIT24_I8WS, c);
     default: return false;
   }
 }
@@ -300,11 +306,15 @@ Variant choose_auto(const Call& c, bool ws_ok) {
   if (eligible(V_SMFMAC_I8SM, c)) return V_SMFMAC_I8SM;
   if (eligible(V_SMFMAC_H, c)) return V_SMFMAC_H;
   // int8 N:M with up to four kept members per group of four columns (3:4,
-  // 4:4, 3:8 .. 8:8), K in (640, 768], large enough for the extra launch:
+  // 3:8 .. 7:8), K in (640, 768], large enough for the extra launch:
   // the two-layer split and the weight-stationary kernel over both layers
   // (1:4, 1:8, 2:8 take the single-layer re-pack below instead)
+  // (dense int8, N = M: the same kernel takes the two layers in registers,
+  // no copy)
+  const double work = (double)c.g->R * (double)c.g->K * (double)c.T;
+  if (eligible(V_DENSE24_I8WS, c) && work >= kRepackMinWork) return V_DENSE24_I8WS;
   if (ws_ok && eligible(V_SPLIT24_I8WS, c) && !(c.g->N == 2 && c.g->M == 4) && !nm::repack24_supported(*c.g) &&
-      (double)c.g->R * (double)c.g->K * (double)c.T >= kRepackMinWork)
+      work >= kRepackMinWork)
     return V_SPLIT24_I8WS;
   if (eligible(V_EXPAND, c)) return V_EXPAND;
   return V_GENERIC;
@@ -681,6 +691,7 @@ nm_status run_variant(Variant v, int S, const SpmmArgs& a, void* part, hipStream
     case V_SMFMAC_I8WSTK: e = nm::launch_spmm_smfmac_i8wstk(a, s); break;
     case V_STREAM24: e = launch_stream24(a, s); break;
     case V_SPLIT24_I8WS: e = nm::launch_spmm_smfmac_i8ws2(a, s); break;
+    case V_DENSE24_I8WS: e = nm::launch_spmm_smfmac_i8ws2_dense(a, s); break;
     default: return NM_EINVAL;
   }
   return e == hipSuccess ? NM_OK : NM_EHIP;

@@ -103,6 +103,9 @@ hipError_t launch_spmm_smfmac_i8ws(const SpmmArgs& a, hipStream_t s);   // weigh
 // weight-stationary over a weight split into two 2:4 layers (a.values /
 // a.meta and a.values2 / a.meta2), K <= 768
 hipError_t launch_spmm_smfmac_i8ws2(const SpmmArgs& a, hipStream_t s);
+// the same kernel on a dense int8 weight (N = M, its own packing), the two
+// layers taken in registers (columns 0, 1 and 2, 3 of every group of four)
+hipError_t launch_spmm_smfmac_i8ws2_dense(const SpmmArgs& a, hipStream_t s);
 hipError_t launch_spmm_smfmac_i8wstk(const SpmmArgs& a, hipStream_t s);   // weight-stationary, [T][K] layout
 hipError_t launch_spmm_smfmac_i8small(const SpmmArgs& a, hipStream_t s);   // any T, unaligned rows
 hipError_t launch_spmm_smfmac_h(const SpmmArgs& a, hipStream_t s);

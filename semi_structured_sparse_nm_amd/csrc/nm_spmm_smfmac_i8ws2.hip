@@ -37,6 +37,13 @@
 //   once in the prologue; a barrier per step publishes a stage and frees the
 //   other.  No count depends on the order in which loads complete.
 //
+// Dense weights (N = M: 8:8, 4:4) need no split copy: every group of four
+// holds its four columns, so the first layer is columns 0 and 1 of each
+// group and the second columns 2 and 3, with the same index word for every
+// lane (positions (0, 1) and (2, 3)).  The kernel loads the dense packed rows
+// (32 bytes per lane and block) and sorts the bytes into the two layers with
+// byte permutes in the first step, just before each block's first products.
+//
 // Epilogue (int8 output): f32(acc) * scale[r] (one rounded product; the bias
 // is the first layer's accumulator start), clamp, add 1.5 * 2^23 so the low
 // byte is the round-half-even int8; the wave's two row blocks of one token
@@ -59,7 +66,7 @@ constexpr int BLK = 128 * BN;          // bytes of one column block of a stage (
 [[maybe_unused]] constexpr int STAGE = NKB * BLK;   // 48 KB
 [[maybe_unused]] constexpr int OST = 64 * RB * 16;    // int8 staging bytes per wave: 64 tokens x 32 rows
 
-template <bool OUT_I8, bool ACT>
+template <bool DENSE, bool OUT_I8, bool ACT>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
   // device pass only (device-only types and builtins)
@@ -104,10 +111,11 @@ smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values), 0, (int)g.values_bytes(), 0x00020000);
   const __amdgpu_buffer_rsrc_t rm0 =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.meta), 0, (int)g.meta_bytes(), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv1 =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values2), 0, (int)g.values_bytes(), 0x00020000);
+  // (dense: the N = M packing, 2048 bytes per block; the meta resources unused)
+  const __amdgpu_buffer_rsrc_t rv1 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(DENSE ? a.values : a.values2), 0, (int)g.values_bytes(), 0x00020000);
   const __amdgpu_buffer_rsrc_t rm1 =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.meta2), 0, (int)g.meta_bytes(), 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(DENSE ? a.meta : a.meta2), 0, DENSE ? 0 : (int)g.meta_bytes(), 0x00020000);
   const v4i rbias = make_rsrc(a.bias, a.bias ? (int)(g.R * 4) : 0);
   const v4i rscale = make_rsrc(a.scale, a.scale ? (int)(g.R * 4) : 0);
 
@@ -136,9 +144,36 @@ smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
   int ai[NKB][NL][RB];
   auto load_a = [&](int kb, int l, int rb) __attribute__((always_inline)) {
     const int blk = __builtin_amdgcn_readfirstlane(min(rb0 + rb, nRB - 1) * NKB + kb);
-    av[kb][l][rb] =
-        __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(l ? rv1 : rv0, voff_v, blk * 1024, 0));
-    ai[kb][l][rb] = (int)__builtin_amdgcn_raw_buffer_load_b32(l ? rm1 : rm0, voff_m, blk * 256, 0);
+    if constexpr (DENSE) {
+      // lane (i, g): the 32 dense bytes of columns 32 g .. 32 g + 31 of row
+      // i, the first 16 in the first layer's registers, the rest in the
+      // second's, until dense_sort arranges them
+      av[kb][l][rb] = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(rv0, li * 128 + lg * 32 + 16 * l, blk * 2048, 0));
+      ai[kb][l][rb] = l ? (int)0xEEEEEEEE : 0x44444444;   // positions (2, 3) / (0, 1) in every group
+    } else {
+      av[kb][l][rb] =
+          __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(l ? rv1 : rv0, voff_v, blk * 1024, 0));
+      ai[kb][l][rb] = (int)__builtin_amdgcn_raw_buffer_load_b32(l ? rm1 : rm0, voff_m, blk * 256, 0);
+    }
+  };
+  // dense: dword j of the 32 bytes is group j's four columns; the first
+  // layer takes bytes 0 and 1 of each group, the second bytes 2 and 3
+  auto dense_sort = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const v4i lo = av[kb][0][rb], hi = av[kb][1][rb];
+      const uint32_t d[8] = {(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)lo[2], (uint32_t)lo[3],
+                             (uint32_t)hi[0], (uint32_t)hi[1], (uint32_t)hi[2], (uint32_t)hi[3]};
+      v4i f, sc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[j] = (int)__builtin_amdgcn_perm(d[2 * j + 1], d[2 * j], 0x05040100u);
+        sc[j] = (int)__builtin_amdgcn_perm(d[2 * j + 1], d[2 * j], 0x07060302u);
+      }
+      av[kb][0][rb] = f;
+      av[kb][1][rb] = sc;
+    }
   };
 #pragma unroll
   for (int l = 0; l < NL; ++l)
@@ -186,7 +221,7 @@ smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
   // input.  The wave's loads of the next stage (step nx into stage np, when
   // nx < sb) go between the products of the first six fragments.
   typedef v4i Acc[RB][TN];
-  auto compute = [&](Acc& acc, const uint8_t* sp, int nx, uint8_t* np, bool spread) __attribute__((always_inline)) {
+  auto compute = [&](Acc& acc, const uint8_t* sp, int nx, uint8_t* np, bool spread, bool first) __attribute__((always_inline)) {
     constexpr int NF = NKB * TN;
     constexpr int NB = 3;              // fragments f + 1, f, f - 1
     v8i bf[NB];
@@ -202,6 +237,7 @@ smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
     for (int f = 0; f < NF; ++f) {
       if (f + 1 < NF) bf[(f + 1) % NB] = bfrag(sp, (f + 1) / TN, (f + 1) % TN);
       const int kb = f / TN, tt = f % TN;
+      if (DENSE && first && tt == 0) dense_sort(kb);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
         acc[rb][tt] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(av[kb][0][rb], bf[f % NB],
@@ -310,7 +346,7 @@ smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
           for (int rb = 0; rb < RB; ++rb) load_a(kb, l, rb);
     }
     Acc acc;
-    compute(acc, ST == 1 ? xs1 : xs0, s + 1, ST == 1 ? xs0 : xs1, ST != 2);
+    compute(acc, ST == 1 ? xs1 : xs0, s + 1, ST == 1 ? xs0 : xs1, ST != 2, ST == 2);
     // the next stage (issued this step) and the previous step's stores:
     // nothing else is outstanding
     __builtin_amdgcn_s_waitcnt(waitcnt(0, 15));
@@ -329,10 +365,17 @@ smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
 #endif
 }
 
-template <bool OUT_I8, bool ACT>
+template <bool DENSE, bool OUT_I8, bool ACT>
 hipError_t launch_cfg(const SpmmArgs& a, int mtiles, int nsteps, int G, hipStream_t s) {
-  hipLaunchKernelGGL((smfmac_i8ws2_kernel<OUT_I8, ACT>), dim3(G), dim3(NW * 64), 0, s, a, mtiles, nsteps);
+  hipLaunchKernelGGL((smfmac_i8ws2_kernel<DENSE, OUT_I8, ACT>), dim3(G), dim3(NW * 64), 0, s, a, mtiles, nsteps);
   return hipGetLastError();
+}
+
+template <bool DENSE>
+hipError_t launch_dt(const SpmmArgs& a, int mtiles, int nsteps, int G, hipStream_t s) {
+  if (a.ydt == NM_I8 && a.act) return launch_cfg<DENSE, true, true>(a, mtiles, nsteps, G, s);
+  if (a.ydt == NM_I8) return launch_cfg<DENSE, true, false>(a, mtiles, nsteps, G, s);
+  return launch_cfg<DENSE, false, false>(a, mtiles, nsteps, G, s);
 }
 
 }  // namespace
@@ -347,9 +390,19 @@ hipError_t launch_spmm_smfmac_i8ws2(const SpmmArgs& a, hipStream_t s) {
   const int G = cu_count(dev) / 8 * 8;
   if (a.g.nKB != NKB || a.g.N != 2 || a.g.M != 4 || !a.values2 || !a.meta2 || G < 8 || mtiles > G)
     return hipErrorInvalidValue;
-  if (a.ydt == NM_I8 && a.act) return launch_cfg<true, true>(a, mtiles, nsteps, G, s);
-  if (a.ydt == NM_I8) return launch_cfg<true, false>(a, mtiles, nsteps, G, s);
-  return launch_cfg<false, false>(a, mtiles, nsteps, G, s);
+  return launch_dt<false>(a, mtiles, nsteps, G, s);
+}
+
+// a dense int8 weight (N = M) in its own packing, split in registers
+hipError_t launch_spmm_smfmac_i8ws2_dense(const SpmmArgs& a, hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const int mtiles = (int)((a.g.R + BM - 1) / BM);
+  const int nsteps = (int)((a.T + BN - 1) / BN);
+  const int G = cu_count(dev) / 8 * 8;
+  if (a.wdt != NM_I8 || a.g.N != a.g.M || a.g.nKB != NKB || a.g.vblk != 2048 || G < 8 || mtiles > G)
+    return hipErrorInvalidValue;
+  return launch_dt<true>(a, mtiles, nsteps, G, s);
 }
 
 }  // namespace nm

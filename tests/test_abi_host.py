@@ -315,7 +315,26 @@ def _split_bytes(R, K):
     return 2 * (((vb + 255) // 256 * 256 + mb + 255) // 256 * 256)
 
 
-@pytest.mark.parametrize("N,M", [(3, 4), (4, 4), (3, 8), (4, 8), (8, 8)])
+@pytest.mark.parametrize("N,M", [(4, 4), (8, 8)])
+def test_dense24_choice(monkeypatch, N, M):
+    """Dense int8 weights (N = M), K in (640, 768], large enough: the
+    two-layer kernel with the layers taken in registers, no workspace;
+    otherwise not."""
+    monkeypatch.delenv("NM_SPMM_VARIANT", raising=False)
+    L = nm.lib()
+    v = lambda d, T, y=nm.NM_I8: L.nm_spmm_variant(ctypes.byref(d), T, y).decode()
+    for R in (3072, 2304, 768):
+        d = _desc(R=R, K=768, N=N, M=M)
+        assert v(d, 12608) == v(d, 12608, nm.NM_I32) == "dense24_smfmac_i8_stationary"
+        assert _ws(d, 12608, nm.NM_I8) == 0
+    assert v(_desc(R=768, K=3072, N=N, M=M), 12608) != "dense24_smfmac_i8_stationary"
+    assert v(_desc(R=3072, K=768, N=N, M=M), 256) != "dense24_smfmac_i8_stationary"
+    monkeypatch.setenv("NM_SPMM_VARIANT", "dense24_smfmac_i8_stationary")
+    assert v(_desc(R=40, K=768, N=N, M=M), 64) == "dense24_smfmac_i8_stationary"
+    assert v(_desc(R=40, K=768, N=4, M=8), 64) != "dense24_smfmac_i8_stationary"   # not dense
+
+
+@pytest.mark.parametrize("N,M", [(3, 4), (3, 8), (4, 8), (7, 8)])
 def test_split24_choice_and_workspace(monkeypatch, N, M):
     """int8 N:M with more than two kept members per group of four, K in
     (640, 768], large enough (R K T >= 2^31): split into two 2:4 layers and

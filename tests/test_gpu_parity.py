@@ -637,6 +637,25 @@ def test_split24_many_steps(force_variant, out, N, M):
     _expand_case(force_variant, SPLIT, "i8", out, N, M, 2048, 768, 6144, 62)
 
 
+DENSE = "dense24_smfmac_i8_stationary"
+
+
+@pytest.mark.parametrize("out", ["i8", "i32"])
+@pytest.mark.parametrize("N,M", [(4, 4), (8, 8)])
+@pytest.mark.parametrize("R,K,T", [(300, 768, 144), (520, 704, 400), (17, 648, 16), (1040, 768, 1008),
+                                   (2048, 768, 6144)])
+def test_dense24_variant(force_variant, out, N, M, R, K, T):
+    """Dense int8 weights through the two-layer kernel with the layers taken
+    in registers (no copy): ragged rows, partial column blocks and steps,
+    several steps per workgroup, padded strides; element by element."""
+    _expand_case(force_variant, DENSE, "i8", out, N, M, R, K, T, 65)
+
+
+def test_gelu_dense24(force_variant):
+    """GELU fused into the dense form's epilogue."""
+    _gelu_case(force_variant, DENSE, "i8", "i8", 8, 8, 300, 768, 144, 66)
+
+
 @pytest.mark.parametrize("N,M", [(3, 4), (4, 4), (1, 8), (4, 8), (6, 8), (8, 8)])
 @pytest.mark.parametrize("R,K", [(17, 648), (40, 768), (33, 704)])
 def test_split24_copy_describes_the_same_matrix(force_variant, N, M, R, K):

@@ -1,7 +1,8 @@
 """nm_spmm_noalloc (the entry point that allocates nothing) against nm_spmm_act
 with a caller-given workspace, through the C ABI, on the calls that use a
 workspace: a K split across workgroups (Swin-T stage-4 MLP out-projection,
-fp16 2:4) and a 2:4 re-pack of an int8 1:4 weight (ViT-B FC1).  Two calls in
+fp16 2:4), a 2:4 re-pack of an int8 1:4 weight (ViT-B FC1) and the two-layer
+split of an int8 4:8 weight (ViT-B FC1).  Two calls in
 a row, the second smaller; the results must be identical bit for bit (same
 kernels, same split) and match the oracle.  A split whose partial sums exceed
 the scratch is rejected before any launch."""
@@ -40,6 +41,7 @@ CASES = [
     # (what, R, K, T first, T second, N, M, dt, out, variant prefix)
     ("ksplit_swin_s4_fc2", 768, 3072, 1568, 784, 2, 4, "f16", "f16", "smfmac_h_2of4_persistent"),
     ("repack_vitb_fc1_1of4", 3072, 768, 12608, 6304, 1, 4, "i8", "i8", "repack24_"),
+    ("split_vitb_fc1_4of8", 3072, 768, 12608, 6304, 4, 8, "i8", "i8", "split24_"),
 ]
 
 
