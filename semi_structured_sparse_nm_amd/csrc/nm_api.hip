@@ -112,6 +112,8 @@ enum Variant {
   V_SPLIT24_I8WS,   // int8 N:M, K <= 768: the weight split into two 2:4 layers in the
                     // workspace, then a weight-stationary kernel over both
   V_DENSE24_I8WS,   // int8 N = M, K <= 768: the same kernel, the two layers taken in registers
+  V_SPLIT24_I8WSTK, // the two-layer split in the [T][K] layout
+  V_DENSE24_I8WSTK, // the dense form in the [T][K] layout
   V_COUNT
 };
 
@@ -131,6 +133,8 @@ const char* variant_name(Variant v) {
     case V_STREAM24: return "smfmac_h_2of4_stream_decode";
     case V_SPLIT24_I8WS: return "split24_smfmac_i8_stationary";
     case V_DENSE24_I8WS: return "dense24_smfmac_i8_stationary";
+    case V_SPLIT24_I8WSTK: return "split24_smfmac_i8_stationary_tk";
+    case V_DENSE24_I8WSTK: return "dense24_smfmac_i8_stationary_tk";
     default: return "invalid";
   }
 }
@@ -152,7 +156,10 @@ Geometry geometry24(const Geometry& g) { return Geometry::make(g.R, g.K, 2, 4, g
 
 bool eligible(Variant v, const Call& c) {
   // the [T][K] layout has kernels of its own (and the generic one)
-  if ((c.layout == NM_LAYOUT_TK) != (v == V_SMFMAC_I8TK || v == V_SMFMAC_I8WSTK) && v != V_GENERIC) return false;
+  if ((c.layout == NM_LAYOUT_TK) !=
+          (v == V_SMFMAC_I8TK || v == V_SMFMAC_I8WSTK || v == V_SPLIT24_I8WSTK || v == V_DENSE24_I8WSTK) &&
+      v != V_GENERIC)
+    return false;
   switch (v) {
     case V_GENERIC: return true;
     case V_SMFMAC_I8P:
@@ -241,6 +248,18 @@ bool eligible(Variant v, const Call& c) {
       // int8 N = M (dense rows of 2048-byte blocks), otherwise as the split
       return c.wdt == NM_I8 && c.g->N == c.g->M && c.g->values_bytes() < (1ull << 31) &&
              eligible(V_SPLIT24_I8WS, c);
+    case V_SPLIT24_I8WSTK: {
+      // as the split, with the 2:4 layers' product as the [T][K] int8 2:4
+      // kernel takes it (R a multiple of 16)
+      if (c.wdt != NM_I8 || !nm::split24_supported(*c.g)) return false;
+      const Geometry g24 = geometry24(*c.g);
+      Call c24 = c;
+      c24.g = &g24;
+      return eligible(V_SMFMAC_I8TK, c24) && g24.nKB == 6 && (c.g->R + 255) / 256 <= device_cus() / 8 * 8;
+    }
+    case V_DENSE24_I8WSTK:
+      return c.wdt == NM_I8 && c.g->N == c.g->M && c.g->values_bytes() < (1ull << 31) &&
+             eligible(V_SPLIT24_I8WSTK, c);
     default: return false;
   }
 }
@@ -253,7 +272,7 @@ Variant choose(const Call& c, bool ws_ok = true) {
   if (f.name[0]) {
     for (int v = V_GENERIC; v < V_COUNT; ++v)
       if (strcmp(f.name, variant_name((Variant)v)) == 0 && eligible((Variant)v, c) &&
-          (ws_ok || v != V_SPLIT24_I8WS))
+          (ws_ok || (v != V_SPLIT24_I8WS && v != V_SPLIT24_I8WSTK)))
         return (Variant)v;
   }
   return choose_auto(c, ws_ok);
@@ -271,6 +290,16 @@ Variant choose_auto(const Call& c, bool ws_ok) {
     if (2 * steps >= 7 * (int64_t)device_cus()) return V_SMFMAC_I8WSTK;
   }
   if (eligible(V_SMFMAC_I8TK, c)) return V_SMFMAC_I8TK;
+  // [T][K] layout, other int8 N:M with K in (640, 768]: the two-layer kernel
+  // (dense weights: the layers in registers; else split in the workspace,
+  // except 1:4, 1:8 and 2:8, which the 2:4 re-pack takes)
+  {
+    const double work = (double)c.g->R * (double)c.g->K * (double)c.T;
+    if (eligible(V_DENSE24_I8WSTK, c) && work >= kRepackMinWork) return V_DENSE24_I8WSTK;
+    if (ws_ok && eligible(V_SPLIT24_I8WSTK, c) && !(c.g->N == 2 && c.g->M == 4) &&
+        !nm::repack24_supported(*c.g) && work >= kRepackMinWork)
+      return V_SPLIT24_I8WSTK;
+  }
   // decode shapes (few tokens), fp16 / bf16 2:4: with more 16-row blocks
   // than compute units, one workgroup per CU walking row blocks with its
   // loads a segment ahead; otherwise K split inside a workgroup per row
@@ -462,7 +491,7 @@ Plan plan_for(const Call& c) {
   const double work = (double)c.g->R * (double)c.g->K * (double)c.T;
 
   // two-layer split (its own variant)
-  if (p.v == V_SPLIT24_I8WS) {
+  if (p.v == V_SPLIT24_I8WS || p.v == V_SPLIT24_I8WSTK) {
     p.split = true;
     p.g24 = geometry24(*c.g);
     return p;
@@ -505,7 +534,7 @@ Plan plan_for(const Call& c) {
     } else {
       inner = choose_auto(ckt, false);
     }
-    if (inner != V_INVALID && inner != V_GENERIC && inner != V_SPLIT24_I8WS) {
+    if (inner != V_INVALID && inner != V_GENERIC && inner != V_SPLIT24_I8WS && inner != V_SPLIT24_I8WSTK) {
       p.v = inner;
       p.transpose = true;
       p.Tp = Tp;
@@ -690,8 +719,10 @@ nm_status run_variant(Variant v, int S, const SpmmArgs& a, void* part, hipStream
     case V_SMFMAC_I8TK: e = nm::launch_spmm_smfmac_i8tk(a, s); break;
     case V_SMFMAC_I8WSTK: e = nm::launch_spmm_smfmac_i8wstk(a, s); break;
     case V_STREAM24: e = launch_stream24(a, s); break;
-    case V_SPLIT24_I8WS: e = nm::launch_spmm_smfmac_i8ws2(a, s); break;
-    case V_DENSE24_I8WS: e = nm::launch_spmm_smfmac_i8ws2_dense(a, s); break;
+    case V_SPLIT24_I8WS:
+    case V_SPLIT24_I8WSTK: e = nm::launch_spmm_smfmac_i8ws2(a, s); break;
+    case V_DENSE24_I8WS:
+    case V_DENSE24_I8WSTK: e = nm::launch_spmm_smfmac_i8ws2_dense(a, s); break;
     default: return NM_EINVAL;
   }
   return e == hipSuccess ? NM_OK : NM_EHIP;

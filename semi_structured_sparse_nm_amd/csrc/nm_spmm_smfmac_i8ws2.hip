@@ -44,6 +44,13 @@
 // (32 bytes per lane and block) and sorts the bytes into the two layers with
 // byte permutes in the first step, just before each block's first products.
 //
+// The PyTorch-linear layout (TK: X [T][K] with K contiguous, Y [T][R]) takes
+// the stages, B-fragment reads and epilogue of the [T][K] weight-stationary
+// kernel (nm_spmm_smfmac_i8wstk.hip): per block 64 tokens of 128 k bytes,
+// token-major (chunk c of token t at c ^ (t & 7)), B fragments as two plain
+// 16-byte reads, and token rows of the wave's 32 output rows staged so each
+// lane stores 16 consecutive rows of one token (R a multiple of 16).
+//
 // Epilogue (int8 output): f32(acc) * scale[r] (one rounded product; the bias
 // is the first layer's accumulator start), clamp, add 1.5 * 2^23 so the low
 // byte is the round-half-even int8; the wave's two row blocks of one token
@@ -66,7 +73,7 @@ constexpr int BLK = 128 * BN;          // bytes of one column block of a stage (
 [[maybe_unused]] constexpr int STAGE = NKB * BLK;   // 48 KB
 [[maybe_unused]] constexpr int OST = 64 * RB * 16;    // int8 staging bytes per wave: 64 tokens x 32 rows
 
-template <bool DENSE, bool OUT_I8, bool ACT>
+template <bool TK, bool DENSE, bool OUT_I8, bool ACT>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
   // device pass only (device-only types and builtins)
@@ -105,7 +112,7 @@ smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
   const int rb0 = __builtin_amdgcn_readfirstlane(r0 / 16 + RB * wave);
 
   // ---- buffer resources (hardware range checks replace bounds tests)
-  const v4i rx = make_rsrc(a.X, (int)(g.K * a.ldx));
+  const v4i rx = make_rsrc(a.X, (int)((TK ? a.T : g.K) * a.ldx));
   const v4i rz = zero_rsrc();
   const __amdgpu_buffer_rsrc_t rv0 =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.values), 0, (int)g.values_bytes(), 0x00020000);
@@ -124,14 +131,22 @@ smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
   // rows 16 w .. 16 w + 15: lane l -> row 16 w + l / 4, position l % 4, the
   // source chunk whose swizzled position that is.  Rows past K lie past the
   // resource's range and read as zero (every wait is a full drain).
+  // (TK: wave w's load of a block fills tokens 8 w .. 8 w + 7: lane l ->
+  // token 8 w + l / 8, position l % 8, source chunk (l % 8) ^ (l / 8);
+  // tokens past T read as zero)
   int xv;
-  {
+  if constexpr (TK) {
+    const int tok = 8 * wave + (lane >> 3);
+    const int c = (lane & 7) ^ (lane >> 3);
+    xv = tok * ldx + 16 * c;
+  } else {
     const int row = 16 * wave + (lane >> 2);
     const int c = (lane & 3) ^ (((row >> 2) & 1) | ((row >> 3) & 2));
     xv = row * ldx + 16 * c;
   }
   auto issue_xb = [&](int step, uint8_t* sp, int kb) __attribute__((always_inline)) {
-    lds_dma16(rx, lds_addr(sp + kb * BLK + wave * 1024), xv, kb * 128 * ldx + step * BN);
+    lds_dma16(rx, lds_addr(sp + kb * BLK + wave * 1024), xv,
+              TK ? step * BN * ldx + kb * 128 : kb * 128 * ldx + step * BN);
   };
 
   // ---- the wave's packed rows of both layers (lane (i, g): 16 bytes at row
@@ -203,15 +218,26 @@ smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
   // ---- B fragments: lane (i, g) of token tile tt reads rows kq + 16 g +
   // i / 2 (kq = 0, 8, 64, 72) of a block, tokens 16 tt + 8 (i & 1) .. + 7,
   // i.e. chunk tt at position tt ^ f(row) = tt ^ (i / 8) ^ 2 (g & 1)
+  // (TK: chunks lg and 4 + lg of token 16 tt + li, positions chunk ^ (li &
+  // 7); 16 tokens are 2048 bytes)
   const int rbase = 64 * (16 * lg + (li >> 1)) + 8 * (li & 1);
   const int fsw = ((li >> 3) & 1) | ((lg & 1) << 1);
+  const int xb0 = 128 * li + 16 * (lg ^ (li & 7));
+  const int xb1 = 128 * li + 16 * ((4 + lg) ^ (li & 7));
   auto bfrag = [&](const uint8_t* sp, int kb, int tt) __attribute__((always_inline)) -> v8i {
-    const uint8_t* p = sp + kb * BLK + rbase + 16 * (tt ^ fsw);
-    const v2i p0 = lds_tr8(p);
-    const v2i p1 = lds_tr8(p + 8 * 64);
-    const v2i p2 = lds_tr8(p + 64 * 64);
-    const v2i p3 = lds_tr8(p + 72 * 64);
-    return v8i{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    if constexpr (TK) {
+      const uint8_t* p = sp + kb * BLK + 2048 * tt;
+      const v4i c0 = *reinterpret_cast<const v4i*>(p + xb0);
+      const v4i c1 = *reinterpret_cast<const v4i*>(p + xb1);
+      return v8i{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    } else {
+      const uint8_t* p = sp + kb * BLK + rbase + 16 * (tt ^ fsw);
+      const v2i p0 = lds_tr8(p);
+      const v2i p1 = lds_tr8(p + 8 * 64);
+      const v2i p2 = lds_tr8(p + 64 * 64);
+      const v2i p3 = lds_tr8(p + 72 * 64);
+      return v8i{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    }
   };
 
   // acc = bias + A0 x B + A1 x B over the stage: the 24 (block, token tile)
@@ -254,6 +280,61 @@ smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
   // 16-byte chunk c of token t sits at c ^ f(t), f(t) = (bit 3 ^ bit 4) of
   // t, so that the 32 lanes served together touch distinct banks.
   uint8_t* const oh = ostage + (OUT_I8 ? wave * OST : 0);
+  // TK: token rows of the wave's 32 rows (32 bytes each, 16 tokens per
+  // token tile): the dword of rows 16 rb + 4 g .. + 3 of token t at byte
+  // 16 (rb ^ f(t)) + 4 g, f(t) = bit 3 of t; each lane then reads one
+  // 16-byte half (16 consecutive rows of one token) and stores it.
+  auto epilogue_i8_tk = [&](Acc& acc, int t0) __attribute__((always_inline)) {
+    const float osc = a.out_scale;
+    const int sw = (li >> 3) & 1;
+#pragma unroll
+    for (int u = 0; u < TN; ++u) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const v4f sv = scale_vec(rb);
+        float f[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          f[v] = __builtin_amdgcn_fmed3f(i8_pre<ACT>(acc[rb][u][v], sv[v], osc), -128.0f, 127.0f);
+        *reinterpret_cast<uint32_t*>(oh + 512 * u + 32 * li + 16 * (rb ^ sw) + 4 * lg) =
+            pack_rne_i8x4(f[0], f[1], f[2], f[3]);
+      }
+    }
+    // the wave reads back only what it wrote, after its staging writes have
+    // completed; the area's next writes (a step later) come after these
+    // reads have returned (the stores consume them)
+    __builtin_amdgcn_s_waitcnt(waitcnt(63, 0));
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)(a.T * a.ldy), 0x00020000);
+    const int oob = (int)(a.T * a.ldy);
+    const int tl = (lane >> 1) & 15, h = lane & 1;   // token of the tile, half (rows 16 h ..)
+    const int row = r0 + 16 * RB * wave + 16 * h;
+#pragma unroll
+    for (int q = 0; q < TN / 2; ++q) {
+      const int u = 2 * q + (lane >> 5);
+      const v4i piece = *reinterpret_cast<const v4i*>(oh + 512 * u + 32 * tl + 16 * (h ^ ((tl >> 3) & 1)));
+      const int tok = t0 + 16 * u + tl;
+      const int off = (tok < a.T && row < (int)g.R) ? tok * (int)a.ldy + row : oob;
+      __builtin_amdgcn_raw_buffer_store_b128(piece, ry, off, 0, kStreamStore);
+    }
+  };
+  // TK, int32 output: a lane's four rows of one token are 16 contiguous bytes
+  auto store_i32_tk = [&](Acc& acc, int t0) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)(a.T * a.ldy * 4), 0x00020000);
+    const int rw = r0 + 16 * RB * wave + 4 * lg;
+    const int oob = (int)(a.T * a.ldy * 4);
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+      for (int tt = 0; tt < TN; ++tt) {
+        const int t = t0 + 16 * tt + li;
+        const int row = rw + 16 * rr;
+        __builtin_amdgcn_raw_buffer_store_b128(acc[rr][tt], ry,
+                                               (t < a.T && row < (int)g.R) ? 4 * (t * (int)a.ldy + row) : oob, 0,
+                                               kStreamStore);
+      }
+  };
   auto epilogue_i8 = [&](Acc& acc, int t0) __attribute__((always_inline)) {
     const float osc = a.out_scale;
     const float magic = 12582912.0f;          // 1.5 * 2^23
@@ -319,7 +400,11 @@ smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
       }
   };
   auto finish = [&](Acc& acc, int t0) __attribute__((always_inline)) {
-    if constexpr (OUT_I8)
+    if constexpr (TK && OUT_I8)
+      epilogue_i8_tk(acc, t0);
+    else if constexpr (TK)
+      store_i32_tk(acc, t0);
+    else if constexpr (OUT_I8)
       epilogue_i8(acc, t0);
     else
       store_i32(acc, t0);
@@ -365,17 +450,25 @@ smfmac_i8ws2_kernel(SpmmArgs a, int mtiles, int nsteps) {
 #endif
 }
 
-template <bool DENSE, bool OUT_I8, bool ACT>
+template <bool TK, bool DENSE, bool OUT_I8, bool ACT>
 hipError_t launch_cfg(const SpmmArgs& a, int mtiles, int nsteps, int G, hipStream_t s) {
-  hipLaunchKernelGGL((smfmac_i8ws2_kernel<DENSE, OUT_I8, ACT>), dim3(G), dim3(NW * 64), 0, s, a, mtiles, nsteps);
+  hipLaunchKernelGGL((smfmac_i8ws2_kernel<TK, DENSE, OUT_I8, ACT>), dim3(G), dim3(NW * 64), 0, s, a, mtiles, nsteps);
   return hipGetLastError();
+}
+
+template <bool TK, bool DENSE>
+hipError_t launch_out(const SpmmArgs& a, int mtiles, int nsteps, int G, hipStream_t s) {
+  if (a.ydt == NM_I8 && a.act) return launch_cfg<TK, DENSE, true, true>(a, mtiles, nsteps, G, s);
+  if (a.ydt == NM_I8) return launch_cfg<TK, DENSE, true, false>(a, mtiles, nsteps, G, s);
+  return launch_cfg<TK, DENSE, false, false>(a, mtiles, nsteps, G, s);
 }
 
 template <bool DENSE>
 hipError_t launch_dt(const SpmmArgs& a, int mtiles, int nsteps, int G, hipStream_t s) {
-  if (a.ydt == NM_I8 && a.act) return launch_cfg<DENSE, true, true>(a, mtiles, nsteps, G, s);
-  if (a.ydt == NM_I8) return launch_cfg<DENSE, true, false>(a, mtiles, nsteps, G, s);
-  return launch_cfg<DENSE, false, false>(a, mtiles, nsteps, G, s);
+  // the [T][K] epilogue stores 16-row pieces: R a multiple of 16
+  if (a.layout == NM_LAYOUT_TK)
+    return a.g.R % 16 ? hipErrorInvalidValue : launch_out<true, DENSE>(a, mtiles, nsteps, G, s);
+  return launch_out<false, DENSE>(a, mtiles, nsteps, G, s);
 }
 
 }  // namespace

@@ -329,6 +329,8 @@ def test_dense24_choice(monkeypatch, N, M):
         assert _ws(d, 12608, nm.NM_I8) == 0
     assert v(_desc(R=768, K=3072, N=N, M=M), 12608) != "dense24_smfmac_i8_stationary"
     assert v(_desc(R=3072, K=768, N=N, M=M), 256) != "dense24_smfmac_i8_stationary"
+    tk = L.nm_spmm_variant_tk(ctypes.byref(_desc(R=3072, K=768, N=N, M=M)), 12608, nm.NM_I8, 0).decode()
+    assert tk == "dense24_smfmac_i8_stationary_tk"
     monkeypatch.setenv("NM_SPMM_VARIANT", "dense24_smfmac_i8_stationary")
     assert v(_desc(R=40, K=768, N=N, M=M), 64) == "dense24_smfmac_i8_stationary"
     assert v(_desc(R=40, K=768, N=4, M=8), 64) != "dense24_smfmac_i8_stationary"   # not dense
@@ -360,7 +362,7 @@ def test_split24_choice_and_workspace(monkeypatch, N, M):
     assert v(_desc(R=3072, K=768, N=N, M=M, dt=nm.NM_F16), 12608, nm.NM_F16) != split
     assert v(_desc(R=65792, K=768, N=N, M=M), 4096) != split   # 257 row tiles
     tk = L.nm_spmm_variant_tk(ctypes.byref(_desc(R=3072, K=768, N=N, M=M)), 12608, nm.NM_I8, 0).decode()
-    assert split not in tk
+    assert tk == split + "_tk"
     monkeypatch.setenv("NM_SPMM_VARIANT", split)
     small = _desc(R=40, K=768, N=1, M=4)
     assert v(small, 64) == split
@@ -384,8 +386,12 @@ def test_tk_transpose_choice_and_workspace(monkeypatch):
 
     r256 = lambda n: (n + 255) // 256 * 256
     d48 = _desc(R=3072, K=768, N=4, M=8)
-    assert tk(d48, 12608, nm.NM_I8) == "transpose_expand_mfma_persistent"
-    assert ws(d48, 12608, nm.NM_I8) == r256(768 * 12608) + r256(3072 * 12608)
+    # int8 4:8 at K 768: the two-layer kernel of the layout (its split copy)
+    assert tk(d48, 12608, nm.NM_I8) == "split24_smfmac_i8_stationary_tk"
+    assert ws(d48, 12608, nm.NM_I8) == _split_bytes(3072, 768)
+    d48k = _desc(R=768, K=3072, N=4, M=8)                   # K past 768: through the [K][T] kernel
+    assert tk(d48k, 12608, nm.NM_I8) == "transpose_expand_mfma_persistent"
+    assert ws(d48k, 12608, nm.NM_I8) == r256(3072 * 12608) + r256(768 * 12608)
     h = _desc(R=3072, K=768, dt=nm.NM_F16)
     assert tk(h, 3137, nm.NM_F16) == "transpose_smfmac_h_2of4_persistent"
     assert ws(h, 3137, nm.NM_F16) == r256(768 * 3152 * 2) + r256(3072 * 3152 * 2)

@@ -276,7 +276,8 @@ def test_tk_full_size_sampled_rows(name):
     L = {l.name: l for ls in nm_inputs.all_configs().values() for l in ls}[name]
     W, X, b, s = layer_case(L)
     p = nm.pack(dev(W, L.dt), L.N, L.M)
-    assert nm.variant_tk(p, L.T, TORCH_DT[L.out]).startswith(("repack24_", "transpose_", "smfmac_i8_2of4_tk"))
+    assert nm.variant_tk(p, L.T, TORCH_DT[L.out]).startswith(("repack24_", "transpose_", "smfmac_i8_2of4_tk",
+                                                              "split24_", "dense24_"))
     Xt = dev(np.ascontiguousarray(X.T), L.dt)
     Yfull = torch.full((L.T, L.R + 16), 5, dtype=TORCH_DT[L.out], device="cuda")
     kw = {}
@@ -1025,6 +1026,35 @@ def _tk_case(dt, out, N, M, R, K, T, seed, act="none", xpad=24, variant=None):
         compare(Yt, reference(W, X, N, M, dt, out, bias=b, scale=sd, act=act), out, f"tk {N}:{M}")
     want = 5 if out != "bf16" else oracle.round_to(np.array([5.0]), "bf16")[0]
     assert np.all(Y[:, R:] == want), "writes beyond R"
+
+
+@pytest.mark.parametrize("out", ["i8", "i32"])
+@pytest.mark.parametrize("N,M", [(3, 4), (4, 4), (1, 8), (4, 8), (7, 8), (8, 8)])
+@pytest.mark.parametrize("R,K,T", [(304, 768, 144), (528, 704, 400), (16, 656, 16), (1040, 768, 1008)])
+def test_tk_two_layer(force_variant, out, N, M, R, K, T):
+    """The two-layer kernel in the [T][K] layout (split copy, or the dense
+    form's layers in registers), forced on partial row tiles, partial column
+    blocks and steps, padded strides: element by element, nothing written
+    past R."""
+    variant = ("dense24" if N == M else "split24") + "_smfmac_i8_stationary_tk"
+    force_variant(variant)
+    _tk_case("i8", out, N, M, R, K, T, 67, xpad=16, variant=variant)
+
+
+@pytest.mark.parametrize("out", ["i8", "i32"])
+@pytest.mark.parametrize("N,M", [(4, 8), (8, 8)])
+def test_tk_two_layer_many_steps(force_variant, out, N, M):
+    """Three 64-token steps per workgroup in the [T][K] layout."""
+    variant = ("dense24" if N == M else "split24") + "_smfmac_i8_stationary_tk"
+    force_variant(variant)
+    _tk_case("i8", out, N, M, 2048, 768, 6144, 68, xpad=16, variant=variant)
+
+
+@pytest.mark.parametrize("N,M", [(4, 8), (8, 8)])
+def test_tk_two_layer_gelu(force_variant, N, M):
+    variant = ("dense24" if N == M else "split24") + "_smfmac_i8_stationary_tk"
+    force_variant(variant)
+    _tk_case("i8", "i8", N, M, 528, 768, 400, 69, act="gelu", xpad=16, variant=variant)
 
 
 @pytest.mark.parametrize("dt,out", PAIRS)
