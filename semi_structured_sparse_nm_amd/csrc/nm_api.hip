@@ -238,7 +238,7 @@ bool eligible(Variant v, const Call& c) {
       // int8, any N:M; the 2:4 layers' product as the persistent kernels
       // take it, K in (640, 768] (six column blocks held in registers), at
       // most one 256-row tile per workgroup (one per CU)
-      if (c.wdt != NM_I8 || !nm::split24_supported(*c.g)) return false;
+      if (c.wdt != NM_I8 || !nm::split24_supported(*c.g) || c.g->values_bytes() >= (1ull << 31)) return false;
       const Geometry g24 = geometry24(*c.g);
       Call c24 = c;
       c24.g = &g24;
@@ -251,7 +251,7 @@ bool eligible(Variant v, const Call& c) {
     case V_SPLIT24_I8WSTK: {
       // as the split, with the 2:4 layers' product as the [T][K] int8 2:4
       // kernel takes it (R a multiple of 16)
-      if (c.wdt != NM_I8 || !nm::split24_supported(*c.g)) return false;
+      if (c.wdt != NM_I8 || !nm::split24_supported(*c.g) || c.g->values_bytes() >= (1ull << 31)) return false;
       const Geometry g24 = geometry24(*c.g);
       Call c24 = c;
       c24.g = &g24;

@@ -177,6 +177,18 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
+// Read the launch arguments a tile kernel's prologue needs in one batch.
+// Left to itself the compiler loads each argument from the kernel-argument
+// segment where it is first used, which puts several dependent scalar
+// memory round trips between the workgroup's start and its first operand
+// loads; an empty asm that takes them as scalar operands makes it issue
+// those loads together, before any of them is waited for.
+__device__ __forceinline__ void load_args_early(const SpmmArgs& a) {
+  asm volatile("" ::"s"(a.X), "s"(a.Y), "s"(a.values), "s"(a.meta), "s"(a.bias), "s"(a.scale), "s"(a.ldx),
+               "s"(a.ldy), "s"(a.T), "s"(a.g.R), "s"(a.g.K), "s"(a.g.nRB), "s"(a.g.nKB), "s"(a.g.vblk),
+               "s"(a.g.mblk), "s"(a.out_scale));
+}
+
 // compile-time integer as a type (unrolled stage / part indices)
 template <int N> struct ic { static constexpr int value = N; };
 

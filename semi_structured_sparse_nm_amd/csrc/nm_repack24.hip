@@ -152,44 +152,60 @@ __global__ void __launch_bounds__(256) repack24_kernel(Geometry gs, const uint8_
 // source's kept values and position bits of those 8 columns (a few dwords,
 // all issued before any is used) and writes, per layer, the 4 value bytes
 // (one dword) and the 8 position bits (one byte) of the 2:4 layout.
+// Launch arguments of the split, 32-bit sizes (the buffers are below 2^31
+// bytes), read by every thread in one batch at its start.
+struct SplitArgs {
+  const uint8_t* sv;   // source values / positions (the N:M packing)
+  const uint8_t* sm;
+  uint8_t* dv0;        // the two 2:4 layers
+  uint8_t* dm0;
+  uint8_t* dv1;
+  uint8_t* dm1;
+  int nKB;             // column blocks
+  int total;           // threads: rows (padding included) x nKB x 16
+  int C, vblk, MR, mblk;   // source: kept slots per block row, bytes per block, position bytes per row / block
+  int vbytes, mbytes;      // source buffer sizes
+};
+
 template <int M, int N>
-__global__ void __launch_bounds__(256) split24_kernel(Geometry gs, const uint8_t* __restrict__ sv,
-                                                      const uint8_t* __restrict__ sm, Geometry gd,
-                                                      uint8_t* __restrict__ dv0, uint8_t* __restrict__ dm0,
-                                                      uint8_t* __restrict__ dv1, uint8_t* __restrict__ dm1) {
+__global__ void __launch_bounds__(256) split24_kernel(SplitArgs a) {
   constexpr int SG = 8 / M;             // source groups per thread
   constexpr int NS = SG * N;            // source slots per thread (at most 8)
   constexpr int W = N == M ? 0 : (M == 4 ? 2 : 3);   // position bits (none when N = M)
-  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = gs.nRB * 16 * gs.nKB * 16;
-  if (tid >= total) return;
-  const int t = (int)(tid & 15);         // 8-column group of the block row
-  const int64_t rk = tid >> 4;
-  const int64_t kb = rk % gs.nKB;
-  const int64_t r = rk / gs.nKB;         // row, padding rows included
-  const int64_t blk = (r >> 4) * gs.nKB + kb;
-  const int rr = (int)(r & 15);
+  asm volatile("" ::"s"(a.sv), "s"(a.sm), "s"(a.dv0), "s"(a.dm0), "s"(a.dv1), "s"(a.dm1), "s"(a.nKB),
+               "s"(a.total), "s"(a.C), "s"(a.vblk), "s"(a.MR), "s"(a.mblk), "s"(a.vbytes), "s"(a.mbytes));
+  const int tid = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (tid >= a.total) return;
+  const int t = tid & 15;                // 8-column group of the block row
+  const int rk = tid >> 4;
+  const int r = rk / a.nKB;              // row, padding rows included
+  const int kb = rk - r * a.nKB;
+  const int blk = (r >> 4) * a.nKB + kb;
+  const int rr = r & 15;
   const int c0 = t * NS;                 // first source slot
 
-  // every load up front: the dwords holding the NS value bytes (reads past
-  // the row stay inside the values buffer or are skipped) and the two
-  // dwords of the row's position bitstream holding the NS W bits
-  const int64_t vb = blk * gs.vblk + (int64_t)rr * gs.C + c0;
-  const int64_t va = vb & ~(int64_t)3;
-  const int64_t vend = (int64_t)gs.values_bytes();
-  const uint32_t* vw = reinterpret_cast<const uint32_t*>(sv + va);
-  uint32_t w0 = vw[0];
-  uint32_t w1 = va + 4 < vend ? vw[1] : 0u;
-  uint32_t w2 = va + 8 < vend ? vw[2] : 0u;
+  // every load up front, through range-checked buffer loads (past the end:
+  // zero): the three dwords holding the NS value bytes and the two dwords
+  // of the row's position bitstream holding the NS W bits (a dword past the
+  // row's end belongs to the next row or reads zero; its bits are never used)
+  const __amdgpu_buffer_rsrc_t rsv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.sv), 0, a.vbytes, 0x00020000);
+  const int vb = blk * a.vblk + rr * a.C + c0;
+  const int va = vb & ~3;
+  const uint32_t w0 = __builtin_amdgcn_raw_buffer_load_b32(rsv, va, 0, 0);
+  const uint32_t w1 = __builtin_amdgcn_raw_buffer_load_b32(rsv, va + 4, 0, 0);
+  const uint32_t w2 = __builtin_amdgcn_raw_buffer_load_b32(rsv, va + 8, 0, 0);
   uint64_t pbits = 0;
   if constexpr (W != 0) {
-    const uint32_t* mrow = reinterpret_cast<const uint32_t*>(sm + blk * gs.mblk + (int64_t)rr * gs.MR);
-    const int b0 = c0 * W, wi = b0 >> 5, nd = gs.MR / 4;
-    const uint32_t m0 = mrow[wi];
-    const uint32_t m1 = wi + 1 < nd ? mrow[wi + 1] : 0u;
+    const __amdgpu_buffer_rsrc_t rsm =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.sm), 0, a.mbytes, 0x00020000);
+    const int b0 = c0 * W;
+    const int mo = blk * a.mblk + rr * a.MR + 4 * (b0 >> 5);
+    const uint32_t m0 = __builtin_amdgcn_raw_buffer_load_b32(rsm, mo, 0, 0);
+    const uint32_t m1 = __builtin_amdgcn_raw_buffer_load_b32(rsm, mo + 4, 0, 0);
     pbits = ((uint64_t)m0 | (uint64_t)m1 << 32) >> (b0 & 31);
   }
-  const int sh = (int)(vb & 3);
+  const int sh = vb & 3;
   const uint64_t lo = ((uint64_t)w0 | (uint64_t)w1 << 32) >> (8 * sh);
   const uint64_t vbits = sh ? lo | ((uint64_t)w2 << (64 - 8 * sh)) : lo;
   auto value = [&](int sl) { return (uint32_t)(vbits >> (8 * sl)) & 0xFFu; };
@@ -252,12 +268,13 @@ __global__ void __launch_bounds__(256) split24_kernel(Geometry gs, const uint8_t
     }
   }
 
-  const int64_t ov = blk * gd.vblk + (int64_t)rr * gd.C + 4 * t;
-  const int64_t om = blk * gd.mblk + (int64_t)rr * gd.MR + t;
-  *reinterpret_cast<uint32_t*>(dv0 + ov) = dval[0];
-  *reinterpret_cast<uint32_t*>(dv1 + ov) = dval[1];
-  dm0[om] = (uint8_t)dpos[0];
-  dm1[om] = (uint8_t)dpos[1];
+  // the 2:4 layout: 64 value bytes and 16 position bytes per block row
+  const int ov = blk * 1024 + rr * 64 + 4 * t;
+  const int om = blk * 256 + rr * 16 + t;
+  *reinterpret_cast<uint32_t*>(a.dv0 + ov) = dval[0];
+  *reinterpret_cast<uint32_t*>(a.dv1 + ov) = dval[1];
+  a.dm0[om] = (uint8_t)dpos[0];
+  a.dm1[om] = (uint8_t)dpos[1];
 }
 
 }  // namespace
@@ -288,15 +305,32 @@ bool split24_supported(const Geometry& g) { return g.eb == 1 && (g.M == 4 || g.M
 
 hipError_t launch_split24(const Geometry& gs, const uint8_t* values, const uint8_t* meta, const Geometry& gd,
                           uint8_t* dvalues0, uint8_t* dmeta0, uint8_t* dvalues1, uint8_t* dmeta1, hipStream_t s) {
-  if (!split24_supported(gs) || gd.N != 2 || gd.M != 4 || gd.eb != gs.eb || gd.nRB != gs.nRB || gd.nKB != gs.nKB)
+  if (!split24_supported(gs) || gd.N != 2 || gd.M != 4 || gd.eb != gs.eb || gd.nRB != gs.nRB || gd.nKB != gs.nKB ||
+      gd.vblk != 1024 || gd.mblk != 256)
     return hipErrorInvalidValue;
   const int64_t total = gs.nRB * 16 * gs.nKB * 16;
+  if (total >= (1ll << 31) || gs.values_bytes() >= (1ull << 31) || gd.values_bytes() >= (1ull << 31))
+    return hipErrorInvalidValue;
+  SplitArgs a;
+  a.sv = values;
+  a.sm = meta ? meta : values;           // N = M: no positions (never read)
+  a.dv0 = dvalues0;
+  a.dm0 = dmeta0;
+  a.dv1 = dvalues1;
+  a.dm1 = dmeta1;
+  a.nKB = (int)gs.nKB;
+  a.total = (int)total;
+  a.C = gs.C;
+  a.vblk = (int)gs.vblk;
+  a.MR = gs.MR;
+  a.mblk = (int)gs.mblk;
+  a.vbytes = (int)gs.values_bytes();
+  a.mbytes = meta ? (int)gs.meta_bytes() : 0;
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-#define NM_SPLIT(M_, N_)                                                                                 \
-  if (gs.M == M_ && gs.N == N_) {                                                                        \
-    hipLaunchKernelGGL((split24_kernel<M_, N_>), grid, block, 0, s, gs, values, meta, gd, dvalues0, dmeta0, \
-                       dvalues1, dmeta1);                                                                \
-    return hipGetLastError();                                                                            \
+#define NM_SPLIT(M_, N_)                                                                   \
+  if (gs.M == M_ && gs.N == N_) {                                                          \
+    hipLaunchKernelGGL((split24_kernel<M_, N_>), grid, block, 0, s, a);                   \
+    return hipGetLastError();                                                              \
   }
   NM_SPLIT(4, 1) NM_SPLIT(4, 2) NM_SPLIT(4, 3) NM_SPLIT(4, 4)
   NM_SPLIT(8, 1) NM_SPLIT(8, 2) NM_SPLIT(8, 3) NM_SPLIT(8, 4) NM_SPLIT(8, 5) NM_SPLIT(8, 6) NM_SPLIT(8, 7)

@@ -67,6 +67,7 @@ smfmac_i8ws_kernel(SpmmArgs a, int mtiles, int nsteps, int nwg_xcd) {
   __shared__ __attribute__((aligned(1024))) uint8_t bsbuf[NW * 512];
 
   const Geometry& g = a.g;
+  load_args_early(a);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
