@@ -343,7 +343,7 @@ def test_fast_i8_variants(force_variant, variant, out, R, K, T):
 # the weight-stationary int8 2:4 kernel takes K in (640, 768] (six column
 # blocks in registers) and R <= 16384 (a workgroup per 512-row tile on each XCD)
 STAT_SHAPES = [(300, 768, 144), (17, 700, 16), (520, 768, 400), (1000, 656, 272), (2304, 768, 1040),
-               (3072, 768, 12608), (16384, 768, 64), (777, 768, 48)]
+               (3072, 768, 12608), (16384, 768, 64), (777, 768, 48), (520, 768, 13408), (300, 768, 38464)]
 
 
 @pytest.mark.parametrize("out", ["i8", "i32"])
