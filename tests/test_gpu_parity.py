@@ -1057,6 +1057,34 @@ def test_tk_two_layer_gelu(force_variant, N, M):
     _tk_case("i8", "i8", N, M, 528, 768, 400, 69, act="gelu", xpad=16, variant=variant)
 
 
+def test_tk_split24_small_workspace_runs_another_kernel():
+    """nm_spmm_tk on a 4:8 weight with less workspace than the two-layer split
+    needs runs another kernel (no copy), with the same bit-exact result;
+    with the full workspace it runs the split."""
+    import ctypes
+    import torch
+    import semi_structured_sparse_nm_amd as nm
+    R, K, T, N, M = 3072, 768, 1024, 4, 8
+    W, X, b, s = _inputs("i8", "i8", R, K, T, N, M, 70, "tk-split-small-ws")
+    p = nm.pack(torch.from_numpy(W).cuda(), N, M)
+    assert nm.variant_tk(p, T, torch.int8) == "split24_smfmac_i8_stationary_tk"
+    need = nm.workspace_size_tk(p, T, torch.int8)
+    assert need > 0
+    Xt = torch.from_numpy(np.ascontiguousarray(X.T)).cuda()
+    bd, sd = torch.from_numpy(b).cuda(), torch.from_numpy(s).cuda()
+    ref = reference(W, X, N, M, "i8", "i8", bias=b, scale=s)
+    small = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    full = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for ws, wsb in ((None, 0), (small, need - 1), (full, need)):
+        Yt = torch.full((T, R), 5, dtype=torch.int8, device="cuda")
+        d = p.desc()
+        st = nm.lib().nm_spmm_tk(ctypes.byref(d), Xt.data_ptr(), K, T, Yt.data_ptr(), R, nm.NM_I8, bd.data_ptr(),
+                                 sd.data_ptr(), 0, 1.0, None if ws is None else ws.data_ptr(), wsb, None)
+        assert st == nm.NM_OK
+        torch.cuda.synchronize()
+        compare(np.ascontiguousarray(Yt.cpu().numpy().T), ref, "i8", f"tk workspace {wsb}")
+
+
 @pytest.mark.parametrize("dt,out", PAIRS)
 @pytest.mark.parametrize("N,M", [(2, 4), (1, 4), (3, 4), (4, 8), (8, 8)])
 @pytest.mark.parametrize("R,K,T", [(17, 8, 1), (300, 200, 37), (259, 1288, 144)])
